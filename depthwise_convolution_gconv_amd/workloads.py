@@ -1,0 +1,107 @@
+"""Seeded synthetic workloads for grouped-convolution forward.
+
+This module only draws and quantises inputs; it holds none of the convolution's
+arithmetic.  Both the HIP path's tests and the oracle's tests take their inputs
+from here, so the two sides see bit-identical operands.
+
+Recipe (the same for every workload):
+
+* ``numpy.random.default_rng(seed).standard_normal(shape, dtype=float32)``,
+  scaled by the standard deviation ``sqrt(var)`` (the variance notation N(0, v)
+  is read as variance: 1/36, 1/1152, 1/31 and 1/288 are each 1/(C/g*KH*KW), the
+  fan-in, which keeps outputs near unit variance);
+* cast to the storage dtype with round-to-nearest-even (``torch.Tensor.to`` on
+  the CPU);
+* seeds: x = 1000 + i, w = 2000 + i, bias = 3000 + i for workload number i.
+
+The shapes are those of the pages' workloads: the layer timed in the
+discuss.pytorch.org thread "F.conv2d runs x15 slower in mixed-precision/
+half-precision mode" (x [1,512,256,256], w [512,128,3,3], groups=4, padding 3//2),
+a Conformer depthwise conv over (batch, steps, channels) from speechbrain issue
+#2733, a fully grouped ResNeXt-style layer (neon issue "Grouped convolutions"),
+and a model ensemble folded into groups (functorch issue #365, the conv batching
+rule).  No dataset is involved; all values are synthetic.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int                    # seed offset
+    layout: str                   # "nchw" or "ntc"
+    x_shape: Tuple[int, ...]
+    w_shape: Tuple[int, ...]
+    groups: int
+    stride: int
+    pad: int
+    dilation: int
+    dtype: str                    # "f32" | "f16" | "bf16"
+    var_x: float
+    var_w: float
+    var_b: Optional[float]        # None: no bias
+    what: str = ""
+
+    @property
+    def has_bias(self) -> bool:
+        return self.var_b is not None
+
+    @property
+    def bias_shape(self) -> Tuple[int, ...]:
+        return (self.w_shape[0],)
+
+
+WORKLOADS = {
+    "c1_g4_f32": Workload(
+        "c1_g4_f32", 1, "nchw", (1, 16, 32, 32), (16, 4, 3, 3), 4, 1, 1, 1, "f32",
+        1.0, 1 / 36, None, "small grouped conv2d, g=4"),
+    "c2_p2layer_f32": Workload(
+        "c2_p2layer_f32", 2, "nchw", (1, 512, 256, 256), (512, 128, 3, 3), 4, 1, 1, 1, "f32",
+        1.0, 1 / 1152, None, "the discuss.pytorch.org layer, fp32"),
+    "c2_p2layer_f16": Workload(
+        "c2_p2layer_f16", 2, "nchw", (1, 512, 256, 256), (512, 128, 3, 3), 4, 1, 1, 1, "f16",
+        1.0, 1 / 1152, None, "the discuss.pytorch.org layer, fp16 in / fp32 accumulate"),
+    "c3_dw1d_btc_f32": Workload(
+        "c3_dw1d_btc_f32", 3, "ntc", (8, 1024, 512), (512, 1, 31), 512, 1, 15, 1, "f32",
+        1.0, 1 / 31, 0.01, "Conformer depthwise conv1d, (batch, steps, channels)"),
+    "c4_fullgroup_bf16": Workload(
+        "c4_fullgroup_bf16", 4, "nchw", (32, 1024, 14, 14), (1024, 4, 3, 3), 256, 1, 1, 1, "bf16",
+        1.0, 1 / 36, 0.01, "fully grouped conv2d, 4 in / 4 out channels per group"),
+    "c5_ensemble_f16": Workload(
+        "c5_ensemble_f16", 5, "nchw", (64, 1024, 28, 28), (2048, 32, 3, 3), 32, 1, 1, 1, "f16",
+        1.0, 1 / 288, 0.01, "32-model ensemble folded into groups"),
+}
+
+HEADLINE = "c2_p2layer_f16"
+
+
+def draw(shape, var: float, seed: int, dtype: str) -> torch.Tensor:
+    """Seeded N(0, var) draw in fp32, rounded to `dtype` (RNE), as a CPU tensor."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal(tuple(shape), dtype=np.float32)
+    a *= np.float32(math.sqrt(var))
+    return torch.from_numpy(a).to(DTYPES[dtype])
+
+
+def make_inputs(wl: Workload, seed_shift: int = 0):
+    """(x, w, bias-or-None) as CPU tensors of the workload's dtype."""
+    x = draw(wl.x_shape, wl.var_x, 1000 + wl.index + seed_shift, wl.dtype)
+    w = draw(wl.w_shape, wl.var_w, 2000 + wl.index + seed_shift, wl.dtype)
+    b = draw(wl.bias_shape, wl.var_b, 3000 + wl.index + seed_shift, wl.dtype) if wl.has_bias else None
+    return x, w, b
+
+
+def as_f64(t: Optional[torch.Tensor]):
+    """Exact widening of a CPU tensor to a float64 numpy array (None passes)."""
+    if t is None:
+        return None
+    return t.detach().to("cpu").to(torch.float64).numpy()
