@@ -1,0 +1,22 @@
+"""Grouped-convolution forward engine for AMD Instinct MI355X (gfx950).
+
+The compute runs in libgconv.so (hand-written HIP kernels behind the C ABI in
+include/gconv.h); this package is its Python binding.  Importing the package
+does not load the library; the first call does, and raises if it is missing.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    GconvError,
+    GconvLaunchError,
+    conv2d,
+    dwconv1d_btc,
+    gconv_fwd,
+    gconv_fwd_route,
+    gconv_last_error,
+    gconv_last_kernel,
+    gconv_out_shape,
+    gconv_select_route,
+    gconv_status_string,
+    lib,
+    lib_path,
+)

@@ -1,0 +1,215 @@
+"""ctypes binding of libgconv.so: argument marshalling only.
+
+Every function here checks and converts its arguments, then calls the C entry
+point of the same name in libgconv.so (declared in include/gconv.h).  No
+arithmetic of the convolution happens in Python; torch supplies device memory,
+the current device and the current HIP stream.  If libgconv.so is missing the
+first call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgconv.so")
+
+OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3, 4
+LAYOUTS = {"nchw": 0, "ntc": 1}
+DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+DTYPE_NAMES = {"f32": 0, "f16": 1, "bf16": 2}
+ROUTES = {"auto": 0, "direct": 1, "igemm": 2}
+ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
+
+# Every symbol include/gconv.h declares.
+EXPORTS = ("gconv_out_shape", "gconv_select_route", "gconv_fwd", "gconv_fwd_route",
+           "gconv_last_kernel", "gconv_status_string", "gconv_last_error")
+
+_i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+_i64p, _i32p = ctypes.POINTER(_i64), ctypes.POINTER(_i32)
+
+_lib = None
+
+
+class GconvError(ValueError):
+    """Argument, shape or coverage error reported by libgconv (status 1-3)."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"gconv status {status}: {detail}")
+        self.status = status
+
+
+class GconvLaunchError(RuntimeError):
+    """The HIP runtime failed to launch a libgconv kernel (status 4)."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"gconv status {status}: {detail}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libgconv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -m depthwise_convolution_gconv_amd.build` (no fallback exists)")
+        L = ctypes.CDLL(_LIB_PATH)
+        conv = [_vp, _i64p, _vp, _i64p, _vp, _vp, _i32p, _i32p, _i32p, _i32, _i32, _i32]
+        L.gconv_fwd.argtypes = conv + [_vp]
+        L.gconv_fwd.restype = _i32
+        L.gconv_fwd_route.argtypes = conv + [_i32, _vp]
+        L.gconv_fwd_route.restype = _i32
+        L.gconv_out_shape.argtypes = [_i64p, _i64p, _i32p, _i32p, _i32p, _i32, _i32, _i64p]
+        L.gconv_out_shape.restype = _i32
+        L.gconv_select_route.argtypes = [_i64p, _i64p, _i32p, _i32p, _i32p, _i32, _i32, _i32, _i32p]
+        L.gconv_select_route.restype = _i32
+        L.gconv_last_kernel.argtypes = []
+        L.gconv_last_kernel.restype = ctypes.c_char_p
+        L.gconv_status_string.argtypes = [_i32]
+        L.gconv_status_string.restype = ctypes.c_char_p
+        L.gconv_last_error.argtypes = []
+        L.gconv_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status == OK:
+        return
+    L = lib()
+    detail = L.gconv_last_error().decode() or L.gconv_status_string(status).decode()
+    if status == ERR_LAUNCH:
+        raise GconvLaunchError(status, detail)
+    raise GconvError(status, detail)
+
+
+def _arr(ctype, vals):
+    vals = list(vals)
+    return (ctype * max(len(vals), 1))(*vals)
+
+
+def _geom(layout: str, stride, pad, dilation):
+    n = 2 if layout == "nchw" else 1
+
+    def norm(v):
+        if isinstance(v, (tuple, list)):
+            if len(v) != n:
+                raise GconvError(ERR_INVALID_ARG, f"expected {n} values, got {v}")
+            return [int(t) for t in v]
+        return [int(v)] * n
+    return _arr(_i32, norm(stride)), _arr(_i32, norm(pad)), _arr(_i32, norm(dilation))
+
+
+def _layout(layout: str) -> int:
+    if layout not in LAYOUTS:
+        raise GconvError(ERR_INVALID_ARG, f"unknown layout {layout!r}")
+    return LAYOUTS[layout]
+
+
+def gconv_out_shape(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, pad=0, dilation=1,
+                    groups: int = 1, layout: str = "nchw") -> Tuple[int, ...]:
+    """Output shape from the library's own host validation (no device work)."""
+    L = lib()
+    s, p, d = _geom(layout, stride, pad, dilation)
+    lay = _layout(layout)
+    out = (_i64 * 4)()
+    _check(L.gconv_out_shape(_arr(_i64, x_shape), _arr(_i64, w_shape), s, p, d, int(groups), lay, out))
+    return tuple(int(v) for v in out[: (4 if layout == "nchw" else 3)])
+
+
+def gconv_select_route(x_shape, w_shape, stride=1, pad=0, dilation=1, groups: int = 1,
+                       layout: str = "nchw", dtype: Union[str, torch.dtype] = "f16") -> str:
+    """The route ("direct" or "igemm") that route="auto" takes for this geometry."""
+    L = lib()
+    s, p, d = _geom(layout, stride, pad, dilation)
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else DTYPE_NAMES[dtype]
+    r = _i32(-1)
+    _check(L.gconv_select_route(_arr(_i64, x_shape), _arr(_i64, w_shape), s, p, d, int(groups),
+                                _layout(layout), dt, ctypes.byref(r)))
+    return ROUTE_NAMES[r.value]
+
+
+def _call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], y: Optional[torch.Tensor],
+          stride, pad, dilation, groups: int, layout: str, route: Optional[str],
+          stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+    L = lib()
+    for name, t in (("x", x), ("w", w), ("bias", bias), ("y", y)):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise GconvError(ERR_INVALID_ARG, f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise GconvError(ERR_INVALID_ARG, f"{name} must be contiguous")
+        if t.dtype != x.dtype:
+            raise GconvError(ERR_INVALID_ARG, f"{name} dtype {t.dtype} differs from x dtype {x.dtype}")
+        if t.device != x.device:
+            raise GconvError(ERR_INVALID_ARG, f"{name} is on {t.device}, x on {x.device}")
+    if x.dtype not in DTYPES:
+        raise GconvError(ERR_INVALID_ARG, f"unsupported dtype {x.dtype}")
+    expect_dims = 4 if layout == "nchw" else 3
+    if x.dim() != expect_dims or w.dim() != expect_dims:
+        raise GconvError(ERR_INVALID_ARG, f"{layout} expects {expect_dims}-D x and w")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != w.shape[0]):
+        raise GconvError(ERR_SHAPE, "bias must have shape [w.shape[0]]")
+    yshape = gconv_out_shape(tuple(x.shape), tuple(w.shape), stride, pad, dilation, groups, layout)
+    if y is None:
+        y = torch.empty(yshape, dtype=x.dtype, device=x.device)
+    elif tuple(y.shape) != yshape:
+        raise GconvError(ERR_SHAPE, f"y has shape {tuple(y.shape)}, expected {yshape}")
+    s, p, d = _geom(layout, stride, pad, dilation)
+    with torch.cuda.device(x.device):
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        args = [_vp(x.data_ptr()), _arr(_i64, x.shape), _vp(w.data_ptr()), _arr(_i64, w.shape),
+                _vp(bias.data_ptr() if bias is not None else 0), _vp(y.data_ptr()), s, p, d, int(groups),
+                _layout(layout), DTYPES[x.dtype]]
+        if route is None:
+            _check(L.gconv_fwd(*args, _vp(st.cuda_stream)))
+        else:
+            if route not in ROUTES:
+                raise GconvError(ERR_INVALID_ARG, f"unknown route {route!r}")
+            _check(L.gconv_fwd_route(*args, ROUTES[route], _vp(st.cuda_stream)))
+    return y
+
+
+def gconv_fwd(x, w, bias=None, stride=1, pad=0, dilation=1, groups: int = 1, layout: str = "nchw",
+              y=None, stream=None) -> torch.Tensor:
+    """Grouped convolution forward (route chosen per shape).  Returns y."""
+    return _call(x, w, bias, y, stride, pad, dilation, groups, layout, None, stream)
+
+
+def gconv_fwd_route(x, w, bias=None, stride=1, pad=0, dilation=1, groups: int = 1, layout: str = "nchw",
+                    route: str = "auto", y=None, stream=None) -> torch.Tensor:
+    """gconv_fwd with the route ("auto", "direct", "igemm") forced."""
+    return _call(x, w, bias, y, stride, pad, dilation, groups, layout, route, stream)
+
+
+def gconv_last_kernel() -> str:
+    return lib().gconv_last_kernel().decode()
+
+
+def gconv_status_string(status: int) -> str:
+    return lib().gconv_status_string(int(status)).decode()
+
+
+def gconv_last_error() -> str:
+    return lib().gconv_last_error().decode()
+
+
+# ---- convenience spellings ------------------------------------------------
+
+def conv2d(x, weight, bias=None, stride=1, padding=0, dilation=1, groups: int = 1, route: str = "auto"):
+    """F.conv2d-style call: x [N,C,H,W], weight [Cout,C/groups,KH,KW]."""
+    return _call(x, weight, bias, None, stride, padding, dilation, groups, "nchw",
+                 None if route == "auto" else route, None)
+
+
+def dwconv1d_btc(x, weight, bias=None, stride=1, padding=0, dilation=1):
+    """Depthwise conv1d over x [B,T,C] (batch, steps, channels), weight [C,1,K]."""
+    return _call(x, weight, bias, None, stride, padding, dilation, x.shape[-1], "ntc", None, None)

@@ -1,0 +1,57 @@
+// common.hpp -- shared definitions of the HIP side of libgconv (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gconv {
+
+// Geometry of one NCHW grouped conv2d call, validated on the host.
+struct Conv2dArgs {
+    const void *x;
+    const void *w;
+    const void *bias;  // nullptr: no bias
+    void *y;
+    int64_t N, C, H, W;
+    int64_t Cout, KH, KW;
+    int64_t groups;
+    int64_t OH, OW;
+    int32_t sh, sw, ph, pw, dh, dw;
+    int dtype;  // gconv_dtype_t
+    hipStream_t stream;
+};
+
+// Geometry of one depthwise conv1d call over (batch, steps, channels).
+struct Dw1dArgs {
+    const void *x;
+    const void *w;
+    const void *bias;
+    void *y;
+    int64_t B, T, C, K, To;
+    int32_t s, p, d;
+    int dtype;
+    hipStream_t stream;
+};
+
+enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+// Storage <-> fp32.  Widening is exact for every storage type; narrowing
+// rounds to nearest, ties to even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(_Float16 v) { return (float)v; }
+__device__ __forceinline__ float to_f32(__bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
+
+// Launchers (each returns the launch status and the kernel name it picked).
+hipError_t launch_direct2d(const Conv2dArgs &a, const char **kname);
+bool igemm_supported(const Conv2dArgs &a);
+hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);
+hipError_t launch_dw1d(const Dw1dArgs &a, const char **kname);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace gconv

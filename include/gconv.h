@@ -1,0 +1,137 @@
+/*
+ * gconv.h -- C ABI of libgconv.so, a grouped-convolution forward engine for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Grouped convolution as the neon issue "Grouped convolutions"
+ * defines it (thestew42's first reply): the C input channels, the Cout filters
+ * and the Cout output channels are split into `groups` groups that are not
+ * connected to each other.  Group k reads input channels [k*C/g, (k+1)*C/g) and
+ * writes output channels [k*Cout/g, (k+1)*Cout/g) (the "usual" group-contiguous
+ * output order in ibmua's reply on the same issue).  Each output is the
+ * cross-correlation F.conv2d computes in the discuss.pytorch.org thread "F.conv2d
+ * runs x15 slower in mixed-precision/half-precision mode" (the poster's script:
+ * F.conv2d(input, weight, padding=3 // 2, groups=4)):
+ *
+ *   y[n,o,oh,ow] = bias[o] + sum_{ci<C/g, kh<KH, kw<KW}
+ *                  x[n, (o/(Cout/g))*(C/g)+ci, oh*sh-ph+kh*dh, ow*sw-pw+kw*dw] * w[o,ci,kh,kw]
+ *
+ * with x read as zero outside [0,H)x[0,W).  The second layout is the depthwise
+ * 1-D convolution of speechbrain issue #2733 (Conformer convolution module,
+ * groups equal to the channel count, tensor laid out (batch, steps, channels)):
+ *
+ *   y[b,t,c] = bias[c] + sum_{k<K} x[b, t*s-p+k*d, c] * w[c,0,k]
+ *
+ * Arithmetic.  fp32 tensors are multiplied and accumulated in fp32.  fp16 and
+ * bf16 tensors are multiplied exactly and accumulated in fp32 (matrix cores or
+ * fp32 FMA); the bias is added to the fp32 accumulator and the result is rounded
+ * once to the tensor dtype, round-to-nearest-even.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers x, w, bias, y are DEVICE pointers owned by the caller, contiguous
+ *    in the stated layout, all of the one dtype `dtype`.  y must not overlap
+ *    x, w or bias.  bias may be NULL (no bias).
+ *  - Shape arrays and stride/pad/dilation arrays are HOST pointers.
+ *      NCHW: x_shape = {N,C,H,W}, w_shape = {Cout, C/groups, KH, KW},
+ *            stride/pad/dilation = {h, w} (2 ints each), y = {N,Cout,OH,OW}.
+ *      NTC : x_shape = {B,T,C}, w_shape = {C,1,K}, groups must equal C,
+ *            stride/pad/dilation = 1 int each, y = {B,To,C}.
+ *    Output length per axis: floor((L + 2p - d*(K-1) - 1)/s) + 1.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
+ *    and the call returns without synchronising.
+ *  - The library keeps no state between calls apart from a thread-local error
+ *    string, allocates no device memory and is safe to call from several host
+ *    threads at once.
+ *  - Errors: argument and shape errors are detected on the host before anything
+ *    is enqueued, and leave y untouched.  A zero-sized batch (N == 0 or B == 0)
+ *    is valid and enqueues nothing; x and y may then be NULL.  No C++ exception
+ *    crosses this boundary.
+ */
+#ifndef GCONV_H
+#define GCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GCONV_OK = 0,
+    GCONV_ERR_INVALID_ARG = 1,  /* NULL pointer, bad enum, size/stride/dilation < 1, pad < 0  */
+    GCONV_ERR_SHAPE = 2,        /* C or Cout not divisible by groups, weight shape mismatch,
+                                   or an output length below 1                               */
+    GCONV_ERR_UNSUPPORTED = 3,  /* a valid convolution this library does not run, e.g. NTC
+                                   with groups != C, or a forced route that cannot run it   */
+    GCONV_ERR_LAUNCH = 4        /* the HIP runtime reported an error when launching         */
+} gconv_status_t;
+
+typedef enum {
+    GCONV_LAYOUT_NCHW = 0,      /* conv2d, x [N,C,H,W]                                      */
+    GCONV_LAYOUT_NTC = 1        /* depthwise conv1d, x [B,T,C] = (batch, steps, channels)   */
+} gconv_layout_t;
+
+typedef enum { GCONV_F32 = 0, GCONV_F16 = 1, GCONV_BF16 = 2 } gconv_dtype_t;
+
+/* Which kernel family runs a call.  The option of choosing the route follows
+ * functorch issue #365 "Optimize convolution batching rule performance", where
+ * the maintainers agree on a user option selecting the group-convolution route. */
+typedef enum {
+    GCONV_ROUTE_AUTO = 0,       /* chosen per shape by gconv_select_route                  */
+    GCONV_ROUTE_DIRECT = 1,     /* direct convolution on the vector ALUs: LDS halo tiles,
+                                   group index folded into the grid (NCHW), or the
+                                   (batch, steps, channels) sliding-window kernel (NTC)     */
+    GCONV_ROUTE_IGEMM = 2       /* implicit GEMM per group on the matrix cores: im2col
+                                   tiles built in LDS, never materialised (NCHW only)      */
+} gconv_route_t;
+
+/* Output shape of a convolution.  y_shape receives 4 (NCHW) or 3 (NTC) values.
+ * Returns GCONV_OK, GCONV_ERR_INVALID_ARG or GCONV_ERR_SHAPE; no device work. */
+gconv_status_t gconv_out_shape(const int64_t *x_shape, const int64_t *w_shape,
+                               const int32_t *stride, const int32_t *pad,
+                               const int32_t *dilation, int32_t groups,
+                               gconv_layout_t layout, int64_t *y_shape);
+
+/* The route GCONV_ROUTE_AUTO takes for this geometry and dtype (written to
+ * *route; never GCONV_ROUTE_AUTO).  Same validation and return codes as
+ * gconv_out_shape; no device work. */
+gconv_status_t gconv_select_route(const int64_t *x_shape, const int64_t *w_shape,
+                                  const int32_t *stride, const int32_t *pad,
+                                  const int32_t *dilation, int32_t groups,
+                                  gconv_layout_t layout, gconv_dtype_t dtype,
+                                  gconv_route_t *route);
+
+/* Grouped convolution forward, route chosen per shape (GCONV_ROUTE_AUTO). */
+gconv_status_t gconv_fwd(const void *x, const int64_t *x_shape,
+                         const void *w, const int64_t *w_shape,
+                         const void *bias, void *y,
+                         const int32_t *stride, const int32_t *pad, const int32_t *dilation,
+                         int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
+                         void *hip_stream);
+
+/* gconv_fwd with the route forced by the caller.  GCONV_ROUTE_IGEMM on NTC, or
+ * on a geometry the implicit-GEMM kernels do not cover, returns
+ * GCONV_ERR_UNSUPPORTED without enqueuing anything. */
+gconv_status_t gconv_fwd_route(const void *x, const int64_t *x_shape,
+                               const void *w, const int64_t *w_shape,
+                               const void *bias, void *y,
+                               const int32_t *stride, const int32_t *pad, const int32_t *dilation,
+                               int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
+                               gconv_route_t route, void *hip_stream);
+
+/* Name of the kernel the last successful gconv_fwd / gconv_fwd_route call on
+ * this host thread launched ("" before the first call or after an empty batch).
+ * The string has static storage. */
+const char *gconv_last_kernel(void);
+
+/* Fixed English text for a status code.  Static storage. */
+const char *gconv_status_string(gconv_status_t status);
+
+/* Detail of the last non-OK status returned on this host thread ("" if none).
+ * Thread-local storage, valid until the next call on the same thread. */
+const char *gconv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GCONV_H */

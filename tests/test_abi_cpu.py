@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol that
+include/gconv.h declares, and its host-side validation, output shapes and route
+selection behave as documented.  No call here enqueues device work: every
+gconv_fwd call below is rejected by host validation before any HIP call."""
+import ctypes
+import itertools
+import os
+import re
+
+import numpy as np
+import pytest
+
+import depthwise_convolution_gconv_amd as gc
+from depthwise_convolution_gconv_amd import _binding as B
+from depthwise_convolution_gconv_amd.workloads import WORKLOADS
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gconv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gconv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(gc.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {gc.lib_path()}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings():
+    assert gc.gconv_status_string(0) == "ok"
+    assert gc.gconv_status_string(3) == "unsupported convolution"
+    assert gc.gconv_status_string(99) == "unknown status"
+
+
+def test_out_shape_of_page_workload_golden():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "page_workload_shapes.json")))
+    for c in g["cases"]:
+        assert list(gc.gconv_out_shape(c["x_shape"], c["w_shape"], 1, c["padding"], 1, c["groups"])) == c["y_shape"]
+
+
+def test_out_shape_matches_oracle_lengths():
+    for L, K, s, p, d in itertools.product(range(1, 9), range(1, 4), range(1, 4), range(0, 3), range(1, 3)):
+        expect = oracle.out_len(L, K, s, p, d)
+        if expect < 1:
+            with pytest.raises(gc.GconvError) as e:
+                gc.gconv_out_shape((1, 2, L, L), (2, 1, K, K), s, p, d, groups=2)
+            assert e.value.status == 2
+            continue
+        assert gc.gconv_out_shape((1, 2, L, L), (4, 1, K, K), s, p, d, groups=2) == (1, 4, expect, expect)
+        assert gc.gconv_out_shape((3, L, 5), (5, 1, K), s, p, d, groups=5, layout="ntc") == (3, expect, 5)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_workload_shapes_and_routes(name):
+    wl = WORKLOADS[name]
+    ys = gc.gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
+    if wl.layout == "nchw":
+        assert ys == (wl.x_shape[0], wl.w_shape[0], wl.x_shape[2], wl.x_shape[3])
+    else:
+        assert ys == wl.x_shape
+    route = gc.gconv_select_route(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups,
+                                  wl.layout, wl.dtype)
+    expected = {"c1_g4_f32": "direct", "c2_p2layer_f32": "direct", "c2_p2layer_f16": "igemm",
+                "c3_dw1d_btc_f32": "direct", "c4_fullgroup_bf16": "direct", "c5_ensemble_f16": "igemm"}
+    assert route == expected[name]
+
+
+def _raw_fwd(x_shape, w_shape, stride, pad, dil, groups, layout, dtype, x=16, w=4096, b=0, y=1 << 20,
+             route=None):
+    """Call the C entry point with fake (never dereferenced) device addresses."""
+    L = gc.lib()
+    arr64 = lambda v: (ctypes.c_int64 * len(v))(*v)
+    arr32 = lambda v: (ctypes.c_int32 * len(v))(*v)
+    args = [ctypes.c_void_p(x), arr64(x_shape), ctypes.c_void_p(w), arr64(w_shape), ctypes.c_void_p(b),
+            ctypes.c_void_p(y), arr32(stride), arr32(pad), arr32(dil), groups, layout, dtype]
+    if route is None:
+        return L.gconv_fwd(*args, None)
+    return L.gconv_fwd_route(*args, route, None)
+
+
+@pytest.mark.parametrize("case,status", [
+    (((1, 6, 5, 5), (4, 3, 3, 3), 4), 2),     # C % groups != 0
+    (((1, 6, 5, 5), (5, 2, 3, 3), 3), 2),     # Cout % groups != 0
+    (((1, 6, 5, 5), (6, 3, 3, 3), 3), 2),     # w.shape[1] != C/groups
+    (((1, 6, 2, 2), (6, 2, 5, 5), 3), 2),     # empty output
+    (((1, 6, 5, 5), (6, 2, 3, 3), 0), 1),     # groups < 1
+    (((1, 0, 5, 5), (6, 2, 3, 3), 3), 1),     # C < 1
+    (((-1, 6, 5, 5), (6, 2, 3, 3), 3), 1),    # N < 0
+])
+def test_nchw_validation_errors(case, status):
+    xs, ws, g = case
+    assert _raw_fwd(xs, ws, (1, 1), (0, 0), (1, 1), g, 0, 0) == status
+    assert gc.gconv_last_error() != ""
+
+
+def test_bad_enums_strides_and_pointers():
+    ok = ((1, 4, 5, 5), (4, 1, 3, 3), (1, 1), (1, 1), (1, 1), 4)
+    assert _raw_fwd(*ok, 0, 7) == 1                           # dtype
+    assert _raw_fwd(*ok, 5, 0) == 1                           # layout
+    assert _raw_fwd(*ok, 0, 0, route=9) == 1                  # route
+    assert _raw_fwd(ok[0], ok[1], (0, 1), ok[3], ok[4], 4, 0, 0) == 1   # stride 0
+    assert _raw_fwd(ok[0], ok[1], ok[2], (-1, 0), ok[4], 4, 0, 0) == 1  # negative pad
+    assert _raw_fwd(ok[0], ok[1], ok[2], ok[3], (1, 0), 4, 0, 0) == 1   # dilation 0
+    assert _raw_fwd(*ok, 0, 0, x=0) == 1                      # NULL x
+    assert _raw_fwd(*ok, 0, 0, y=0) == 1                      # NULL y
+    assert _raw_fwd(*ok, 0, 0, y=16) == 1                     # y overlaps x
+
+
+def test_ntc_validation():
+    # depthwise only: groups must equal C
+    assert _raw_fwd((2, 10, 8), (8, 2, 3), (1,), (1,), (1,), 4, 1, 0) == 3
+    # channel multiplier
+    assert _raw_fwd((2, 10, 8), (16, 1, 3), (1,), (1,), (1,), 8, 1, 0) == 3
+    # forced implicit GEMM on the NTC layout
+    assert _raw_fwd((2, 10, 8), (8, 1, 3), (1,), (1,), (1,), 8, 1, 0, route=2) == 3
+    # empty output
+    assert _raw_fwd((2, 2, 8), (8, 1, 5), (1,), (0,), (1,), 8, 1, 0) == 2
+
+
+def test_forced_igemm_rejected_for_fp32():
+    assert _raw_fwd((1, 64, 8, 8), (64, 64, 3, 3), (1, 1), (1, 1), (1, 1), 1, 0, 0, route=2) == 3
+
+
+def test_zero_batch_enqueues_nothing():
+    assert _raw_fwd((0, 4, 5, 5), (4, 1, 3, 3), (1, 1), (1, 1), (1, 1), 4, 0, 0) == 0
+    assert gc.gconv_last_kernel() == ""
+    assert _raw_fwd((0, 10, 8), (8, 1, 3), (1,), (1,), (1,), 8, 1, 0) == 0
+
+
+def test_zero_batch_accepts_null_x_and_y():
+    assert _raw_fwd((0, 4, 5, 5), (4, 1, 3, 3), (1, 1), (1, 1), (1, 1), 4, 0, 0, x=0, y=0) == 0
+    assert _raw_fwd((0, 4, 5, 5), (4, 1, 3, 3), (1, 1), (1, 1), (1, 1), 4, 0, 0, w=0) == 1
