@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped-convolution forward engine on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-others]
+
+One step = one gconv_fwd call (host validation, route selection, the kernel and
+its fused epilogue) on one batch of the workload.  The default workload is the
+layer timed in the discuss.pytorch.org thread "F.conv2d runs x15 slower in
+mixed-precision/half-precision mode": x [1,512,256,256], w [512,128,3,3],
+groups=4, padding 1, no bias, here in fp16 with fp32 accumulation.
+
+Timing: W untimed warm-up steps, then K steps bracketed by
+torch.cuda.synchronize().  Inputs are seeded synthetic tensors already resident
+in HBM; successive steps rotate over enough copies of the input/output buffers
+(>= 512 MB in total) that a step never finds its operands in the 256 MB
+Infinity Cache.  Each launch is also bracketed by HIP events on the launch
+stream, which gives the kernel's average duration for the roofline object.
+
+Prints ONE JSON line.  `value` is effective TFLOP/s (2*N*Cout*OH*OW*C/g*KH*KW per
+step, padding taps included, divided by the step time).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+PEAK_TFLOPS = {"f16": 2500.0,  # dense MFMA, published
+               "bf16": 2500.0,
+               "f32": 157.3}   # fp32 vector / fp32 MFMA, published
+METRIC = "grouped-conv fwd effective TFLOP/s & GB/s, % roofline, ms per call (1 GPU)"
+# The pages' own figure for the headline layer: 60.74 ms median for fp16 (apex O2)
+# on a Titan RTX with cuDNN 7.6.3, i.e. 77.31 GFLOP / 60.74 ms.
+PAGE_FP16_MS = 60.74
+
+
+def flops(wl, exact=False):
+    from depthwise_convolution_gconv_amd import gconv_out_shape
+    ys = gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
+    if wl.layout == "nchw":
+        N, Co, OH, OW = ys
+        _, Cg, KH, KW = wl.w_shape
+        if not exact:
+            return 2 * N * Co * OH * OW * Cg * KH * KW
+        rows = sum(1 for o in range(OH) for k in range(KH)
+                   if 0 <= o * wl.stride - wl.pad + k * wl.dilation < wl.x_shape[2])
+        cols = sum(1 for o in range(OW) for k in range(KW)
+                   if 0 <= o * wl.stride - wl.pad + k * wl.dilation < wl.x_shape[3])
+        return 2 * N * Co * Cg * rows * cols
+    B, To, C = ys
+    K = wl.w_shape[2]
+    if not exact:
+        return 2 * B * To * C * K
+    taps = sum(1 for t in range(To) for k in range(K)
+               if 0 <= t * wl.stride - wl.pad + k * wl.dilation < wl.x_shape[1])
+    return 2 * B * C * taps
+
+
+def alg_bytes(wl):
+    """|x| + |w| + |bias| + |y| in bytes, each touched once."""
+    from depthwise_convolution_gconv_amd import gconv_out_shape
+    es = 4 if wl.dtype == "f32" else 2
+    ys = gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
+    n = math.prod(wl.x_shape) + math.prod(wl.w_shape) + math.prod(ys)
+    if wl.has_bias:
+        n += wl.w_shape[0]
+    return n * es
+
+
+def compute_peak(wl, route):
+    """(bound name, peak TFLOP/s) of the arithmetic unit the route runs on."""
+    if route == "igemm":
+        return "mfma", PEAK_TFLOPS[wl.dtype]
+    return "alu", PEAK_TFLOPS["f32"]
+
+
+def source_digest(kernel_file):
+    path = os.path.join(ROOT, "depthwise_convolution_gconv_amd", "csrc", kernel_file)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+KERNEL_FILES = {"igemm": "igemm.hip", "direct_nchw": "direct2d.hip", "direct_ntc": "dw1d_ntc.hip"}
+
+
+def counters_traffic(wl_name, kernel_file):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"counters_{wl_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256_16") != source_digest(kernel_file):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def measure(wl, steps, warmup, rotate_bytes=512 << 20):
+    """Time `steps` gconv_fwd calls on rotating buffer sets.  Returns a dict."""
+    import torch
+    import depthwise_convolution_gconv_amd as gc
+    from depthwise_convolution_gconv_amd.workloads import make_inputs
+
+    dev = torch.device("cuda", 0)
+    x, w, b = make_inputs(wl)
+    x, w = x.to(dev), w.to(dev)
+    b = b.to(dev) if b is not None else None
+    ys = gc.gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
+    ws_bytes = alg_bytes(wl)
+    nsets = min(32, max(1, math.ceil(rotate_bytes / ws_bytes)))
+    calls = []
+    for i in range(nsets):
+        xi = x if i == 0 else x.clone()
+        wi = w if i == 0 else w.clone()
+        bi = None if b is None else (b if i == 0 else b.clone())
+        yi = torch.empty(ys, dtype=x.dtype, device=dev)
+        calls.append(gc.PreparedCall(xi, wi, bi, yi, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout))
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        calls[i % nsets]()
+    kernel = gc.gconv_last_kernel()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        calls[i % nsets]()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t_start.elapsed_time(t_end) / steps
+    kms = sorted(a.elapsed_time(b_) for a, b_ in ev)
+    return {"step_ms": step_ms, "kernel_ms_avg": sum(kms) / len(kms), "kernel_ms_median": kms[len(kms) // 2],
+            "kernel_ms_p10": kms[len(kms) // 10], "kernel_ms_p90": kms[(9 * len(kms)) // 10],
+            "wall_s": wall, "kernel": kernel, "rotation_sets": nsets}
+
+
+def roofline(wl, route, kernel_ms, traffic):
+    f = flops(wl)
+    byts = alg_bytes(wl)
+    cname, cpeak = compute_peak(wl, route)
+    t_hbm = byts / (PEAK_HBM_GBS * 1e9)
+    t_cmp = f / (cpeak * 1e12)
+    t = kernel_ms * 1e-3
+    if t_hbm >= t_cmp:
+        return {"bound": "hbm", "achieved": round(byts / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(byts / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic}
+    return {"bound": cname, "achieved": round(f / t / 1e12, 2), "peak": cpeak, "unit": "TFLOP/s",
+            "frac": round(f / t / 1e12 / cpeak, 4), "traffic": traffic}
+
+
+def cpu_baseline(wl, target_s=10.0):
+    """The fp64 oracle, unmodified, timed on the host cores on a random sample
+    of the workload's outputs (each evaluated one by one)."""
+    import numpy as np
+    import oracle
+    from depthwise_convolution_gconv_amd.workloads import as_f64, make_inputs
+    from depthwise_convolution_gconv_amd import gconv_out_shape
+    x, w, b = make_inputs(wl)
+    xd, wd, bd = as_f64(x), as_f64(w), as_f64(b)
+    ys = gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
+    total = math.prod(ys)
+    per_point = 2 * math.prod(wl.w_shape[1:])
+    rng = np.random.default_rng(12345)
+
+    def run(n):
+        idx = rng.integers(0, total, n)
+        t0 = time.perf_counter()
+        if wl.layout == "nchw":
+            oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
+        else:
+            oracle.dwconv1d_btc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation)
+        return time.perf_counter() - t0
+
+    probe = 4096
+    dt = run(probe)
+    n = int(min(max(probe, probe * target_s / max(dt, 1e-6)), 50_000_000))
+    dt = run(n)
+    return {"value": round(per_point * n / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} random outputs of the workload, each evaluated by the oracle's point "
+                      f"function (fp64, {per_point} FLOP each, padding taps counted), {dt:.1f} s"}
+
+
+def route_of(wl):
+    import depthwise_convolution_gconv_amd as gc
+    return gc.gconv_select_route(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups,
+                                 wl.layout, wl.dtype)
+
+
+def kernel_file(wl, route):
+    if route == "igemm":
+        return KERNEL_FILES["igemm"]
+    return KERNEL_FILES["direct_ntc" if wl.layout == "ntc" else "direct_nchw"]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 plain device copies of 256 MiB (scale for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the forward conv shards by batch or group with no communication; "
+              "multi-GPU runs are not part of this engine).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from depthwise_convolution_gconv_amd.workloads import HEADLINE, WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.calibrate_copy:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": nbytes, "copy_bytes_written_per_launch": nbytes,
+                          "launches": 5}))
+        return
+
+    name = args.workload or HEADLINE
+    wl = WORKLOADS[name]
+    route = route_of(wl)
+    m = measure(wl, args.steps, args.warmup)
+    kfile = kernel_file(wl, route)
+    f = flops(wl)
+    value = f / (m["step_ms"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / (f / (PAGE_FP16_MS * 1e-3) / 1e12), 2) if name == "c2_p2layer_f16" else None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded N(0,1) x, N(0,1/fan_in) w; no dataset)",
+        "config": {"workload": name, "x": list(wl.x_shape), "w": list(wl.w_shape), "groups": wl.groups,
+                   "stride": wl.stride, "pad": wl.pad, "dilation": wl.dilation, "bias": wl.has_bias,
+                   "layout": wl.layout, "route": route, "kernel": m["kernel"],
+                   "rotation_sets": m["rotation_sets"]},
+        "gb_per_s": round(alg_bytes(wl) / (m["step_ms"] * 1e-3) / 1e9, 1),
+        "kernel_ms": {k: round(m[k], 5) for k in ("kernel_ms_avg", "kernel_ms_median", "kernel_ms_p10",
+                                                   "kernel_ms_p90")},
+        "roofline": roofline(wl, route, m["kernel_ms_avg"], counters_traffic(name, kfile)),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if not args.no_others:
+        others = {}
+        for oname, owl in WORKLOADS.items():
+            if oname == name:
+                continue
+            oroute = route_of(owl)
+            om = measure(owl, max(20, args.steps // 2), 5)
+            rf = roofline(owl, oroute, om["kernel_ms_avg"], counters_traffic(oname, kernel_file(owl, oroute)))
+            others[oname] = {"route": oroute, "kernel": om["kernel"], "ms_per_step": round(om["step_ms"], 5),
+                             "kernel_ms_avg": round(om["kernel_ms_avg"], 5),
+                             "tflops": round(flops(owl) / (om["kernel_ms_avg"] * 1e-3) / 1e12, 3),
+                             "gb_per_s": round(alg_bytes(owl) / (om["kernel_ms_avg"] * 1e-3) / 1e9, 1),
+                             "roofline": rf}
+        out["others"] = others
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

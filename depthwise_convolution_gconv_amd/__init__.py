@@ -8,6 +8,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     GconvError,
     GconvLaunchError,
+    PreparedCall,
     conv2d,
     dwconv1d_btc,
     gconv_fwd,
