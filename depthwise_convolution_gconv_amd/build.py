@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgconv.so")
 
 SOURCES = ["api.cpp", "direct2d.hip", "dw1d_ntc.hip", "igemm.hip"]
-HEADERS = ["common.hpp"]
+HEADERS = ["common.hpp", "fastdiv.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
