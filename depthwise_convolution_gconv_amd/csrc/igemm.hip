@@ -12,29 +12,31 @@
 // traces the slow fp16 grouped conv to grouped convs not reaching the tensor
 // cores; this route puts every group's contraction on the matrix cores.
 //
-// Tile: one workgroup = 4 waves computes BN = WN*32 output channels of one
-// group x BM = 256 consecutive output positions (flattened over n, oh, ow, so a
-// tile may span image boundaries).  Every wave computes all BN channels for 64
-// of the positions: WN x 2 blocks of v_mfma_f32_32x32x16_{f16,bf16}, filters as
-// the A operand (rows = output channels), the im2col tile as the B operand
-// (columns = positions).  Column j of block mb of wave w is tile position
-// 8j + 2w + mb, which keeps the LDS operand reads free of bank conflicts.
+// Tile: one workgroup = 4 waves computes BN = WN*32 output channels of one group
+// x BM = 512 consecutive output positions (flattened over n, oh, ow, so a tile may
+// span image boundaries).  Waves 0-1 take the first 256 positions, waves 2-3 the
+// second 256; within its half, wave w owns the positions 8j + 4*(w&1) + mb for
+// j < 32 and mb < 4.  Every wave computes all BN channels for its 128 positions:
+// WN x 4 blocks of v_mfma_f32_32x32x16_{f16,bf16}, filters as the A operand
+// (rows = output channels), the im2col tile as the B operand (columns =
+// positions).  Per tap a wave reads WN + 4 operand fragments for 4*WN MFMAs, and
+// the lanes of a fragment read halo slots 8 apart, which the LDS map below keeps
+// free of bank conflicts.
 //
 // K loop: input channels in chunks of 16, then taps; one MFMA step = one tap x
-// 16 channels.  Per chunk:
-//  * filters: a small pre-pass (igemm_pack_filters) lays out every (group, filter
-//    tile, chunk) as the exact LDS image, [tap][filter][16 channels]; the main
-//    kernel copies it with plain 16-byte loads and stores;
+// 16 channels.  Chunk c+1 is loaded into registers while chunk c computes:
+//  * filters: one thread per (filter, channel octet) loads the octet's 8 x KH*KW
+//    weights, one contiguous 16-byte aligned run of w, and transposes it with
+//    v_perm into KH*KW tap-major LDS units of 8 channels;
 //  * input: whole zero-padded input rows of the 16 channels, stored as
 //    [row][col][16 channels] so that one MFMA fragment (8 consecutive channels at
-//    one position) is a single 16-byte LDS read; loaded 8 positions at a time per
+//    one position) is a single 16-byte LDS read; loaded VW positions at a time per
 //    channel with buffer loads (out-of-range offsets read as zero, which provides
 //    the padding rows), transposed in registers with v_perm.
-// Epilogue: bias added in fp32, one rounding to the output dtype, the tile staged
-// through LDS and written 16 bytes per lane along W.
+// Epilogue: the bias is the accumulators' initial value (fp32); one rounding to
+// the output dtype; the tile is staged through LDS and written 16 bytes per lane
+// along W, while the next tile's first chunk is still in flight.
 #include <algorithm>
-#include <mutex>
-#include <vector>
 
 #include "common.hpp"
 #include "fastdiv.hpp"
@@ -45,11 +47,14 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;
-constexpr int kCK = 16;            // input channels per K chunk
-constexpr int kLdsBudget = 160 * 1024;  // one workgroup per CU
+constexpr int kCK = 16;                  // input channels per K chunk
+constexpr int kLdsBudget = 160 * 1024;   // one workgroup per CU
+constexpr int kWaves = 4;
+constexpr int kIgThreads = kWaves * 64;
+constexpr int kWM = 4;                   // 32-position MFMA blocks per wave
+constexpr int kBM = 512;                 // positions per tile
+constexpr int kCStride = kBM + 8;        // epilogue LDS row, in elements
 
 template <typename T> struct Mfma;
 template <> struct Mfma<_Float16> {
@@ -67,18 +72,45 @@ template <> struct Mfma<__bf16> {
     }
 };
 
+// 16-bit storage <-> fp32 bits.
+template <typename T> __device__ __forceinline__ float half_bits_to_f32(uint32_t h);
+template <> __device__ __forceinline__ float half_bits_to_f32<_Float16>(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+template <> __device__ __forceinline__ float half_bits_to_f32<__bf16>(uint32_t h)
+{
+    return __builtin_bit_cast(float, h << 16);
+}
+template <typename T> __device__ __forceinline__ uint32_t f32_to_half_bits(float v)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(v));
+}
+
+// Copy of one accumulator (held in an accumulation register) into a VGPR, at this
+// point of the program: without it the register allocator moves every accumulator
+// into VGPRs at once when the K loop ends, which does not fit.
+__device__ __forceinline__ float acc_read(float v)
+{
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+    return r;
+}
+
 struct IgemmGeom {
     int N, C, H, W, Cout, Cg, Ng, OH, OW, KH, KW;
     int sh, sw, ph, pw, dh, dw;
     int Hp;              // H + 2*ph: height of one zero-padded image in the virtual row space
     int NR, WL;          // LDS halo: rows, columns (padded coordinates)
     int xslots;          // NR*WL rounded up to whole 8-slot rows of lds_unit
+    int padl, npad;      // halo columns left of the image; all halo columns outside it
     int nseg;            // W / VW: vector segments per input row
     int xtasks;          // 2 channel octets * NR * nseg
     int P;               // N*OH*OW output positions (< 2^31)
     int m_tiles, n_tiles, groups, nchunks;
     int tiles, tiles_per_xcd;   // m_tiles*n_tiles*groups; ceil(tiles/8)
     int y_vec;           // 1: 8 consecutive positions of a channel are one aligned 16-byte run of y
+    uint32_t w_bytes, b_bytes;
     FastDiv fd_ohw, fd_ow, fd_hp, fd_nseg, fd_nr, fd_mt, fd_nt;
 };
 
@@ -88,8 +120,8 @@ struct IgemmGeom {
 // 256-byte row (8 slots) XORs its unit column with the row number, so 16 slots that
 // lie 8 apart -- in 16 consecutive rows -- land in 16 different columns.  Both hot
 // patterns are of that kind: the staging writes (one slot per 8-wide row segment)
-// and the MFMA operand reads (lanes own positions 8 apart, see igemm_fwd).  The
-// filter image is read 16 consecutive slots at a time: two rows, one per parity.
+// and the MFMA operand reads (lanes own positions 8 apart).  The filter image is
+// read 16 consecutive slots at a time: two rows, one per parity.
 __device__ __forceinline__ int lds_unit(int s, int half)
 {
     const int r = s >> 3;
@@ -107,28 +139,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
-
-// 16 bytes per lane from global memory straight into LDS: lane l writes the LDS
-// bytes [lds_byte + 16*l, +16).  Written as inline assembly so that the compiler
-// does not treat it as an LDS store it must wait for before every later LDS read;
-// the caller waits (vmcnt(0)) before the barrier that publishes the data.  lds_byte
-// must be uniform over the wave.
-__device__ __forceinline__ void dma16(const void *gbase, uint32_t voff, uint32_t lds_byte)
-{
-    // The global base and the LDS address are wave-uniform by construction; make
-    // that explicit so both live in scalar registers as the instruction requires.
-    // readfirstlane works on (signed) int: widen through uint32_t, never sign-extend.
-    const uint64_t b = reinterpret_cast<uint64_t>(gbase);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"((uint32_t)__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(bu)
-                 : "memory");
-}
-
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // VW consecutive 16-bit elements, returned as VW/2 (or 1) dwords.
 template <int VW> struct VecLoad;
@@ -174,7 +184,7 @@ __device__ __forceinline__ uint32_t col_pair(const uint32_t *ra, const uint32_t 
 }
 
 // Writes position v of 8 channel rows d[0..7] as one 16-byte channel octet to halo
-// slot slot0+v (or to the spare slot when v >= limit).
+// slot slot0+v (or to the spare unit when v >= limit).
 template <int VW, int DW, int v>
 __device__ __forceinline__ void write_octets(uint4 *xs, int slot0, int octet, int limit, int dummy,
                                              const uint32_t (*d)[DW])  // dummy: unit index relative to xs
@@ -186,74 +196,46 @@ __device__ __forceinline__ void write_octets(uint4 *xs, int slot0, int octet, in
     if constexpr (v + 1 < VW) write_octets<VW, DW, v + 1>(xs, slot0, octet, limit, dummy, d);
 }
 
-
-// Filters of one (group, filter tile, 16-channel chunk), laid out exactly as the
-// kernel's LDS image (wimg_unit: per tap, two 16-byte channel octets per filter).
-// One thread writes one 16-byte unit (consecutive threads, consecutive units): it
-// inverts wimg_unit to find its (tap, filter, octet) and gathers the 8 channels of
-// that octet.  Filters past Cout/g and channels past C/g are zero.
-__global__ void __launch_bounds__(kThreads)
-igemm_pack_filters(const uint16_t *__restrict__ w, uint4 *__restrict__ wp, int64_t units, int Ng, int Cg,
-                   int KT, int BN, int n_tiles, int nchunks)
+// Dword q of tap t's channel octet, taken from the octet's weights as loaded from
+// w: 8 channels x KT taps, channel-major, two 16-bit values per dword (wr).
+template <int KT, int t, int q>
+__device__ __forceinline__ uint32_t filter_pair(const uint32_t *wr)
 {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= units) return;
-    const int per_chunk = KT * BN * 2;
-    const int u = (int)(i % per_chunk);
-    int64_t r = i / per_chunk;
-    const int ch = (int)(r % nchunks); r /= nchunks;
-    const int nt = (int)(r % n_tiles);
-    const int k = (int)(r / n_tiles);
-    // invert wimg_unit: unit u -> (tap t, filter nn, half)
-    const int t = u / (BN * 2), ut = u % (BN * 2);
-    const int row = ut >> 4;
-    const int col = (ut & 15) ^ (row & 15);
-    const int nn = row * 8 + (col >> 1), octet = col & 1;
-    const int on = nt * BN + nn;
-    uint32_t v[4] = {0, 0, 0, 0};
-    if (on < Ng) {
-        const uint16_t *src = w + ((int64_t)(k * Ng + on) * Cg) * KT + t;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = ch * kCK + octet * 8 + e;
-            const uint32_t h = (c < Cg) ? src[(int64_t)c * KT] : 0u;
-            v[e >> 1] |= h << (16 * (e & 1));
-        }
-    }
-    wp[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    constexpr int a = 2 * q * KT + t;   // channel 2q, tap t
+    constexpr int b = a + KT;           // channel 2q+1, tap t
+    constexpr uint32_t ba = 2 * (a & 1), bb = 2 * (b & 1);
+    constexpr uint32_t sel = ((bb + 5) << 24) | ((bb + 4) << 16) | ((ba + 1) << 8) | ba;
+    return __builtin_amdgcn_perm(wr[b >> 1], wr[a >> 1], sel);
 }
 
-// Workgroup: 4 waves, one per SIMD (the accumulators live in the matrix-core
-// accumulator registers).  Wave w computes every filter of the tile for the
-// positions SR*j + 2*w + mb.
-constexpr int kWaves = 4;
-constexpr int kIgThreads = kWaves * 64;
-constexpr int kMaxXRounds = 1;   // input staging tasks per thread
+template <int KT, int BN, int t>
+__device__ __forceinline__ void write_filters(uint4 *ws, int n, int octet, const uint32_t *wr)
+{
+    ws[wimg_unit(t, BN, n, octet)] = make_uint4(filter_pair<KT, t, 0>(wr), filter_pair<KT, t, 1>(wr),
+                                                filter_pair<KT, t, 2>(wr), filter_pair<KT, t, 3>(wr));
+    if constexpr (t + 1 < KT) write_filters<KT, BN, t + 1>(ws, n, octet, wr);
+}
 
 template <typename T, int WN, int KT, int VW>
 __global__ void __launch_bounds__(kIgThreads, 1)
-igemm_fwd(const T *__restrict__ x, const uint4 *__restrict__ wp, const T *__restrict__ bias,
+igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
           T *__restrict__ y, IgemmGeom g)
 {
-    constexpr int WM = 2;                         // 32-position MFMA blocks per wave
     constexpr int BN = WN * 32;                   // filters per tile (all in every wave)
-    constexpr int BM = 4 * WM * 32;               // positions per tile (256)
-    constexpr int SR = BM / 32;                   // position stride between MFMA columns
     constexpr int DW = VW > 1 ? VW / 2 : 1;       // dwords per staged row segment
+    constexpr int XR = 4 / DW;                    // input staging tasks per thread (<= 32 dwords)
     constexpr int WCHUNK = KT * BN * 2;           // 16-byte units of one chunk's filters
-    constexpr int EROWS = 64;                     // output channels per epilogue pass
-    constexpr int CSTRIDE = BM + 8;               // padded epilogue LDS row (elements)
     extern __shared__ uint4 lds[];
-    // LDS: two pipeline stages [input halo | filter image], one spare unit for
-    // masked-off writes, then the epilogue staging area.
+    // LDS: two pipeline stages [input halo | filter image] and one spare unit for
+    // masked-off writes.  Between tiles the epilogue reuses the whole area.
     const int XU = g.xslots * 2;
     const int SU = XU + WCHUNK;
     const int dummy = 2 * SU;
-    T *ct = reinterpret_cast<T *>(lds + 2 * SU + 1);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave;
     const int half = lane >> 5, l32 = lane & 31;
+    // Tile position of column l32 of this wave's MFMA block 0 (block mb adds mb).
+    const int pbase = 256 * (wave >> 1) + 8 * l32 + 4 * (wave & 1);
     const int OHW = g.OH * g.OW;
     const int HW = g.H * g.W;
 
@@ -271,10 +253,10 @@ igemm_fwd(const T *__restrict__ x, const uint4 *__restrict__ wp, const T *__rest
     // Tile-independent part of this thread's input staging tasks: (channel octet,
     // halo row rr, segment sg) -> VW positions of 8 channels; task i of the thread is
     // tid + i*kIgThreads.
-    int xrr[kMaxXRounds], xsg[kMaxXRounds], xoct[kMaxXRounds], xslot0[kMaxXRounds], xlim[kMaxXRounds];
-    bool xtask[kMaxXRounds];
+    int xrr[XR], xsg[XR], xoct[XR], xslot0[XR], xlim[XR];
+    bool xtask[XR];
 #pragma unroll
-    for (int i = 0; i < kMaxXRounds; ++i) {
+    for (int i = 0; i < XR; ++i) {
         const int tk = tid + i * kIgThreads;
         xtask[i] = tk < g.xtasks;
         xrr[i] = xsg[i] = xoct[i] = xslot0[i] = xlim[i] = 0;
@@ -288,15 +270,32 @@ igemm_fwd(const T *__restrict__ x, const uint4 *__restrict__ wp, const T *__rest
             xlim[i] = min(VW, g.WL - c0);             // elements that land inside the halo
         }
     }
+    // Filter staging task: (filter fn of the tile, channel octet foct).
+    const bool ftask = tid < 2 * BN;
+    const int fn = tid >> 1, foct = tid & 1;
+    const __amdgpu_buffer_rsrc_t wr_rsrc = make_rsrc(w, g.w_bytes);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bias, g.b_bytes);
+
+    // Halo offset of each tap, in slots (wave-uniform).
+    int xoff[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const int kh = t / g.KW, kw = t - kh * g.KW;
+        xoff[t] = kh * g.dh * g.WL + kw * g.dw;
+    }
+    // Filter-image unit of this lane's A fragment of block nb at tap 0.
+    int fu[WN];
+#pragma unroll
+    for (int nb = 0; nb < WN; ++nb) fu[nb] = lds_unit(nb * 32 + l32, half);
 
     // Per-tile state: coordinates, the input buffer resource, this thread's input
     // offset (out of range for rows outside the image, which then read as zeros),
-    // and the packed filters.
+    // and its filter offset (out of range for filters past Cout/g).
     struct TileState {
         int p0, n_first, R_lo, k, nt;
         __amdgpu_buffer_rsrc_t xr;
-        uint32_t xvo[kMaxXRounds];
-        const uint4 *wsrc;
+        uint32_t xvo[XR];
+        uint32_t wvo;
     };
     auto tile_state = [&](int t) {
         TileState ts;
@@ -304,13 +303,13 @@ igemm_fwd(const T *__restrict__ x, const uint4 *__restrict__ wp, const T *__rest
         const int mt = fmod_q(t, bq, g.fd_mt);
         ts.k = fdiv(bq, g.fd_nt);
         ts.nt = fmod_q(bq, ts.k, g.fd_nt);
-        ts.p0 = mt * BM;
+        ts.p0 = mt * kBM;
         ts.n_first = fdiv(ts.p0, g.fd_ohw);
         const int oh_first = fdiv(fmod_q(ts.p0, ts.n_first, g.fd_ohw), g.fd_ow);
         ts.R_lo = ts.n_first * g.Hp + oh_first * g.sh;
         ts.xr = make_rsrc(x + ((int64_t)ts.n_first * g.C + (int64_t)ts.k * g.Cg) * HW, 0x7fffffffu);
 #pragma unroll
-        for (int i = 0; i < kMaxXRounds; ++i) {
+        for (int i = 0; i < XR; ++i) {
             ts.xvo[i] = kOOB;
             if (xtask[i]) {
                 const int R = ts.R_lo + xrr[i];
@@ -321,184 +320,238 @@ igemm_fwd(const T *__restrict__ x, const uint4 *__restrict__ wp, const T *__rest
                                             (int64_t)ih * g.W + xsg[i] * VW) * 2);
             }
         }
-        ts.wsrc = wp + (int64_t)(ts.k * g.n_tiles + ts.nt) * g.nchunks * WCHUNK;
+        const int on = ts.nt * BN + fn;
+        ts.wvo = (ftask && on < g.Ng) ? (uint32_t)(((ts.k * g.Ng + on) * g.Cg + 8 * foct) * KT * 2) : kOOB;
         return ts;
     };
+    // Bias of this lane's accumulator rows: rows nb*32 + 8q + 4*half + (0..3) are
+    // one 8-byte load (Cout/g is a multiple of 4 when there is a bias).
+    auto load_bias = [&](const TileState &ts, uint2 (&bz)[WN][4]) {
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int on = ts.nt * BN + nb * 32 + 8 * q + 4 * half;
+                const uint32_t off = on < g.Ng ? (uint32_t)((ts.k * g.Ng + on) * 2) : kOOB;
+                bz[nb][q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b_rsrc, off, 0, 0));
+            }
+    };
 
-    // Staging for one pipeline step: the filter image goes straight from global
-    // memory into the stage buffer (dma16); 8 channel rows x VW input positions go
-    // through registers, where they are transposed into channel octets.
-    uint32_t d[kMaxXRounds][8][DW];
-#define GCONV_LOAD_STEP(ts_, ch_, stage_)                                                    \
-    do {                                                                                     \
-        const uint4 *wc_ = (ts_).wsrc + (int64_t)(ch_) * WCHUNK;                             \
-        const uint32_t wl_ = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint4 *)((stage_) + XU); \
-        for (int u_ = wave * 64; u_ < WCHUNK; u_ += kIgThreads)                              \
-            dma16(wc_ + u_, (uint32_t)lane * 16u, wl_ + (uint32_t)u_ * 16u);                  \
-        const int ci0_ = (ch_) * kCK;                                                        \
-        _Pragma("unroll") for (int r_ = 0; r_ < kMaxXRounds; ++r_) {                          \
-            if (xtask[r_]) {                                                                 \
-                _Pragma("unroll") for (int e_ = 0; e_ < 8; ++e_) {                           \
-                    const bool ok_ = ci0_ + 8 * xoct[r_] + e_ < g.Cg;                        \
-                    VecLoad<VW>::run((ts_).xr, ok_ ? (ts_).xvo[r_] : kOOB, (uint32_t)(ci0_ + e_) * HW * 2, \
-                                     d[r_][e_]);                                              \
-                }                                                                            \
-            }                                                                                \
-        }                                                                                    \
-    } while (0)
+    // Staging for one pipeline step: 8 channel rows x VW input positions per input
+    // task and one filter octet per filter task go to registers, then (after the
+    // current step's MFMAs) are transposed into the stage's LDS layout.
+    uint32_t d[XR][8][DW];
+    uint32_t wr[KT * 4];
+    // Staging loads.  In the K loop they are issued one or two at a time between
+    // the MFMAs of the taps (all at once, the memory pipeline would stall the wave).
+    // Threads without a task load zeros from an out-of-range offset, so there are no
+    // branches around the loads.
+    constexpr int NXL = XR * 8;                   // input loads per step
+    constexpr int LW = KT > 1 ? (KT + 1) / 2 : 1;  // taps over which a step's loads are spread
+    auto load_x = [&](const TileState &s, int ch, int j) {   // task j/8, channel j%8
+        const int r = j >> 3, e = j & 7;
+        const int ci0 = ch * kCK;
+        const bool ok = ci0 + 8 * xoct[r] + e < g.Cg;
+        VecLoad<VW>::run(s.xr, ok ? s.xvo[r] : kOOB, (uint32_t)(ci0 + e) * HW * 2, d[r][e]);
+    };
+    auto load_w = [&](const TileState &s, int ch, int i) {   // 16-byte piece i of the octet
+        const int ci0 = ch * kCK;
+        const uint32_t wo = (ci0 + 8 * foct < g.Cg) ? s.wvo : kOOB;
+        const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+            wr_rsrc, wo, (uint32_t)(ci0 * KT * 2 + 16 * i), 0));
+        wr[4 * i] = u.x; wr[4 * i + 1] = u.y; wr[4 * i + 2] = u.z; wr[4 * i + 3] = u.w;
+    };
 #define GCONV_WRITE_STEP(stage_)                                                             \
     do {                                                                                     \
-        _Pragma("unroll") for (int r_ = 0; r_ < kMaxXRounds; ++r_)                           \
+        _Pragma("unroll") for (int r_ = 0; r_ < XR; ++r_)                                    \
             if (xtask[r_]) write_octets<VW, DW, 0>((stage_), xslot0[r_], xoct[r_], xlim[r_], \
                                                    dummy - (int)((stage_) - lds), d[r_]);     \
+        if (ftask) write_filters<KT, BN, 0>((stage_) + XU, fn, foct, wr);                    \
     } while (0)
 
-    // Zero both halos once: padding columns are never written by the staging tasks.
+    // Halo columns outside the image (left/right padding) are never written by the
+    // staging tasks; they are zeroed at the start and after every epilogue, which
+    // reuses the LDS.
+    auto zero_pads = [&](int st) {
+        for (int j = tid; j < g.NR * g.npad; j += kIgThreads) {
+            const int row = j / g.npad, pc = j - row * g.npad;
+            const int col = pc < g.padl ? pc : pc - g.padl + g.pw + g.W;
+            const int s = row * g.WL + col;
+            lds[st * SU + lds_unit(s, 0)] = make_uint4(0, 0, 0, 0);
+            lds[st * SU + lds_unit(s, 1)] = make_uint4(0, 0, 0, 0);
+        }
+    };
+
     for (int i = tid; i < XU; i += kIgThreads) {
         lds[i] = make_uint4(0, 0, 0, 0);
         lds[SU + i] = make_uint4(0, 0, 0, 0);
     }
     TileState ts = tile_state(tile);
     __syncthreads();
-    GCONV_LOAD_STEP(ts, 0, lds);
+#pragma unroll
+    for (int j = 0; j < NXL; ++j) load_x(ts, 0, j);
+#pragma unroll
+    for (int i = 0; i < KT; ++i) load_w(ts, 0, i);
     GCONV_WRITE_STEP(lds);
-    wait_vmem_all();
     __syncthreads();
 
     int stage = 0;
     for (;;) {
-        // LDS slot of tap (0,0) for each of this lane's output positions.  Column j
-        // of MFMA block mb of wave column wm is tile position SR*j + WM*wm + mb, so
-        // the 16 lanes of a half-block read halo slots SR apart, which lds_unit
-        // spreads over all 16 bank columns; the epilogue restores position order.
-        int xslot[WM];
+        // LDS slot of tap (0,0) for each of this lane's output positions.
+        int xslot[kWM];
 #pragma unroll
-        for (int mb = 0; mb < WM; ++mb) {
-            const int p = min(ts.p0 + SR * l32 + wm * WM + mb, g.P - 1);
+        for (int mb = 0; mb < kWM; ++mb) {
+            const int p = min(ts.p0 + pbase + mb, g.P - 1);
             const int n = fdiv(p, g.fd_ohw);
             const int q = fmod_q(p, n, g.fd_ohw);
             const int oh = fdiv(q, g.fd_ow), ow = fmod_q(q, oh, g.fd_ow);
             xslot[mb] = (n * g.Hp + oh * g.sh - ts.R_lo) * g.WL + ow * g.sw;
         }
-        f32x16 acc[WN][WM];
+        f32x16 acc[WN][kWM];
 #pragma unroll
-        for (int i = 0; i < WN; ++i)
+        for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
-            for (int j = 0; j < WM; ++j)
+            for (int mb = 0; mb < kWM; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
 
         const int next_tile = tile + nbx;
         const bool has_next_tile = next_tile < t_hi;
         TileState nts = ts;
-        for (int ch = 0; ch < g.nchunks; ++ch) {
-            uint4 *cur = lds + stage * SU;
+        int ch = 0;
+        do {  // nchunks >= 1
+            const uint4 *cur = lds + stage * SU;
             uint4 *nxt = lds + (stage ^ 1) * SU;
             // Fetch the next pipeline step (next chunk, or chunk 0 of the next tile)
             // into registers while this one computes.
             const bool last = ch + 1 == g.nchunks;
             const bool more = !last || has_next_tile;
             if (last && has_next_tile) nts = tile_state(next_tile);
-            if (more) {
-                // One load path: the source is (this tile, ch+1) or (next tile, 0).
-                TileState src;
-                src.xr = last ? nts.xr : ts.xr;
+            // Source of the next pipeline step: (this tile, ch+1) or (next tile, 0);
+            // after the last chunk of the last tile the loads fetch nothing.
+            TileState src;
+            src.xr = last ? nts.xr : ts.xr;
 #pragma unroll
-                for (int i = 0; i < kMaxXRounds; ++i) src.xvo[i] = last ? nts.xvo[i] : ts.xvo[i];
-                src.wsrc = last ? nts.wsrc : ts.wsrc;
-                GCONV_LOAD_STEP(src, last ? 0 : ch + 1, nxt);
-            }
+            for (int i = 0; i < XR; ++i) src.xvo[i] = !more ? kOOB : last ? nts.xvo[i] : ts.xvo[i];
+            src.wvo = !more ? kOOB : last ? nts.wvo : ts.wvo;
+            const int nch = last ? 0 : ch + 1;
             const uint4 *xs = cur;
             const uint4 *ws = cur + XU;
+            // Re-derive the tap addresses in every chunk instead of keeping all
+            // KT x kWM of them live across the loop.
+            int xsl[kWM];
+#pragma unroll
+            for (int mb = 0; mb < kWM; ++mb) {
+                xsl[mb] = xslot[mb];
+                asm volatile("" : "+v"(xsl[mb]));
+            }
             // Operand registers are double-buffered across taps: every LDS read of tap
             // t+1 is issued before the MFMAs of tap t (the scheduling fences keep the
             // compiler from folding the two buffers into one and waiting on each read).
-            uint4 bf[2][WM], af[2][WN];
+            uint4 bf[2][kWM], af[2][WN];
             auto read_tap = [&](int t, int buf) {
-                const int kh = t / g.KW, kw = t - kh * g.KW;
-                const int xoff = kh * g.dh * g.WL + kw * g.dw;
 #pragma unroll
-                for (int mb = 0; mb < WM; ++mb) bf[buf][mb] = xs[lds_unit(xslot[mb] + xoff, half)];
+                for (int mb = 0; mb < kWM; ++mb) bf[buf][mb] = xs[lds_unit(xsl[mb] + xoff[t], half)];
 #pragma unroll
-                for (int nb = 0; nb < WN; ++nb) af[buf][nb] = ws[wimg_unit(t, BN, nb * 32 + l32, half)];
+                for (int nb = 0; nb < WN; ++nb) af[buf][nb] = ws[t * BN * 2 + fu[nb]];
             };
             read_tap(0, 0);
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
                 const int c = t & 1;
                 if (t + 1 < KT) read_tap(t + 1, c ^ 1);
+                // The loads go out during the first LW taps, so the last ones have the
+                // remaining taps to arrive before they are staged.
+                if (t < LW) {
+#pragma unroll
+                    for (int j = t * NXL / LW; j < (t + 1) * NXL / LW; ++j) load_x(src, nch, j);
+#pragma unroll
+                    for (int i = t * KT / LW; i < (t + 1) * KT / LW; ++i) load_w(src, nch, i);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
-                    for (int mb = 0; mb < WM; ++mb) acc[nb][mb] = Mfma<T>::run(af[c][nb], bf[c][mb], acc[nb][mb]);
+                    for (int mb = 0; mb < kWM; ++mb) acc[nb][mb] = Mfma<T>::run(af[c][nb], bf[c][mb], acc[nb][mb]);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            if (more) GCONV_WRITE_STEP(nxt);
-            wait_vmem_all();  // the filter image of the next step has landed in LDS
-            __syncthreads();
-            stage ^= 1;
-        }
-
-        // ---- epilogue: + bias in fp32, one rounding to T, then through the LDS
-        // staging area so that each thread stores 8 consecutive positions of one
-        // output channel (16 bytes).  These stores drain while the next tile computes.
-        const bool vec_ok = g.y_vec && (ts.p0 <= g.P - BM);
-#pragma unroll
-        for (int pass = 0; pass < BN / EROWS; ++pass) {
-            if (pass > 0) __syncthreads();
-#pragma unroll
-            for (int nb = 0; nb < WN; ++nb) {
-                const int nrow = nb * 32;             // tile row of this 32-filter block
-                if (nrow / EROWS != pass) continue;
-#pragma unroll
-                for (int mb = 0; mb < WM; ++mb) {
-                    const int pl = SR * l32 + wm * WM + mb;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int nl = nrow % EROWS + (r >> 2) * 8 + half * 4 + (r & 3);
-                        const int on = ts.nt * BN + pass * EROWS + nl;
-                        float v = acc[nb][mb][r];
-                        if (bias && on < g.Ng) v += to_f32(bias[ts.k * g.Ng + on]);
-                        ct[nl * CSTRIDE + pl] = from_f32<T>(v);
-                    }
-                }
+            if (!last) {
+                GCONV_WRITE_STEP(nxt);
+                __syncthreads();
+                stage ^= 1;
             }
-            __syncthreads();
-            for (int c = tid; c < EROWS * (BM / 8); c += kIgThreads) {
-                const int row = c / (BM / 8), p8 = c % (BM / 8);
-                const int on = ts.nt * BN + pass * EROWS + row;
-                const int p = ts.p0 + p8 * 8;
-                if (on >= g.Ng || p >= g.P) continue;
-                const int co = ts.k * g.Ng + on;
-                const T *src = ct + row * CSTRIDE + p8 * 8;
-                if (vec_ok) {
-                    const int n = fdiv(p, g.fd_ohw);
-                    const int q = fmod_q(p, n, g.fd_ohw);
-                    *reinterpret_cast<uint4 *>(y + ((int64_t)n * g.Cout + co) * OHW + q) =
-                        *reinterpret_cast<const uint4 *>(src);
-                } else {
-                    for (int e = 0; e < 8 && p + e < g.P; ++e) {
-                        const int n = fdiv(p + e, g.fd_ohw);
-                        const int q = fmod_q(p + e, n, g.fd_ohw);
-                        y[((int64_t)n * g.Cout + co) * OHW + q] = src[e];
-                    }
+        } while (++ch < g.nchunks);
+
+        // ---- epilogue: + bias in fp32, one rounding to T, then through LDS so that
+        // each thread stores 8 consecutive positions of one output channel (16 bytes).
+        // The next tile's first chunk is still in registers; it is staged afterwards.
+        __syncthreads();   // every wave is done with the operands of the last chunk
+        uint2 bz[WN][4];
+        if (bias) load_bias(ts, bz);
+        T *ct = reinterpret_cast<T *>(lds);
+        // Converted 16 accumulators at a time (the fences stop the scheduler from
+        // moving every accumulator into VGPRs at once).
+#pragma unroll
+        for (int nb = 0; nb < WN; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if ((r & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+                const int row = nb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                float b0 = 0.0f;
+                if (bias) {
+                    const uint32_t dw = (r & 2) ? bz[nb][r >> 2].y : bz[nb][r >> 2].x;
+                    b0 = half_bits_to_f32<T>((r & 1) ? (dw >> 16) : (dw & 0xffffu));
+                }
+                uint2 v;
+                v.x = f32_to_half_bits<T>(acc_read(acc[nb][0][r]) + b0) |
+                      (f32_to_half_bits<T>(acc_read(acc[nb][1][r]) + b0) << 16);
+                v.y = f32_to_half_bits<T>(acc_read(acc[nb][2][r]) + b0) |
+                      (f32_to_half_bits<T>(acc_read(acc[nb][3][r]) + b0) << 16);
+                *reinterpret_cast<uint2 *>(ct + row * kCStride + pbase) = v;
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        // The next step's loads (issued during the last chunk) have landed by now.
+        // Waiting for them here, before any store is issued, keeps the staging after
+        // the stores from waiting for the stores to drain (the counter is in order).
+        __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+        __syncthreads();
+        for (int c = tid; c < BN * (kBM / 8); c += kIgThreads) {
+            const int row = c / (kBM / 8), p8 = c % (kBM / 8);
+            const int on = ts.nt * BN + row;
+            const int p = ts.p0 + p8 * 8;
+            if (on >= g.Ng || p >= g.P) continue;
+            const int co = ts.k * g.Ng + on;
+            const T *srcp = ct + row * kCStride + p8 * 8;
+            if (g.y_vec) {
+                const int n = fdiv(p, g.fd_ohw);
+                const int q = fmod_q(p, n, g.fd_ohw);
+                *reinterpret_cast<uint4 *>(y + ((int64_t)n * g.Cout + co) * OHW + q) =
+                    *reinterpret_cast<const uint4 *>(srcp);
+            } else {
+                for (int e = 0; e < 8 && p + e < g.P; ++e) {
+                    const int n = fdiv(p + e, g.fd_ohw);
+                    const int q = fmod_q(p + e, n, g.fd_ohw);
+                    y[((int64_t)n * g.Cout + co) * OHW + q] = srcp[e];
                 }
             }
         }
         if (!has_next_tile) break;
+        __syncthreads();   // the staged outputs have been read
+        zero_pads(0);
+        zero_pads(1);
+        GCONV_WRITE_STEP(lds + (stage ^ 1) * SU);
+        __syncthreads();
+        stage ^= 1;
         tile = next_tile;
         ts = nts;
     }
 }
-#undef GCONV_LOAD_STEP
 #undef GCONV_WRITE_STEP
 
 struct Plan {
     IgemmGeom g;
-    int WN, WM, KT, VW;
+    int WN, KT, VW;
     size_t lds;
-    int64_t packed_units;   // 16-byte units of the packed filters
     bool ok;
 };
 
@@ -514,41 +567,61 @@ Plan make_plan(const Conv2dArgs &a)
     g.sh = a.sh; g.sw = a.sw; g.ph = a.ph; g.pw = a.pw; g.dh = a.dh; g.dw = a.dw;
     g.Hp = g.H + 2 * g.ph;
     const int64_t P = a.N * a.OH * a.OW;
-    if (P >= (int64_t(1) << 31) || a.N * (int64_t)g.Hp + a.KH * (int64_t)a.dh + 512 >= (int64_t(1) << 31)) return pl;
+    if (P >= (int64_t(1) << 31) || a.N * (int64_t)g.Hp + a.KH * (int64_t)a.dh + 1024 >= (int64_t(1) << 31)) return pl;
     g.P = (int)P;
     g.groups = (int)a.groups;
     const int64_t KT = a.KH * a.KW;
     if (KT != 1 && KT != 9) return pl;
     pl.KT = (int)KT;
+    // Filters: 8-channel octets of one filter are contiguous runs of 16*KT bytes.
+    if (g.Cg % 8 != 0 || (reinterpret_cast<uintptr_t>(a.w) & 15) != 0) return pl;
+    const int64_t w_bytes = a.Cout * (int64_t)g.Cg * KT * 2;
+    if (w_bytes >= (int64_t(1) << 31)) return pl;
+    g.w_bytes = (uint32_t)w_bytes;
+    // Bias: 4 consecutive filters per 8-byte load.
+    g.b_bytes = 0;
+    if (a.bias) {
+        if (g.Ng % 4 != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 7) != 0) return pl;
+        g.b_bytes = (uint32_t)(a.Cout * 2);
+    }
     pl.WN = g.Ng > 64 ? 4 : 2;                       // 32-filter blocks per wave (= per tile)
-    pl.WM = 2;
-    const int BN = pl.WN * 32, BM = 4 * pl.WM * 32;
+    const int BN = pl.WN * 32;
     // Vector width of the input row loads.
     const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
     pl.VW = (g.W % 8 == 0 && xa % 16 == 0) ? 8 : (g.W % 4 == 0 && xa % 8 == 0) ? 4
           : (g.W % 2 == 0 && xa % 4 == 0) ? 2 : 1;
+    const int DW = pl.VW > 1 ? pl.VW / 2 : 1;
+    const int XR = 4 / DW;
     // Virtual output rows one tile can touch, image boundaries inside them, and
-    // the resulting bound on the virtual padded input rows of its halo.
-    const bool aligned_rows = BM % g.OW == 0;
-    const int64_t V = aligned_rows ? BM / g.OW : (BM - 1) / g.OW + 2;
-    const int64_t crossings = (V <= 1) ? 0 : ((aligned_rows && g.OH % (BM / g.OW) == 0) ? 0 : (V - 2) / g.OH + 1);
+    // the resulting bound on the virtual padded input rows of its halo (never more
+    // than all N*Hp of them).
+    const bool aligned_rows = kBM % g.OW == 0;
+    const int64_t V = aligned_rows ? kBM / g.OW : (kBM - 1) / g.OW + 2;
+    const int64_t crossings = (V <= 1) ? 0 : ((aligned_rows && g.OH % (kBM / g.OW) == 0) ? 0 : (V - 2) / g.OH + 1);
     const int64_t gap = std::max<int64_t>(0, (int64_t)g.Hp - (int64_t)g.OH * g.sh);
-    const int64_t NR = (V - 1) * g.sh + crossings * gap + (int64_t)(g.KH - 1) * g.dh + 1;
+    int64_t NR = (V - 1) * g.sh + crossings * gap + (int64_t)(g.KH - 1) * g.dh + 1;
+    NR = std::min<int64_t>(NR, a.N * (int64_t)g.Hp);
     const int64_t WL = (int64_t)(g.OW - 1) * g.sw + (int64_t)(g.KW - 1) * g.dw + 1;
+    if (NR * WL >= (int64_t(1) << 24)) return pl;
     g.NR = (int)NR; g.WL = (int)WL;
     g.xslots = (int)((NR * WL + 7) / 8 * 8);
+    g.padl = (int)std::min<int64_t>(g.pw, WL);
+    g.npad = g.padl + (int)std::max<int64_t>(0, WL - g.pw - g.W);
     g.nseg = (g.W + pl.VW - 1) / pl.VW;
     const int64_t xtasks = 2 * NR * g.nseg;
-    if (xtasks > (int64_t)kMaxXRounds * kIgThreads) return pl;
+    if (xtasks > (int64_t)XR * kIgThreads) return pl;
     g.xtasks = (int)xtasks;
     // Byte offsets of the staged input, relative to one tile's first image, stay below 2^31.
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 2 >= (int64_t(1) << 31)) return pl;
-    // Two pipeline stages + spare unit + epilogue staging area (64 rows of BM+8 16-bit).
-    pl.lds = (size_t)(2 * ((int64_t)g.xslots * 2 + KT * BN * 2) + 1) * sizeof(uint4) + (size_t)64 * (BM + 8) * 2;
+    // Two pipeline stages + spare unit; the epilogue reuses the same area.
+    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * BN * 2) * sizeof(uint4);
+    pl.lds = 2 * stage_bytes + sizeof(uint4);
+    if (pl.lds > (size_t)kLdsBudget) return pl;
+    pl.lds = std::max(pl.lds, (size_t)BN * kCStride * 2);   // the epilogue uses the whole area
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
-    g.m_tiles = (int)ceil_div(g.P, BM);
+    g.m_tiles = (int)ceil_div(g.P, kBM);
     g.n_tiles = (int)ceil_div(g.Ng, BN);
     g.nchunks = (int)ceil_div(g.Cg, kCK);
     const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.groups;
@@ -562,13 +635,12 @@ Plan make_plan(const Conv2dArgs &a)
     g.fd_nr = make_fastdiv((uint32_t)g.NR);
     g.fd_mt = make_fastdiv((uint32_t)g.m_tiles);
     g.fd_nt = make_fastdiv((uint32_t)g.n_tiles);
-    pl.packed_units = (int64_t)g.groups * g.n_tiles * g.nchunks * KT * BN * 2;
     pl.ok = true;
     return pl;
 }
 
 template <typename T, int WN, int KT, int VW>
-hipError_t run(const Conv2dArgs &a, const Plan &pl, const uint4 *wp)
+hipError_t run(const Conv2dArgs &a, const Plan &pl)
 {
     // Dynamic LDS beyond 64 KB must be allowed explicitly, once per kernel.
     static const hipError_t attr = hipFuncSetAttribute(
@@ -582,102 +654,43 @@ hipError_t run(const Conv2dArgs &a, const Plan &pl, const uint4 *wp)
     if (err != hipSuccess) return err;
     const int64_t blocks = std::min<int64_t>(pl.g.tiles, std::max(cus, 8));
     hipLaunchKernelGGL((igemm_fwd<T, WN, KT, VW>), dim3((unsigned)blocks), dim3(kIgThreads), pl.lds,
-                       a.stream, (const T *)a.x, wp, (const T *)a.bias, (T *)a.y, pl.g);
+                       a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, pl.g);
     return hipGetLastError();
 }
 
 template <typename T, int WN, int KT>
-hipError_t run_vw(const Conv2dArgs &a, const Plan &pl, const uint4 *wp)
+hipError_t run_vw(const Conv2dArgs &a, const Plan &pl)
 {
     switch (pl.VW) {
-    case 8: return run<T, WN, KT, 8>(a, pl, wp);
-    case 4: return run<T, WN, KT, 4>(a, pl, wp);
-    case 2: return run<T, WN, KT, 2>(a, pl, wp);
-    default: return run<T, WN, KT, 1>(a, pl, wp);
+    case 8: return run<T, WN, KT, 8>(a, pl);
+    case 4: return run<T, WN, KT, 4>(a, pl);
+    case 2: return run<T, WN, KT, 2>(a, pl);
+    default: return run<T, WN, KT, 1>(a, pl);
     }
 }
 
 template <typename T, int WN>
-hipError_t run_kt(const Conv2dArgs &a, const Plan &pl, const uint4 *wp)
+hipError_t run_kt(const Conv2dArgs &a, const Plan &pl)
 {
-    return pl.KT == 9 ? run_vw<T, WN, 9>(a, pl, wp) : run_vw<T, WN, 1>(a, pl, wp);
+    return pl.KT == 9 ? run_vw<T, WN, 9>(a, pl) : run_vw<T, WN, 1>(a, pl);
 }
 
 template <typename T>
-hipError_t run_typed(const Conv2dArgs &a, const Plan &pl, const uint4 *wp)
+hipError_t run_typed(const Conv2dArgs &a, const Plan &pl)
 {
-    return pl.WN == 4 ? run_kt<T, 4>(a, pl, wp) : run_kt<T, 2>(a, pl, wp);
+    return pl.WN == 4 ? run_kt<T, 4>(a, pl) : run_kt<T, 2>(a, pl);
 }
 
 }  // namespace
 
 bool igemm_supported(const Conv2dArgs &a) { return make_plan(a).ok; }
 
-namespace {
-
-// Packed-filter workspace, one buffer per (device, stream): calls on one stream are
-// ordered, so they can share a buffer; calls on different streams never do.  A
-// buffer only grows, after the stream has drained the work that used it.
-struct Workspace {
-    int device;
-    hipStream_t stream;
-    void *ptr;
-    size_t bytes;
-};
-std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
-
-hipError_t workspace(hipStream_t stream, size_t bytes, void **out)
-{
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    for (Workspace &w : g_ws) {
-        if (w.device != dev || w.stream != stream) continue;
-        if (w.bytes >= bytes) {
-            *out = w.ptr;
-            return hipSuccess;
-        }
-        err = hipStreamSynchronize(stream);
-        if (err != hipSuccess) return err;
-        err = hipFree(w.ptr);
-        if (err != hipSuccess) return err;
-        w.ptr = nullptr;
-        w.bytes = 0;
-        err = hipMalloc(&w.ptr, bytes);
-        if (err != hipSuccess) return err;
-        w.bytes = bytes;
-        *out = w.ptr;
-        return hipSuccess;
-    }
-    Workspace w{dev, stream, nullptr, 0};
-    err = hipMalloc(&w.ptr, bytes);
-    if (err != hipSuccess) return err;
-    w.bytes = bytes;
-    g_ws.push_back(w);
-    *out = w.ptr;
-    return hipSuccess;
-}
-
-}  // namespace
-
 hipError_t launch_igemm(const Conv2dArgs &a, const char **kname)
 {
     const Plan pl = make_plan(a);
     if (!pl.ok) return hipErrorInvalidValue;
-    void *wsp = nullptr;
-    hipError_t err = workspace(a.stream, (size_t)pl.packed_units * sizeof(uint4), &wsp);
-    if (err != hipSuccess) return err;
-    uint4 *wp = static_cast<uint4 *>(wsp);
-    const int BN = pl.WN * 32;
-    hipLaunchKernelGGL(igemm_pack_filters, dim3((unsigned)ceil_div(pl.packed_units, kThreads)), dim3(kThreads), 0,
-                       a.stream, (const uint16_t *)a.w, wp, pl.packed_units, pl.g.Ng, pl.g.Cg, pl.KT, BN,
-                       pl.g.n_tiles, pl.g.nchunks);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
     *kname = "igemm_fwd_mfma32x32x16";
-    return a.dtype == DT_F16 ? run_typed<_Float16>(a, pl, wp) : run_typed<__bf16>(a, pl, wp);
+    return a.dtype == DT_F16 ? run_typed<_Float16>(a, pl) : run_typed<__bf16>(a, pl);
 }
 
 }  // namespace gconv
