@@ -13,8 +13,9 @@ Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize().  Inputs are seeded synthetic tensors already resident
 in HBM; successive steps rotate over enough copies of the input/output buffers
 (>= 512 MB in total) that a step never finds its operands in the 256 MB
-Infinity Cache.  Each launch is also bracketed by HIP events on the launch
-stream, which gives the kernel's average duration for the roofline object.
+Infinity Cache.  The same calls are also captured into a HIP graph (one per
+buffer set) and replayed; HIP events on the replay stream give the average
+device duration of one launch, which the roofline object uses.
 
 Prints ONE JSON line.  `value` is effective TFLOP/s (2*N*Cout*OH*OW*C/g*KH*KW per
 step, padding taps included, divided by the step time).
@@ -103,7 +104,15 @@ def counters_traffic(wl_name, kernel_file):
 
 
 def measure(wl, steps, warmup, rotate_bytes=512 << 20):
-    """Time `steps` gconv_fwd calls on rotating buffer sets.  Returns a dict."""
+    """Time `steps` gconv_fwd calls on rotating buffer sets.  Returns a dict.
+
+    step_ms: `steps` back-to-back calls from Python (host validation, route
+    selection and launch included), bracketed by one pair of HIP events on the
+    launch stream.  kernel_ms: the same calls captured once into a HIP graph (one
+    call per buffer set) and replayed until about `steps` launches ran, bracketed
+    by HIP events on the replay stream; that is the average device duration of
+    one launch without the host in the loop.  The graph's first replay is checked
+    bit for bit against the eager result of the same buffer set."""
     import torch
     import depthwise_convolution_gconv_amd as gc
     from depthwise_convolution_gconv_amd.workloads import make_inputs
@@ -115,35 +124,63 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20):
     ys = gc.gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
     ws_bytes = alg_bytes(wl)
     nsets = min(32, max(1, math.ceil(rotate_bytes / ws_bytes)))
-    calls = []
+    calls, outs, sets = [], [], []
     for i in range(nsets):
         xi = x if i == 0 else x.clone()
         wi = w if i == 0 else w.clone()
         bi = None if b is None else (b if i == 0 else b.clone())
         yi = torch.empty(ys, dtype=x.dtype, device=dev)
+        outs.append(yi)
+        sets.append((xi, wi, bi, yi))
         calls.append(gc.PreparedCall(xi, wi, bi, yi, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout))
     stream = torch.cuda.current_stream(dev)
     for i in range(warmup):
         calls[i % nsets]()
     kernel = gc.gconv_last_kernel()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ref0 = outs[0].clone()
+
+    # eager: back-to-back calls
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(steps):
-        ev[i][0].record(stream)
         calls[i % nsets]()
-        ev[i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = t_start.elapsed_time(t_end) / steps
-    kms = sorted(a.elapsed_time(b_) for a, b_ in ev)
-    return {"step_ms": step_ms, "kernel_ms_avg": sum(kms) / len(kms), "kernel_ms_median": kms[len(kms) // 2],
-            "kernel_ms_p10": kms[len(kms) // 10], "kernel_ms_p90": kms[(9 * len(kms)) // 10],
+
+    # graph replay: one launch per buffer set, no host work in between
+    gstream = torch.cuda.Stream(dev)
+    gcalls = [gc.PreparedCall(*t, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout, stream=gstream)
+              for t in sets]
+    graph = torch.cuda.CUDAGraph()
+    outs[0].zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gstream):
+        for c in gcalls:
+            c()
+    with torch.cuda.stream(gstream):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(outs[0], ref0):
+        raise RuntimeError("graph replay differs from the eager result")
+    reps = max(1, round(steps / nsets))
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gstream):   # replay() launches on the current stream
+        g0.record(gstream)
+        for _ in range(reps):
+            graph.replay()
+        g1.record(gstream)
+    torch.cuda.synchronize()
+    kernel_ms = g0.elapsed_time(g1) / (reps * nsets)
+    del graph
+    return {"step_ms": step_ms, "kernel_ms_avg": kernel_ms, "graph_launches": reps * nsets,
             "wall_s": wall, "kernel": kernel, "rotation_sets": nsets}
 
 
@@ -266,8 +303,8 @@ def main():
                    "layout": wl.layout, "route": route, "kernel": m["kernel"],
                    "rotation_sets": m["rotation_sets"]},
         "gb_per_s": round(alg_bytes(wl) / (m["step_ms"] * 1e-3) / 1e9, 1),
-        "kernel_ms": {k: round(m[k], 5) for k in ("kernel_ms_avg", "kernel_ms_median", "kernel_ms_p10",
-                                                   "kernel_ms_p90")},
+        "kernel_ms": {"avg_per_launch": round(m["kernel_ms_avg"], 5), "graph_launches": m["graph_launches"],
+                      "how": "HIP graph of one call per buffer set, replayed; events on the replay stream"},
         "roofline": roofline(wl, route, m["kernel_ms_avg"], counters_traffic(name, kfile)),
     }
     if not args.no_cpu:
