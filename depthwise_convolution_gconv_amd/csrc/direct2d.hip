@@ -15,6 +15,13 @@
 //  * direct2d_naive: one thread per output, everything read from global memory.
 //    Used only when a halo tile of one channel does not fit in LDS (huge
 //    dilation or kernel).
+//  * direct2d_g4: fully grouped 3x3 layers with 4 input and 4 output channels
+//    per group (the ResNeXt-style cardinality the neon issue discusses), 16-bit
+//    types, stride 1, dilation 1, padding 0 or 1.  One wave per (image, group)
+//    slab: the slab's 4 channels go to LDS as a zero-bordered [row][col][4]
+//    image (one 8-byte entry per position), and each tap is one 4x4x4 MFMA per
+//    64 positions (16 blocks of 4 positions: the group's 4x4 filter matrix times
+//    the 4 channels of each position), fp32 accumulation.
 #include <algorithm>
 
 #include "common.hpp"
@@ -151,9 +158,165 @@ hipError_t run_tiled(const Conv2dArgs &a, const TiledGeom &g, size_t lds, int64_
     return hipGetLastError();
 }
 
+typedef _Float16 g4_f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 g4_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float g4_f32x4 __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_4x4x4_16b_{f16,bf16}: 16 independent 4x4x4 products per wave.  Block b
+// is lanes 4b..4b+3; lane m holds row m%4 of its block's A (4 k values), lane l
+// holds column l%4 of B (4 k values) and column l%4 of D (4 rows).
+template <typename T> struct Mfma4;
+template <> struct Mfma4<_Float16> {
+    static __device__ __forceinline__ g4_f32x4 run(uint2 a, uint2 b, g4_f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(g4_f16x4, a), __builtin_bit_cast(g4_f16x4, b),
+                                                 c, 0, 0, 0);
+    }
+};
+template <> struct Mfma4<__bf16> {
+    static __device__ __forceinline__ g4_f32x4 run(uint2 a, uint2 b, g4_f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(g4_bf16x4, a),
+                                                     __builtin_bit_cast(g4_bf16x4, b), c, 0, 0, 0);
+    }
+};
+template <typename T> __device__ __forceinline__ uint32_t bits16(T v) { return __builtin_bit_cast(uint16_t, v); }
+
+constexpr int kG4Waves = kThreads / 64;
+constexpr int kG4MaxPos = 1024;   // positions of one padded slab image (8 KB of LDS per wave)
+constexpr int kG4Filters = 36;    // LDS entries of a group's filters: [tap][output][4 inputs]
+
+// One wave per (image, group) slab.  Per tap, the 16 MFMA blocks of a wave each
+// take 4 consecutive output positions: A = the group's 4 x 4 filter matrix at that
+// tap (the same in every block), B = the 4 input channels of each position at the
+// tap's offset (one 8-byte LDS entry per lane), D = the 4 outputs of the lane's
+// position.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+            T *__restrict__ y, int G, int H, int W, int OH, int OW, int ph, int pw, int slabs)
+{
+    extern __shared__ uint2 g4s[];
+    const int HP = H + 2 * ph, WP = W + 2 * pw;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int slab = blockIdx.x * kG4Waves + wave;
+    if (slab >= slabs) return;   // whole wave; this kernel has no workgroup barrier
+    uint2 *xs = g4s + wave * (HP * WP + kG4Filters);
+    uint2 *fs = xs + HP * WP;
+    const int HW = H * W, C = 4 * G;
+    const int n = slab / G, k = slab - n * G;
+    auto wave_sync = [&]() {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // Every global load of the wave is issued before the first is used: the 4
+    // channels of this lane's position pairs (one 32-bit load per channel and
+    // pair; H*W is even), its share of the group's 144 filter values, and the 4
+    // biases.
+    constexpr int kMaxL = kG4MaxPos / 128;
+    const T *xg = x + ((int64_t)n * C + 4 * k) * HW;
+    const T *wg = w + (int64_t)(4 * k) * 36;   // [output o][input c][tap t]
+    const int npair = HW / 2;
+    uint32_t xv[kMaxL][4], wv[3];
+#pragma unroll
+    for (int j = 0; j < kMaxL; ++j) {
+        if (64 * j < npair) {   // uniform; the pair index is clamped, not branched on
+            const int q = min(lane + 64 * j, npair - 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) xv[j][c] = *reinterpret_cast<const uint32_t *>(xg + c * HW + 2 * q);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 3; ++j) wv[j] = bits16(wg[min(lane + 64 * j, 143)]);
+    const T *bp = bias ? bias + 4 * k : wg;   // loaded either way; zero when there is no bias
+    g4_f32x4 b0;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) b0[o] = to_f32(bp[o]);
+    if (!bias) b0 = g4_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
+
+    // The padded image (zero border) with the 4 channels of a position in one
+    // 8-byte entry, and the filters as [tap][output] entries of 4 inputs.
+    for (int i = lane; i < HP * WP; i += 64) xs[i] = make_uint2(0, 0);
+    wave_sync();
+#pragma unroll
+    for (int j = 0; j < kMaxL; ++j) {
+        const int q = lane + 64 * j;
+        if (64 * j < npair && q < npair) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int p = 2 * q + e;
+                const int h = p / W, ww = p - h * W;
+                // half e of each channel's pair: channels (0,1) and (2,3) side by side
+                const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+                xs[(h + ph) * WP + ww + pw] = make_uint2(__builtin_amdgcn_perm(xv[j][1], xv[j][0], sel),
+                                                         __builtin_amdgcn_perm(xv[j][3], xv[j][2], sel));
+            }
+        }
+    }
+    uint16_t *fs16 = reinterpret_cast<uint16_t *>(fs);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int i = lane + 64 * j;
+        if (i < 144) {
+            const int o = i / 36, c = (i / 9) % 4, t = i % 9;
+            fs16[(t * 4 + o) * 4 + c] = (uint16_t)wv[j];
+        }
+    }
+    wave_sync();
+
+    uint2 fa[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) fa[t] = fs[t * 4 + (lane & 3)];
+
+    T *yg = y + ((int64_t)n * C + 4 * k) * OH * OW;
+    for (int p0 = 0; p0 < OH * OW; p0 += 64) {
+        const int p = min(p0 + lane, OH * OW - 1);
+        const int oh = p / OW, ow = p - oh * OW;
+        const uint2 *xp = xs + oh * WP + ow;
+        g4_f32x4 acc = b0;
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) acc = Mfma4<T>::run(fa[kh * 3 + kw], xp[kh * WP + kw], acc);
+        if (p0 + lane < OH * OW) {
+#pragma unroll
+            for (int o = 0; o < 4; ++o) yg[(int64_t)o * OH * OW + p] = from_f32<T>(acc[o]);
+        }
+    }
+}
+
+template <typename T>
+bool g4_applies(const Conv2dArgs &a)
+{
+    if constexpr (sizeof(T) != 2) {
+        return false;
+    } else {
+        const int64_t Cg = a.C / a.groups, Ng = a.Cout / a.groups;
+        return Cg == 4 && Ng == 4 && a.KH == 3 && a.KW == 3 && a.sh == 1 && a.sw == 1 && a.dh == 1 &&
+               a.dw == 1 && a.ph <= 1 && a.pw <= 1 && (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= kG4MaxPos &&
+               (a.H * a.W) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 3) == 0 &&
+               a.N * a.groups < (int64_t(1) << 30);
+    }
+}
+
 template <typename T>
 hipError_t run_typed(const Conv2dArgs &a, const char **kname)
 {
+    if constexpr (sizeof(T) == 2) {
+        if (!g4_applies<T>(a)) goto tiled;
+        const int slabs = (int)(a.N * a.groups);
+        const size_t lds = (size_t)kG4Waves * ((a.H + 2 * a.ph) * (a.W + 2 * a.pw) + kG4Filters) * sizeof(uint2);
+        *kname = "direct2d_g4";
+        hipLaunchKernelGGL((direct2d_g4<T>), dim3((unsigned)ceil_div(slabs, kG4Waves)), dim3(kThreads), lds,
+                           a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
+                           (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, slabs);
+        return hipGetLastError();
+    }
+tiled:
     const int Cg = (int)(a.C / a.groups), Ng = (int)(a.Cout / a.groups);
     TiledGeom g;
     g.C = (int)a.C; g.H = (int)a.H; g.W = (int)a.W; g.Cout = (int)a.Cout;

@@ -55,6 +55,8 @@ SWEEP = [  # N, C, Cout, H, W, K(h,w), groups, stride, pad, dil, bias
     (2, 12, 18, 10, 11, (3, 2), 3, (2, 1), (1, 0), (1, 2), True),  # anisotropic
     (1, 16, 16, 40, 70, (3, 3), 4, 1, 1, 1, True),      # several spatial tiles + ragged edge
     (2, 20, 20, 6, 6, (3, 3), 20, 1, 0, 1, False),      # depthwise, no padding
+    (3, 16, 16, 7, 10, (3, 3), 4, 1, 1, 1, True),       # 4 in / 4 out per group, ragged (16-bit: g4 kernel)
+    (2, 32, 32, 14, 14, (3, 3), 8, 1, 0, 1, True),      # 4 in / 4 out per group, no padding
 ]
 
 
