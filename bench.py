@@ -88,7 +88,8 @@ def source_digest(kernel_file):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-KERNEL_FILES = {"igemm": "igemm.hip", "direct_nchw": "direct2d.hip", "direct_ntc": "dw1d_ntc.hip"}
+KERNEL_FILES = {"igemm": "igemm.hip", "igemm_f32": "igemm_f32.hip", "direct_nchw": "direct2d.hip",
+                "direct_ntc": "dw1d_ntc.hip"}
 
 
 def counters_traffic(wl_name, kernel_file):
@@ -239,7 +240,7 @@ def route_of(wl):
 
 def kernel_file(wl, route):
     if route == "igemm":
-        return KERNEL_FILES["igemm"]
+        return KERNEL_FILES["igemm_f32" if wl.dtype == "f32" else "igemm"]
     return KERNEL_FILES["direct_ntc" if wl.layout == "ntc" else "direct_nchw"]
 
 

@@ -144,7 +144,7 @@ gconv_route_t auto_route(const Geometry &g, gconv_dtype_t dtype, bool igemm_ok)
     if (g.layout == GCONV_LAYOUT_NTC) return GCONV_ROUTE_DIRECT;
     const int64_t Kg = g.Cg_w * g.KH * g.KW;
     const int64_t Ng = g.Cout / g.groups;
-    if (dtype != GCONV_F32 && igemm_ok && Kg >= 64 && Ng >= 16) return GCONV_ROUTE_IGEMM;
+    if (igemm_ok && Kg >= 64 && Ng >= 16) return GCONV_ROUTE_IGEMM;
     return GCONV_ROUTE_DIRECT;
 }
 
@@ -187,13 +187,14 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
     const char *kname = "";
     if (nchw) {
         const gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
-        const bool igemm_ok = gconv::igemm_supported(a);
+        const bool igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
         if (route == GCONV_ROUTE_AUTO) route = auto_route(g, dtype, igemm_ok);
         if (route == GCONV_ROUTE_IGEMM) {
             if (!igemm_ok)
                 return fail(GCONV_ERR_UNSUPPORTED, "the implicit-GEMM route does not cover this geometry "
-                            "or dtype (fp16/bf16 only; halo tile must fit in LDS)");
-            err = gconv::launch_igemm(a, &kname);
+                            "(3x3 or 1x1 kernels, C/g a multiple of 8 (fp16/bf16) or 4 (fp32), halo tile "
+                            "within LDS)");
+            err = dtype == GCONV_F32 ? gconv::launch_igemm_f32(a, &kname) : gconv::launch_igemm(a, &kname);
         } else {
             err = gconv::launch_direct2d(a, &kname);
         }
@@ -252,7 +253,7 @@ gconv_status_t gconv_select_route(const int64_t *x_shape, const int64_t *w_shape
         // A 16-byte aligned dummy filter pointer: the plan only inspects its alignment.
         alignas(16) static const char dummy[16] = {0};
         const gconv::Conv2dArgs a = conv2d_args(g, dummy, dummy, nullptr, nullptr, dtype, nullptr);
-        igemm_ok = gconv::igemm_supported(a);
+        igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
     }
     *route = auto_route(g, dtype, igemm_ok);
     return GCONV_OK;

@@ -48,8 +48,10 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return
 
 // Launchers (each returns the launch status and the kernel name it picked).
 hipError_t launch_direct2d(const Conv2dArgs &a, const char **kname);
-bool igemm_supported(const Conv2dArgs &a);
+bool igemm_supported(const Conv2dArgs &a);            // fp16 / bf16
 hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);
+bool igemm_f32_supported(const Conv2dArgs &a);        // fp32
+hipError_t launch_igemm_f32(const Conv2dArgs &a, const char **kname);
 hipError_t launch_dw1d(const Dw1dArgs &a, const char **kname);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

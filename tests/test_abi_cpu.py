@@ -72,7 +72,7 @@ def test_workload_shapes_and_routes(name):
         assert ys == wl.x_shape
     route = gc.gconv_select_route(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups,
                                   wl.layout, wl.dtype)
-    expected = {"c1_g4_f32": "direct", "c2_p2layer_f32": "direct", "c2_p2layer_f16": "igemm",
+    expected = {"c1_g4_f32": "direct", "c2_p2layer_f32": "igemm", "c2_p2layer_f16": "igemm",
                 "c3_dw1d_btc_f32": "direct", "c4_fullgroup_bf16": "direct", "c5_ensemble_f16": "igemm"}
     assert route == expected[name]
 
@@ -129,8 +129,12 @@ def test_ntc_validation():
     assert _raw_fwd((2, 2, 8), (8, 1, 5), (1,), (0,), (1,), 8, 1, 0) == 2
 
 
-def test_forced_igemm_rejected_for_fp32():
-    assert _raw_fwd((1, 64, 8, 8), (64, 64, 3, 3), (1, 1), (1, 1), (1, 1), 1, 0, 0, route=2) == 3
+def test_forced_igemm_rejected_outside_its_plan():
+    # 5x5 kernels (fp32 and fp16) and fp32 groups of 2 channels are not covered by the
+    # implicit-GEMM plans; forcing the route reports UNSUPPORTED before any launch.
+    assert _raw_fwd((1, 64, 8, 8), (64, 64, 5, 5), (1, 1), (2, 2), (1, 1), 1, 0, 0, route=2) == 3
+    assert _raw_fwd((1, 64, 8, 8), (64, 64, 5, 5), (1, 1), (2, 2), (1, 1), 1, 0, 1, route=2) == 3
+    assert _raw_fwd((1, 64, 8, 8), (64, 2, 3, 3), (1, 1), (1, 1), (1, 1), 32, 0, 0, route=2) == 3
 
 
 def test_zero_batch_enqueues_nothing():

@@ -70,9 +70,9 @@ def test_sweep_vs_oracle(ci, dt):
     b = draw((Co,), 0.01, 9000 + seed, dt) if has_b else None
     r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=p, dilation=d, groups=g)
     routes = ["direct"]
-    if dt != "f32" and gc.gconv_select_route(x.shape, w.shape, s, p, d, g, "nchw", dt) == "igemm":
+    if gc.gconv_select_route(x.shape, w.shape, s, p, d, g, "nchw", dt) == "igemm":
         routes.append("igemm")
-    elif dt != "f32":
+    else:
         try:
             run_conv2d(x, w, b, s, p, d, g, "igemm")
             routes.append("igemm")
