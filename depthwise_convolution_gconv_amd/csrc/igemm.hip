@@ -110,6 +110,7 @@ struct IgemmGeom {
     int m_tiles, n_tiles, groups, nchunks;
     int tiles, tiles_per_xcd;   // m_tiles*n_tiles*groups; ceil(tiles/8)
     int y_vec;           // 1: 8 consecutive positions of a channel are one aligned 16-byte run of y
+    int defer;           // 1: outputs staged in their own LDS area, stored during the next tile
     uint32_t w_bytes, b_bytes;
     FastDiv fd_ohw, fd_ow, fd_hp, fd_nseg, fd_nr, fd_mt, fd_nt;
 };
@@ -361,12 +362,26 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             wr_rsrc, wo, (uint32_t)(ci0 * KT * 2 + 16 * i), 0));
         wr[4 * i] = u.x; wr[4 * i + 1] = u.y; wr[4 * i + 2] = u.z; wr[4 * i + 3] = u.w;
     };
+    // The staged registers count as read here in every thread, also where a task is
+    // off: otherwise the compiler finds their loads still pending later on and waits
+    // for every outstanding memory operation before it reuses those registers.
+    auto consume_staging = [&]() {
+#pragma unroll
+        for (int r = 0; r < XR; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int k = 0; k < DW; ++k) asm volatile("" ::"v"(d[r][e][k]));
+#pragma unroll
+        for (int i = 0; i < KT * 4; ++i) asm volatile("" ::"v"(wr[i]));
+    };
 #define GCONV_WRITE_STEP(stage_)                                                             \
     do {                                                                                     \
         _Pragma("unroll") for (int r_ = 0; r_ < XR; ++r_)                                    \
             if (xtask[r_]) write_octets<VW, DW, 0>((stage_), xslot0[r_], xoct[r_], xlim[r_], \
                                                    dummy - (int)((stage_) - lds), d[r_]);     \
         if (ftask) write_filters<KT, BN, 0>((stage_) + XU, fn, foct, wr);                    \
+        consume_staging();                                                                   \
     } while (0)
 
     // Halo columns outside the image (left/right padding) are never written by the
@@ -380,6 +395,31 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             lds[st * SU + lds_unit(s, 0)] = make_uint4(0, 0, 0, 0);
             lds[st * SU + lds_unit(s, 1)] = make_uint4(0, 0, 0, 0);
         }
+    };
+
+    // Deferred output stores (64-filter tiles whose staged outputs fit in LDS next to
+    // the two stages): a tile's outputs wait in their own LDS area and are stored
+    // while the next tile computes, a few per tap ahead of that tap's loads, so the
+    // output stream overlaps the MFMAs instead of stalling every CU at once.
+    constexpr bool kCanDefer = WN == 2;
+    constexpr int kDefItems = BN * (kBM / 8) / kIgThreads;   // 16-byte stores per thread per tile
+    // 16-byte unit of the staged outputs: their own area after the stages, or the
+    // start of the LDS (then the items are read but never stored, as none is pending).
+    const int ctu = g.defer ? 2 * SU + 1 : 0;
+    int dnext = kDefItems;                                  // nothing pending before the first tile
+    int64_t dy = 0;                                         // this thread's output offset, row 0
+    int drow0 = 0, dlimit = 0;                              // its first row; rows < dlimit are valid
+    // Two items at a time: read from LDS with one tap's operands, stored after that
+    // tap's MFMAs, when the reads have long landed.
+    auto fetch_deferred = [&](int u) {   // item dnext + u (an in-range row past the end)
+        const T *dct = reinterpret_cast<const T *>(lds + ctu);
+        const int row = drow0 + 4 * min(dnext + u, kDefItems - 1);
+        return *reinterpret_cast<const uint4 *>(dct + row * kCStride + (tid & 63) * 8);
+    };
+    auto put_deferred = [&](int u, uint4 v) {
+        const int row = drow0 + 4 * (dnext + u);
+        if (dnext + u < kDefItems && row < dlimit)
+            *reinterpret_cast<uint4 *>(y + dy + (int64_t)row * OHW) = v;
     };
 
     for (int i = tid; i < XU; i += kIgThreads) {
@@ -418,6 +458,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         const int next_tile = tile + nbx;
         const bool has_next_tile = next_tile < t_hi;
         TileState nts = ts;
+        uint2 bz[WN][4];
         int ch = 0;
         do {  // nchunks >= 1
             const uint4 *cur = lds + stage * SU;
@@ -445,9 +486,10 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
                 xsl[mb] = xslot[mb];
                 asm volatile("" : "+v"(xsl[mb]));
             }
-            // Operand registers are double-buffered across taps: every LDS read of tap
-            // t+1 is issued before the MFMAs of tap t (the scheduling fences keep the
-            // compiler from folding the two buffers into one and waiting on each read).
+            // Operand registers are double-buffered across taps: the LDS reads of tap
+            // t+1 are issued among the MFMAs of tap t (the scheduling groups and fences
+            // keep the compiler from folding the two buffers into one and waiting on
+            // each read).
             uint4 bf[2][kWM], af[2][WN];
             auto read_tap = [&](int t, int buf) {
 #pragma unroll
@@ -462,18 +504,40 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
                 if (t + 1 < KT) read_tap(t + 1, c ^ 1);
                 // The loads go out during the first LW taps, so the last ones have the
                 // remaining taps to arrive before they are staged.
+                uint4 dv0, dv1;
                 if (t < LW) {
+                    if (kCanDefer) {
+                        dv0 = fetch_deferred(0);
+                        dv1 = fetch_deferred(1);
+                    }
 #pragma unroll
                     for (int j = t * NXL / LW; j < (t + 1) * NXL / LW; ++j) load_x(src, nch, j);
 #pragma unroll
                     for (int i = t * KT / LW; i < (t + 1) * KT / LW; ++i) load_w(src, nch, i);
+                    // 64-filter tiles: the bias goes out with the last chunk's last loads.
+                    if (kCanDefer && t == LW - 1 && last && bias) load_bias(ts, bz);
                 }
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
                     for (int mb = 0; mb < kWM; ++mb) acc[nb][mb] = Mfma<T>::run(af[c][nb], bf[c][mb], acc[nb][mb]);
+                // Issue order of the tap: each MFMA is followed by one LDS read, a few
+                // vector ALU instructions and one global load of the operands to come,
+                // which then run while the matrix core works (one wave per SIMD leaves
+                // nothing else to fill those cycles).
+#pragma unroll
+                for (int i = 0; i < WN * kWM; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+                }
                 __builtin_amdgcn_sched_barrier(0);
+                if (kCanDefer && t < LW) {
+                    put_deferred(0, dv0);
+                    put_deferred(1, dv1);
+                    dnext = min(dnext + 2, kDefItems);
+                }
             }
             if (!last) {
                 GCONV_WRITE_STEP(nxt);
@@ -485,10 +549,11 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         // ---- epilogue: + bias in fp32, one rounding to T, then through LDS so that
         // each thread stores 8 consecutive positions of one output channel (16 bytes).
         // The next tile's first chunk is still in registers; it is staged afterwards.
+        if (kCanDefer && g.defer)   // the rest of the previous tile
+            for (; dnext < kDefItems; ++dnext) put_deferred(0, fetch_deferred(0));
         __syncthreads();   // every wave is done with the operands of the last chunk
-        uint2 bz[WN][4];
-        if (bias) load_bias(ts, bz);
-        T *ct = reinterpret_cast<T *>(lds);
+        if (!kCanDefer && bias) load_bias(ts, bz);
+        T *ct = reinterpret_cast<T *>(lds + (kCanDefer ? ctu : 0));
         // Converted 16 accumulators at a time (the fences stop the scheduler from
         // moving every accumulator into VGPRs at once).
 #pragma unroll
@@ -510,6 +575,23 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
                 *reinterpret_cast<uint2 *>(ct + row * kCStride + pbase) = v;
             }
         __builtin_amdgcn_sched_barrier(0);
+        if (kCanDefer && g.defer && has_next_tile) {
+            // Stage the next tile's first chunk (its loads were issued during the last
+            // chunk) and leave this tile's outputs for the next tile's taps.
+            GCONV_WRITE_STEP(lds + (stage ^ 1) * SU);
+            __syncthreads();
+            const int p = ts.p0 + (tid & 63) * 8;
+            dnext = 0;
+            drow0 = tid >> 6;
+            dlimit = p < g.P ? min(BN, g.Ng - ts.nt * BN) : 0;
+            const int n = fdiv(min(p, g.P - 1), g.fd_ohw);
+            const int q = fmod_q(min(p, g.P - 1), n, g.fd_ohw);
+            dy = ((int64_t)n * g.Cout + ts.k * g.Ng + ts.nt * BN) * OHW + q;
+            stage ^= 1;
+            tile = next_tile;
+            ts = nts;
+            continue;
+        }
         // The next step's loads (issued during the last chunk) have landed by now.
         // Waiting for them here, before any store is issued, keeps the staging after
         // the stores from waiting for the stores to drain (the counter is in order).
@@ -618,9 +700,13 @@ Plan make_plan(const Conv2dArgs &a)
     const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * BN * 2) * sizeof(uint4);
     pl.lds = 2 * stage_bytes + sizeof(uint4);
     if (pl.lds > (size_t)kLdsBudget) return pl;
-    pl.lds = std::max(pl.lds, (size_t)BN * kCStride * 2);   // the epilogue uses the whole area
-    if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
+    const size_t ct_bytes = (size_t)BN * kCStride * 2;      // staged outputs of one tile
+    g.defer = pl.WN == 2 && g.y_vec && pl.lds + ct_bytes <= (size_t)kLdsBudget;
+    // Deferred stores: the outputs get their own area after the stages; otherwise
+    // the epilogue reuses the whole area.
+    pl.lds = g.defer ? pl.lds + ct_bytes : std::max(pl.lds, ct_bytes);
+    if (pl.lds > (size_t)kLdsBudget) return pl;
     g.m_tiles = (int)ceil_div(g.P, kBM);
     g.n_tiles = (int)ceil_div(g.Ng, BN);
     g.nchunks = (int)ceil_div(g.Cg, kCK);

@@ -88,6 +88,30 @@ def test_sweep_vs_oracle(ci, dt):
         assert normwise(as_f64(outs["igemm"].cpu()), as_f64(outs["direct"].cpu())) <= TOL[dt]
 
 
+# More tiles than the chip runs workgroups (256), so every workgroup of the implicit
+# GEMM takes several tiles in turn; with at most 64 filters per group a tile's outputs
+# are stored while the next tile computes.  Compared in full.
+MANY_TILES = [  # N, C, Cout, H, W, K, groups, bias
+    (4, 128, 128, 56, 56, 3, 16, True),     # 8 filters per group, ragged last tile
+    (16, 256, 1024, 24, 24, 1, 16, True),   # 64 filters per group, 1x1
+    (15, 128, 1024, 24, 24, 3, 16, False),  # 64 filters per group, 3x3, ragged last tile
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(MANY_TILES)))
+def test_igemm_many_tiles_per_workgroup(ci, dt):
+    N, C, Co, H, W, K, g, has_b = MANY_TILES[ci]
+    seed = 30 * ci + {"f16": 1, "bf16": 2}[dt]
+    x = draw((N, C, H, W), 1.0, 7300 + seed, dt)
+    w = draw((Co, C // g, K, K), 1.0 / (C // g * K * K), 8300 + seed, dt)
+    b = draw((Co,), 0.01, 9300 + seed, dt) if has_b else None
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=1, padding=K // 2, dilation=1, groups=g)
+    y = run_conv2d(x, w, b, 1, K // 2, 1, g, "igemm")
+    assert gc.gconv_last_kernel().startswith("igemm")
+    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+
+
 DW_SWEEP = [  # B, T, C, K, stride, pad, dil, bias
     (2, 100, 64, 31, 1, 15, 1, True),
     (3, 37, 300, 3, 1, 1, 1, False),
