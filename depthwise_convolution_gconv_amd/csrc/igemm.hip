@@ -25,9 +25,11 @@
 //
 // K loop: input channels in chunks of 16, then taps; one MFMA step = one tap x
 // 16 channels.  Chunk c+1 is loaded into registers while chunk c computes:
-//  * filters: one thread per (filter, channel octet) loads the octet's 8 x KH*KW
-//    weights, one contiguous 16-byte aligned run of w, and transposes it with
-//    v_perm into KH*KW tap-major LDS units of 8 channels;
+//  * filters: the chunk's 16 channels x KH*KW taps of one filter are one contiguous
+//    run of w; consecutive lanes load consecutive 16-byte pieces of the tile's runs
+//    (a wave reads a few whole runs, not one piece of 64 runs), and each element is
+//    written with a 2-byte LDS store to its place in the tap-major image, where one
+//    16-byte unit is 8 channels of one filter at one tap;
 //  * input: whole zero-padded input rows of the 16 channels, stored as
 //    [row][col][16 channels] so that one MFMA fragment (8 consecutive channels at
 //    one position) is a single 16-byte LDS read; loaded VW positions at a time per
@@ -121,18 +123,19 @@ struct IgemmGeom {
 // 256-byte row (8 slots) XORs its unit column with the row number, so 16 slots that
 // lie 8 apart -- in 16 consecutive rows -- land in 16 different columns.  Both hot
 // patterns are of that kind: the staging writes (one slot per 8-wide row segment)
-// and the MFMA operand reads (lanes own positions 8 apart).  The filter image is
-// read 16 consecutive slots at a time: two rows, one per parity.
+// and the MFMA operand reads (lanes own positions 8 apart).
 __device__ __forceinline__ int lds_unit(int s, int half)
 {
     const int r = s >> 3;
     return (r << 4) + ((2 * (s & 7) + half) ^ (r & 15));
 }
 
-// Filter image: one block of 2*BN units per tap, each laid out by lds_unit over
-// the filter index, so a tap's operand addresses are the tap-0 addresses plus a
-// constant.
-__device__ __forceinline__ int wimg_unit(int t, int BN, int n, int half) { return t * BN * 2 + lds_unit(n, half); }
+// Filter image: per tap, two planes of BN units (channels 0-7, then 8-15 of the
+// chunk), one unit per filter, and one spare unit, so that a tap's operand addresses
+// are the tap-0 addresses plus a constant.  The A-operand reads (32 consecutive
+// filters) are conflict-free; the spare unit staggers the taps across the banks for
+// the 2-byte staging writes.
+template <int BN> constexpr int kTapUnits = 2 * BN + 1;
 
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past num_records: the load returns 0
 
@@ -197,24 +200,31 @@ __device__ __forceinline__ void write_octets(uint4 *xs, int slot0, int octet, in
     if constexpr (v + 1 < VW) write_octets<VW, DW, v + 1>(xs, slot0, octet, limit, dummy, d);
 }
 
-// Dword q of tap t's channel octet, taken from the octet's weights as loaded from
-// w: 8 channels x KT taps, channel-major, two 16-bit values per dword (wr).
-template <int KT, int t, int q>
-__device__ __forceinline__ uint32_t filter_pair(const uint32_t *wr)
+// Writes the filter pieces a thread loaded into the chunk's filter image (wimg, in
+// bytes).  Piece i belongs to filter ff0 + FPT*i of the tile; wdst[u] is the image
+// offset of its element u for filter ff0 (the filter adds 16 bytes per step).  With
+// KT = 1 a piece is one whole unit; otherwise its 8 elements go to 8 (tap, channel)
+// places, 2 bytes each.
+template <int KT, int BN, int NI, int FPT>
+__device__ __forceinline__ void write_filter_pieces(char *wimg, const uint32_t *wdst, int ff0,
+                                                    const uint32_t *wr)
 {
-    constexpr int a = 2 * q * KT + t;   // channel 2q, tap t
-    constexpr int b = a + KT;           // channel 2q+1, tap t
-    constexpr uint32_t ba = 2 * (a & 1), bb = 2 * (b & 1);
-    constexpr uint32_t sel = ((bb + 5) << 24) | ((bb + 4) << 16) | ((ba + 1) << 8) | ba;
-    return __builtin_amdgcn_perm(wr[b >> 1], wr[a >> 1], sel);
-}
-
-template <int KT, int BN, int t>
-__device__ __forceinline__ void write_filters(uint4 *ws, int n, int octet, const uint32_t *wr)
-{
-    ws[wimg_unit(t, BN, n, octet)] = make_uint4(filter_pair<KT, t, 0>(wr), filter_pair<KT, t, 1>(wr),
-                                                filter_pair<KT, t, 2>(wr), filter_pair<KT, t, 3>(wr));
-    if constexpr (t + 1 < KT) write_filters<KT, BN, t + 1>(ws, n, octet, wr);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        if (i + 1 < NI || ff0 + FPT * i < BN) {
+            if constexpr (KT == 1) {
+                *reinterpret_cast<uint4 *>(wimg + wdst[0] + 16 * FPT * i) =
+                    make_uint4(wr[4 * i], wr[4 * i + 1], wr[4 * i + 2], wr[4 * i + 3]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t dw = wr[4 * i + (u >> 1)];
+                    *reinterpret_cast<uint16_t *>(wimg + wdst[u] + 16 * FPT * i) =
+                        (uint16_t)((u & 1) ? (dw >> 16) : dw);
+                }
+            }
+        }
+    }
 }
 
 template <typename T, int WN, int KT, int VW>
@@ -225,7 +235,8 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     constexpr int BN = WN * 32;                   // filters per tile (all in every wave)
     constexpr int DW = VW > 1 ? VW / 2 : 1;       // dwords per staged row segment
     constexpr int XR = 4 / DW;                    // input staging tasks per thread (<= 32 dwords)
-    constexpr int WCHUNK = KT * BN * 2;           // 16-byte units of one chunk's filters
+    constexpr int TSU = kTapUnits<BN>;            // 16-byte units per tap of the filter image
+    constexpr int WCHUNK = KT * TSU;              // 16-byte units of one chunk's filters
     extern __shared__ uint4 lds[];
     // LDS: two pipeline stages [input halo | filter image] and one spare unit for
     // masked-off writes.  Between tiles the epilogue reuses the whole area.
@@ -271,9 +282,24 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             xlim[i] = min(VW, g.WL - c0);             // elements that land inside the halo
         }
     }
-    // Filter staging task: (filter fn of the tile, channel octet foct).
-    const bool ftask = tid < 2 * BN;
-    const int fn = tid >> 1, foct = tid & 1;
+    // Filter staging.  A chunk's filters are BN runs of 16*KT contiguous elements of
+    // w (16 channels x KT taps, channel-major), 2*KT pieces of 16 bytes each; piece fj
+    // of a run holds elements 8fj .. 8fj+7.  Consecutive lanes load consecutive
+    // pieces, so a wave's loads cover a few contiguous runs.  Thread tid takes piece
+    // fj = tid % (2KT) of filters ff0 + FPT*i (ff0 = tid / (2KT), i < NI).
+    constexpr int PPF = 2 * KT;                   // pieces per filter run
+    constexpr int FPT = kIgThreads / PPF;         // filters per step
+    constexpr int NI = (BN + FPT - 1) / FPT;      // steps
+    const int fj = tid % PPF, ff0 = tid / PPF;
+    const bool fact = ff0 < FPT;                  // the last kIgThreads % PPF threads idle
+    // Image offset (bytes) of element u of this thread's piece of filter ff0: element
+    // e = 8fj + u is channel e / KT at tap e % KT.
+    uint32_t wdst[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int e = 8 * fj + u, c = e / KT, t = e - c * KT;
+        wdst[u] = (uint32_t)(((t * TSU + (c >> 3) * BN + ff0) * 16) + (c & 7) * 2);
+    }
     const __amdgpu_buffer_rsrc_t wr_rsrc = make_rsrc(w, g.w_bytes);
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bias, g.b_bytes);
 
@@ -287,13 +313,14 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     // Filter-image unit of this lane's A fragment of block nb at tap 0.
     int fu[WN];
 #pragma unroll
-    for (int nb = 0; nb < WN; ++nb) fu[nb] = lds_unit(nb * 32 + l32, half);
+    for (int nb = 0; nb < WN; ++nb) fu[nb] = half * BN + nb * 32 + l32;
 
     // Per-tile state: coordinates, the input buffer resource, this thread's input
     // offset (out of range for rows outside the image, which then read as zeros),
     // and its filter offset (out of range for filters past Cout/g).
     struct TileState {
         int p0, n_first, R_lo, k, nt;
+        int nf;   // filters of the tile that exist (BN, or fewer in the last n-tile)
         __amdgpu_buffer_rsrc_t xr;
         uint32_t xvo[XR];
         uint32_t wvo;
@@ -321,8 +348,8 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
                                             (int64_t)ih * g.W + xsg[i] * VW) * 2);
             }
         }
-        const int on = ts.nt * BN + fn;
-        ts.wvo = (ftask && on < g.Ng) ? (uint32_t)(((ts.k * g.Ng + on) * g.Cg + 8 * foct) * KT * 2) : kOOB;
+        ts.nf = min(BN, g.Ng - ts.nt * BN);
+        ts.wvo = fact ? (uint32_t)(((ts.k * g.Ng + ts.nt * BN + ff0) * g.Cg) * KT * 2 + 16 * fj) : kOOB;
         return ts;
     };
     // Bias of this lane's accumulator rows: rows nb*32 + 8q + 4*half + (0..3) are
@@ -342,7 +369,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     // task and one filter octet per filter task go to registers, then (after the
     // current step's MFMAs) are transposed into the stage's LDS layout.
     uint32_t d[XR][8][DW];
-    uint32_t wr[KT * 4];
+    uint32_t wr[NI * 4];
     // Staging loads.  In the K loop they are issued one or two at a time between
     // the MFMAs of the taps (all at once, the memory pipeline would stall the wave).
     // Threads without a task load zeros from an out-of-range offset, so there are no
@@ -355,11 +382,13 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         const bool ok = ci0 + 8 * xoct[r] + e < g.Cg;
         VecLoad<VW>::run(s.xr, ok ? s.xvo[r] : kOOB, (uint32_t)(ci0 + e) * HW * 2, d[r][e]);
     };
-    auto load_w = [&](const TileState &s, int ch, int i) {   // 16-byte piece i of the octet
+    auto load_w = [&](const TileState &s, int ch, int i) {   // piece of filter ff0 + FPT*i
         const int ci0 = ch * kCK;
-        const uint32_t wo = (ci0 + 8 * foct < g.Cg) ? s.wvo : kOOB;
+        // The filter exists, and the piece lies in channels < C/g (C/g is a multiple
+        // of 8, so a last chunk of 8 channels holds exactly the pieces fj < KT).
+        const bool ok = ff0 + FPT * i < s.nf && (fj < KT || ci0 + kCK <= g.Cg);
         const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            wr_rsrc, wo, (uint32_t)(ci0 * KT * 2 + 16 * i), 0));
+            wr_rsrc, ok ? s.wvo : kOOB, (uint32_t)((FPT * i * g.Cg + ci0) * KT * 2), 0));
         wr[4 * i] = u.x; wr[4 * i + 1] = u.y; wr[4 * i + 2] = u.z; wr[4 * i + 3] = u.w;
     };
     // The staged registers count as read here in every thread, also where a task is
@@ -373,14 +402,16 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
                 for (int k = 0; k < DW; ++k) asm volatile("" ::"v"(d[r][e][k]));
 #pragma unroll
-        for (int i = 0; i < KT * 4; ++i) asm volatile("" ::"v"(wr[i]));
+        for (int i = 0; i < NI * 4; ++i) asm volatile("" ::"v"(wr[i]));
     };
 #define GCONV_WRITE_STEP(stage_)                                                             \
     do {                                                                                     \
         _Pragma("unroll") for (int r_ = 0; r_ < XR; ++r_)                                    \
             if (xtask[r_]) write_octets<VW, DW, 0>((stage_), xslot0[r_], xoct[r_], xlim[r_], \
                                                    dummy - (int)((stage_) - lds), d[r_]);     \
-        if (ftask) write_filters<KT, BN, 0>((stage_) + XU, fn, foct, wr);                    \
+        if (fact)                                                                            \
+            write_filter_pieces<KT, BN, NI, FPT>(reinterpret_cast<char *>((stage_) + XU),     \
+                                                 wdst, ff0, wr);                             \
         consume_staging();                                                                   \
     } while (0)
 
@@ -431,7 +462,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
     for (int j = 0; j < NXL; ++j) load_x(ts, 0, j);
 #pragma unroll
-    for (int i = 0; i < KT; ++i) load_w(ts, 0, i);
+    for (int i = 0; i < NI; ++i) load_w(ts, 0, i);
     GCONV_WRITE_STEP(lds);
     __syncthreads();
 
@@ -475,6 +506,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
             for (int i = 0; i < XR; ++i) src.xvo[i] = !more ? kOOB : last ? nts.xvo[i] : ts.xvo[i];
             src.wvo = !more ? kOOB : last ? nts.wvo : ts.wvo;
+            src.nf = last ? nts.nf : ts.nf;
             const int nch = last ? 0 : ch + 1;
             const uint4 *xs = cur;
             const uint4 *ws = cur + XU;
@@ -495,7 +527,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
                 for (int mb = 0; mb < kWM; ++mb) bf[buf][mb] = xs[lds_unit(xsl[mb] + xoff[t], half)];
 #pragma unroll
-                for (int nb = 0; nb < WN; ++nb) af[buf][nb] = ws[t * BN * 2 + fu[nb]];
+                for (int nb = 0; nb < WN; ++nb) af[buf][nb] = ws[t * TSU + fu[nb]];
             };
             read_tap(0, 0);
 #pragma unroll
@@ -513,7 +545,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
                     for (int j = t * NXL / LW; j < (t + 1) * NXL / LW; ++j) load_x(src, nch, j);
 #pragma unroll
-                    for (int i = t * KT / LW; i < (t + 1) * KT / LW; ++i) load_w(src, nch, i);
+                    for (int i = t * NI / LW; i < (t + 1) * NI / LW; ++i) load_w(src, nch, i);
                     // 64-filter tiles: the bias goes out with the last chunk's last loads.
                     if (kCanDefer && t == LW - 1 && last && bias) load_bias(ts, bz);
                 }
@@ -697,7 +729,7 @@ Plan make_plan(const Conv2dArgs &a)
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 2 >= (int64_t(1) << 31)) return pl;
     // Two pipeline stages + spare unit; the epilogue reuses the same area.
-    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * BN * 2) * sizeof(uint4);
+    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * (2 * BN + 1)) * sizeof(uint4);
     pl.lds = 2 * stage_bytes + sizeof(uint4);
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
