@@ -13,9 +13,10 @@
 //  * one MFMA consumes 2 channels.  Its k-step s (0..3) pairs channel s (lanes
 //    0-31) with channel 4+s (lanes 32-63), so a lane's operand for all four
 //    k-steps of a tap is element s of one 16-byte LDS read;
-//  * filters: one thread per (filter, channel quad) loads the quad's 4 x KH*KW
-//    weights, one contiguous 16-byte aligned run of w, and picks the per-tap units
-//    out of its registers;
+//  * filters: the chunk's 8 channels x KH*KW taps of one filter are one contiguous
+//    run of w; consecutive lanes load consecutive 16-byte pieces of the tile's runs,
+//    and each float is written with a 4-byte LDS store to its (tap, channel) place
+//    in the image of quad units;
 //  * the epilogue stages 64 output channels at a time in fp32.
 #include <algorithm>
 
@@ -63,7 +64,11 @@ __device__ __forceinline__ int lds_unit(int s, int half)
     return (r << 4) + ((2 * (s & 7) + half) ^ (r & 15));
 }
 
-__device__ __forceinline__ int wimg_unit(int t, int BN, int n, int half) { return t * BN * 2 + lds_unit(n, half); }
+// Filter image: per tap, two planes of BN units (channels 0-3, then 4-7 of the
+// chunk), one unit per filter, and one spare unit that staggers the taps across the
+// banks for the 4-byte staging writes.  The A-operand reads (32 consecutive filters)
+// are conflict-free.
+template <int BN> constexpr int kTapUnitsF32 = 2 * BN + 1;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -109,7 +114,8 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
 {
     constexpr int BN = WN * 32;                   // filters per tile (all in every wave)
     constexpr int XR = 4 / VW;                    // input staging tasks per thread (<= 32 floats)
-    constexpr int WCHUNK = KT * BN * 2;           // 16-byte units of one chunk's filters
+    constexpr int TSU = kTapUnitsF32<BN>;         // 16-byte units per tap of the filter image
+    constexpr int WCHUNK = KT * TSU;              // 16-byte units of one chunk's filters
     extern __shared__ uint4 lds[];
     const int XU = g.xslots * 2;
     const int SU = XU + WCHUNK;
@@ -146,9 +152,24 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
             xlim[i] = min(VW, g.WL - c0);
         }
     }
-    // Filter staging task: (filter fn of the tile, channel quad fq).
-    const bool ftask = tid < 2 * BN;
-    const int fn = tid >> 1, fq = tid & 1;
+    // Filter staging.  A chunk's filters are BN runs of 8*KT contiguous floats of w
+    // (8 channels x KT taps, channel-major), 2*KT pieces of 16 bytes each; piece fj of
+    // a run holds elements 4fj .. 4fj+3.  Consecutive lanes load consecutive pieces,
+    // so a wave's loads cover a few contiguous runs.  Thread tid takes piece
+    // fj = tid % (2KT) of filters ff0 + FPT*i (ff0 = tid / (2KT), i < NI).
+    constexpr int PPF = 2 * KT;                   // pieces per filter run
+    constexpr int FPT = kThreads / PPF;           // filters per step
+    constexpr int NI = (BN + FPT - 1) / FPT;      // steps
+    const int fj = tid % PPF, ff0 = tid / PPF;
+    const bool fact = ff0 < FPT;                  // the last kThreads % PPF threads idle
+    // Image offset (bytes) of element u of this thread's piece of filter ff0: element
+    // e = 4fj + u is channel e / KT at tap e % KT.
+    uint32_t wdst[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int e = 4 * fj + u, c = e / KT, t = e - c * KT;
+        wdst[u] = (uint32_t)(((t * TSU + (c >> 2) * BN + ff0) * 16) + (c & 3) * 4);
+    }
     const __amdgpu_buffer_rsrc_t wr_rsrc = make_rsrc(w, g.w_bytes);
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bias, g.b_bytes);
 
@@ -160,10 +181,11 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
     }
     int fu[WN];
 #pragma unroll
-    for (int nb = 0; nb < WN; ++nb) fu[nb] = lds_unit(nb * 32 + l32, half);
+    for (int nb = 0; nb < WN; ++nb) fu[nb] = half * BN + nb * 32 + l32;
 
     struct TileState {
         int p0, n_first, R_lo, k, nt;
+        int nf;   // filters of the tile that exist (BN, or fewer in the last n-tile)
         __amdgpu_buffer_rsrc_t xr;
         uint32_t xvo[XR];
         uint32_t wvo;
@@ -191,15 +213,15 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
                                             xsg[i] * VW) * 4);
             }
         }
-        const int on = ts.nt * BN + fn;
-        ts.wvo = (ftask && on < g.Ng) ? (uint32_t)(((ts.k * g.Ng + on) * g.Cg + 4 * fq) * KT * 4) : kOOB;
+        ts.nf = min(BN, g.Ng - ts.nt * BN);
+        ts.wvo = fact ? (uint32_t)(((ts.k * g.Ng + ts.nt * BN + ff0) * g.Cg) * KT * 4 + 16 * fj) : kOOB;
         return ts;
     };
 
-    // Staging registers: 8 channel rows x VW positions per input task, and the
-    // 4 x KT weights of one filter quad (channel-major).
+    // Staging registers: 8 channel rows x VW positions per input task, and NI
+    // filter pieces of 4 floats.
     float d[XR][8][VW];
-    float wr[4 * KT];
+    float wr[4 * NI];
     constexpr int NXL = XR * 8;
     constexpr int LW = KT > 1 ? (KT + 1) / 2 : 1;
     auto load_x = [&](const TileState &s, int ch, int j) {   // task j/8, channel j%8
@@ -208,11 +230,13 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
         const bool ok = ci0 + e < g.Cg;
         VecLoadF32<VW>::run(s.xr, ok ? s.xvo[r] : kOOB, (uint32_t)(ci0 + e) * HW * 4, d[r][e]);
     };
-    auto load_w = [&](const TileState &s, int ch, int i) {   // 16-byte piece i of the quad
+    auto load_w = [&](const TileState &s, int ch, int i) {   // piece of filter ff0 + FPT*i
         const int ci0 = ch * kCK;
-        const uint32_t wo = (ci0 + 4 * fq < g.Cg) ? s.wvo : kOOB;
+        // The filter exists, and the piece lies in channels < C/g (C/g is a multiple
+        // of 4, so a last chunk of 4 channels holds exactly the pieces fj < KT).
+        const bool ok = ff0 + FPT * i < s.nf && (fj < KT || ci0 + kCK <= g.Cg);
         const f32x4 u = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            wr_rsrc, wo, (uint32_t)(ci0 * KT * 4 + 16 * i), 0));
+            wr_rsrc, ok ? s.wvo : kOOB, (uint32_t)((FPT * i * g.Cg + ci0) * KT * 4), 0));
         wr[4 * i] = u.x; wr[4 * i + 1] = u.y; wr[4 * i + 2] = u.z; wr[4 * i + 3] = u.w;
     };
     auto write_step = [&](uint4 *st) {
@@ -229,12 +253,35 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
                     __builtin_bit_cast(uint4, f32x4{d[r][4][v], d[r][5][v], d[r][6][v], d[r][7][v]});
             }
         }
-        if (ftask) {
+        if (fact) {
+            // Piece i goes to filter ff0 + FPT*i (16 bytes further per step); with
+            // KT = 1 it is one whole unit, otherwise 4 (tap, channel) places.
+            char *wimg = reinterpret_cast<char *>(st + XU);
 #pragma unroll
-            for (int t = 0; t < KT; ++t)
-                st[XU + wimg_unit(t, BN, fn, fq)] =
-                    __builtin_bit_cast(uint4, f32x4{wr[t], wr[KT + t], wr[2 * KT + t], wr[3 * KT + t]});
+            for (int i = 0; i < NI; ++i) {
+                if (i + 1 < NI || ff0 + FPT * i < BN) {
+                    if constexpr (KT == 1) {
+                        *reinterpret_cast<f32x4 *>(wimg + wdst[0] + 16 * FPT * i) =
+                            f32x4{wr[4 * i], wr[4 * i + 1], wr[4 * i + 2], wr[4 * i + 3]};
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            *reinterpret_cast<float *>(wimg + wdst[u] + 16 * FPT * i) = wr[4 * i + u];
+                    }
+                }
+            }
         }
+        // The staged registers count as read here in every thread, also where a task
+        // is off: otherwise the compiler finds their loads still pending later on and
+        // waits for every outstanding memory operation before it reuses them.
+#pragma unroll
+        for (int r = 0; r < XR; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int v = 0; v < VW; ++v) asm volatile("" ::"v"(d[r][e][v]));
+#pragma unroll
+        for (int i = 0; i < 4 * NI; ++i) asm volatile("" ::"v"(wr[i]));
     };
     auto zero_pads = [&](int st) {
         for (int j = tid; j < g.NR * g.npad; j += kThreads) {
@@ -255,7 +302,7 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
 #pragma unroll
     for (int j = 0; j < NXL; ++j) load_x(ts, 0, j);
 #pragma unroll
-    for (int i = 0; i < KT; ++i) load_w(ts, 0, i);
+    for (int i = 0; i < NI; ++i) load_w(ts, 0, i);
     write_step(lds);
     __syncthreads();
 
@@ -293,6 +340,7 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
 #pragma unroll
             for (int i = 0; i < XR; ++i) src.xvo[i] = !more ? kOOB : last ? nts.xvo[i] : ts.xvo[i];
             src.wvo = !more ? kOOB : last ? nts.wvo : ts.wvo;
+            src.nf = last ? nts.nf : ts.nf;
             const int nch = last ? 0 : ch + 1;
             const uint4 *xs = cur;
             const uint4 *ws = cur + XU;
@@ -307,7 +355,7 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
 #pragma unroll
                 for (int mb = 0; mb < kWM; ++mb) bf[buf][mb] = xs[lds_unit(xsl[mb] + xoff[t], half)];
 #pragma unroll
-                for (int nb = 0; nb < WN; ++nb) af[buf][nb] = ws[t * BN * 2 + fu[nb]];
+                for (int nb = 0; nb < WN; ++nb) af[buf][nb] = ws[t * TSU + fu[nb]];
             };
             read_tap(0, 0);
 #pragma unroll
@@ -318,7 +366,7 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
 #pragma unroll
                     for (int j = t * NXL / LW; j < (t + 1) * NXL / LW; ++j) load_x(src, nch, j);
 #pragma unroll
-                    for (int i = t * KT / LW; i < (t + 1) * KT / LW; ++i) load_w(src, nch, i);
+                    for (int i = t * NI / LW; i < (t + 1) * NI / LW; ++i) load_w(src, nch, i);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -462,7 +510,7 @@ PlanF32 make_plan_f32(const Conv2dArgs &a)
     g.xtasks = (int)xtasks;
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 4 >= (int64_t(1) << 31)) return pl;
-    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * BN * 2) * sizeof(uint4);
+    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * (2 * BN + 1)) * sizeof(uint4);
     pl.lds = std::max(2 * stage_bytes + sizeof(uint4), (size_t)kERows * kCStride * sizeof(float));
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 4 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
