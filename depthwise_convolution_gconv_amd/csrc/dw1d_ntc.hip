@@ -9,12 +9,12 @@
 // one load per input step instead of one per tap, the "single load" the issue's
 // author wanted in place of a loop over the kernel taps.
 //
-// dw1d_btc_tile<T, K, VE>: stride 1, dilation 1, compile-time K.  A persistent
-//   workgroup walks a run of TT x CT tiles; for each it stages the TT + K - 1
-//   input steps in LDS once (16-byte buffer loads, zero outside [0, T)) and each
-//   thread runs a register window over RT outputs of one channel, while the next
-//   tile's loads are in flight.  Tiles are dealt to the XCDs in contiguous runs,
-//   so the halo steps shared by neighbouring tiles come from one L2.
+// dw1d_btc_tile<T, K, VE>: stride 1, dilation 1, compile-time K.  One workgroup
+//   per TT x CT tile: it stages the tile's filters and its TT + K - 1 input steps
+//   in LDS once (16-byte buffer loads, zero outside [0, T)), each thread takes the
+//   K taps of its channel into registers and streams the input steps of its RT
+//   outputs through them.  Tiles are dealt to the XCDs in contiguous runs, so the
+//   halo steps shared by neighbouring tiles come from one L2.
 // dw1d_btc_window<T, K, R>: stride 1, dilation 1, compile-time K, no LDS (used
 //   when the tile kernel's alignment conditions do not hold).
 // dw1d_btc_generic<T>: any K, stride, dilation; one thread per output.
@@ -66,15 +66,11 @@ dw1d_btc_window(const T *__restrict__ x, const T *__restrict__ w, const T *__res
 
 constexpr int kCT = 64;   // channels per tile (one wave's lanes)
 constexpr int kRG = kThreads / kCT;   // thread groups per tile, kRT outputs each
-// Tile shape and schedule, chosen by measurement on the Conformer shape
-// (8 x 1024 x 512, K = 31): 8 outputs per thread (32-step tiles), one LDS buffer
-// and one workgroup per tile, so that many more workgroups than resident slots
-// exist and the hardware overlaps one's loads with another's arithmetic.  (Two
-// buffers with a persistent grid of 2 or 4 workgroups per CU measured slower.)
+// Tile shape, chosen by measurement on the Conformer shape (8 x 1024 x 512, K = 31):
+// 8 outputs per thread (32-step tiles).  64-step tiles measured the same; a
+// persistent grid with double-buffered tiles measured slower.
 constexpr int kRT = 8;                // outputs per thread
 constexpr int kTT = kRG * kRT;        // outputs (steps) per tile
-constexpr int kNB = 1;                // LDS buffers (2: the next tile stages while this one computes)
-constexpr int kBPC = 0;               // resident workgroups per CU the grid is sized for (0: one per tile)
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past num_records: the load returns 0
 
 template <int BYTES> struct RawLoad;
@@ -119,10 +115,13 @@ template <> __device__ __forceinline__ float elem_f32<__bf16>(const uint32_t *d,
     return __builtin_bit_cast(float, (d[e >> 1] >> (16 * (e & 1))) << 16);
 }
 
-// VE: elements per staging load (16 bytes, or one element when C or x is not
-// aligned for that).
+// VE: elements per input staging load (16 bytes, or one element when C or x is not
+// aligned for that).  One workgroup per tile, sized so that every workgroup of the
+// grid is resident at once on the Conformer shape (at most 64 registers a thread, 8
+// workgroups per CU): the loads of all tiles are in flight together and no second
+// round of workgroups waits for the first.
 template <typename T, int K, int VE>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 8)
 dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
               T *__restrict__ y, int T_in, int C, int To, int pad, int tblocks, int cblocks,
               int tiles, int tiles_per_xcd)
@@ -131,97 +130,103 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
     constexpr int VPR = kCT / VE;                  // loads per staged step
     constexpr int NL = (NRW * VPR + kThreads - 1) / kThreads;   // input loads per thread
     constexpr int DW = (VE * sizeof(T) + 3) / 4;
-    constexpr int NW = (kCT * K + kThreads - 1) / kThreads;     // filter loads per thread
-    __shared__ float xs[kNB][NRW][kCT];            // input steps
-    __shared__ float ws[kNB][kCT * K];             // the tile's filters, [channel][tap]
+    constexpr int WVE = 16 / sizeof(T);            // filter elements per 16-byte load
+    constexpr int NWP = (kCT * K + WVE - 1) / WVE; // filter loads per tile
+    constexpr int NW = (NWP + kThreads - 1) / kThreads;         // filter loads per thread
+    // LDS: the tile's input steps, fp32 [step][channel].  The tile's filters (fp32,
+    // [channel][tap]) pass through the same area first.
+    __shared__ float xs[NRW][kCT];
+    float *const ws = &xs[0][0];
+    static_assert(kCT * K <= NRW * kCT, "the filters fit in the input area");
 
-    // Persistent tile walk: workgroup b runs on XCD b % 8, which owns the tiles
-    // [xcd * tiles_per_xcd, ...); its workgroups take them round-robin, so the
-    // tiles in flight on one XCD are neighbours whose halo steps share its L2.
+    // Tile of this workgroup: tiles are dealt to the XCDs in contiguous runs
+    // (workgroup b runs on XCD b % 8), so neighbouring tiles, which share halo steps,
+    // are read through one L2.
     const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
-    const int nbx = ((int)gridDim.x - xcd + 7) >> 3;
-    const int t_hi = min((xcd + 1) * tiles_per_xcd, tiles);
-    int tile = xcd * tiles_per_xcd + rank;
-    if (tile >= t_hi) return;   // uniform over the workgroup
+    const int tile = xcd * tiles_per_xcd + rank;
+    if (tile >= min((xcd + 1) * tiles_per_xcd, tiles)) return;   // uniform over the workgroup
 
     const int tid = threadIdx.x;
     const int lane = tid % kCT, rg = tid / kCT;
+    const int cb = tile % cblocks, tb = (tile / cblocks) % tblocks, bi = tile / (cblocks * tblocks);
+    const int t0 = tb * kTT, c0 = cb * kCT;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(x), (short)0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(w), (short)0, (int)((int64_t)C * K * sizeof(T)), 0x00020000);
 
-    // Loads of one tile into registers: input steps [t0 - pad, t0 - pad + NRW) x
-    // channels [c0, c0 + kCT) (zero outside the sequence and past channel C), and
-    // the tile's filters w[c0 .. c0+kCT), one contiguous run of kCT*K elements.
-    uint32_t d[NL][DW], e[NW];
-    auto load_tile = [&](int t) {
-        const int cb = t % cblocks, tb = (t / cblocks) % tblocks, bi = t / (cblocks * tblocks);
-        const int t0 = tb * kTT, c0 = cb * kCT;
-        const int64_t xbase = (int64_t)bi * T_in * C;
+    // All loads first: the tile's filters w[c0 .. c0+kCT), one contiguous run of
+    // kCT*K elements (zero past the end of w), and input steps [t0 - pad, t0 - pad +
+    // NRW) x channels [c0, c0 + kCT) (zero outside the sequence and past channel C).
+    uint32_t d[NL][DW], e[NW][4];
+    // Filters first: they are waited for (and staged) while the inputs are in flight.
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int i = tid + j * kThreads;
-            const int r = i / VPR, v = i - r * VPR;
-            const int ti = t0 - pad + r, c = c0 + v * VE;
-            const bool ok = i < NRW * VPR && ti >= 0 && ti < T_in && c < C;
-            RawLoad<VE * sizeof(T)>::run(xr, ok ? (uint32_t)((xbase + (int64_t)ti * C + c) * sizeof(T)) : kOOB, d[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            const int i = tid + j * kThreads;
-            RawLoad<sizeof(T)>::run(wrs, i < kCT * K ? (uint32_t)(((int64_t)c0 * K + i) * sizeof(T)) : kOOB, &e[j]);
-        }
-    };
-    auto stage_tile = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < NL; ++j) {
-            const int i = tid + j * kThreads;
-            if (i < NRW * VPR) {
-                const int r = i / VPR, v = i - r * VPR;
-#pragma unroll
-                for (int q = 0; q < VE; ++q) xs[buf][r][v * VE + q] = elem_f32<T>(d[j], q);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NW; ++j) {
-            const int i = tid + j * kThreads;
-            if (i < kCT * K) ws[buf][i] = elem_f32<T>(&e[j], 0);
-        }
-    };
-
-    load_tile(tile);
-    int buf = 0;
-    for (;;) {
-        if (kNB == 1 && buf != 0) __syncthreads();   // single buffer: the last tile is read
-        stage_tile(kNB == 1 ? 0 : buf);
-        __syncthreads();   // buffer `buf` complete; the other buffer is no longer read
-        const int next = tile + nbx;
-        if (next < t_hi) load_tile(next);   // in flight while this tile computes
-
-        const int cb = tile % cblocks, tb = (tile / cblocks) % tblocks, bi = tile / (cblocks * tblocks);
-        const int t0 = tb * kTT, c = cb * kCT + lane;
-        const bool cok = c < C;
-        const float b0 = (bias && cok) ? to_f32(bias[c]) : 0.0f;
-        float wr[K];
-#pragma clang loop unroll(full)
-        for (int k = 0; k < K; ++k) wr[k] = ws[kNB == 1 ? 0 : buf][lane * K + k];
-        float xw[kRT + K - 1];
-#pragma clang loop unroll(full)
-        for (int i = 0; i < kRT + K - 1; ++i) xw[i] = xs[kNB == 1 ? 0 : buf][rg * kRT + i][lane];
-        T *yb = y + ((int64_t)bi * To + t0 + rg * kRT) * C + c;
-        const int rmax = min(kRT, To - (t0 + rg * kRT));
-#pragma clang loop unroll(full)
-        for (int r = 0; r < kRT; ++r) {
-            float acc = b0;
-#pragma clang loop unroll(full)
-            for (int k = 0; k < K; ++k) acc = fmaf(xw[r + k], wr[k], acc);
-            if (cok && r < rmax) yb[(int64_t)r * C] = from_f32<T>(acc);
-        }
-        if (next >= t_hi) break;
-        tile = next;
-        buf = kNB == 1 ? 1 : buf ^ 1;
+    for (int j = 0; j < NW; ++j) {
+        const int i = tid + j * kThreads;
+        RawLoad<16>::run(wrs, i < NWP ? (uint32_t)(((int64_t)c0 * K + (int64_t)i * WVE) * sizeof(T)) : kOOB, e[j]);
     }
+    const int64_t xbase = (int64_t)bi * T_in * C;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int i = tid + j * kThreads;
+        const int r = i / VPR, v = i - r * VPR;
+        const int ti = t0 - pad + r, c = c0 + v * VE;
+        const bool ok = i < NRW * VPR && ti >= 0 && ti < T_in && c < C;
+        RawLoad<VE * sizeof(T)>::run(xr, ok ? (uint32_t)((xbase + (int64_t)ti * C + c) * sizeof(T)) : kOOB, d[j]);
+    }
+
+    // Filters: through LDS into registers (tap k of this thread's channel).
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+#pragma unroll
+        for (int q = 0; q < WVE; ++q) {
+            const int idx = (tid + j * kThreads) * WVE + q;
+            if (idx < kCT * K) ws[idx] = elem_f32<T>(e[j], q);
+        }
+    }
+    __syncthreads();
+    float wr[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wr[k] = ws[lane * K + k];
+    const int c = c0 + lane;
+    const bool cok = c < C;
+    const float b0 = (bias && cok) ? to_f32(bias[c]) : 0.0f;
+    __syncthreads();   // every thread has its taps; the area now takes the inputs
+
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < NRW * VPR) {
+            const int r = i / VPR, v = i - r * VPR;
+#pragma unroll
+            for (int q = 0; q < VE; ++q) xs[r][v * VE + q] = elem_f32<T>(d[j], q);
+        }
+    }
+    __syncthreads();
+
+    // kRT outputs of channel c: input step i of the thread's window feeds output r
+    // through tap i - r.
+    float acc[kRT];
+#pragma unroll
+    for (int r = 0; r < kRT; ++r) acc[r] = b0;
+#pragma unroll
+    for (int i = 0; i < kRT + K - 1; ++i) {
+        // Input steps are read a few at a time (the other resident waves cover the
+        // LDS latency), which keeps the thread within its 64 registers.
+        const float xv = xs[rg * kRT + i][lane];
+#pragma unroll
+        for (int r = 0; r < kRT; ++r)
+            if (i - r >= 0 && i - r < K) acc[r] = fmaf(xv, wr[i - r], acc[r]);
+        // Each step's products are taken here (not sunk to the stores, which would
+        // keep every input step live at once).
+#pragma unroll
+        for (int r = 0; r < kRT; ++r) asm volatile("" : "+v"(acc[r]));
+    }
+    T *yb = y + ((int64_t)bi * To + t0 + rg * kRT) * C + c;
+    const int rmax = min(kRT, To - (t0 + rg * kRT));
+#pragma unroll
+    for (int r = 0; r < kRT; ++r)
+        if (cok && r < rmax) yb[(int64_t)r * C] = from_f32<T>(acc[r]);
 }
 
 template <typename T>
@@ -262,12 +267,7 @@ hipError_t run_tile(const Dw1dArgs &a)
     const int tblocks = (int)ceil_div(a.To, kTT), cblocks = (int)ceil_div(a.C, kCT);
     const int64_t tiles = a.B * tblocks * cblocks;
     const int64_t per_xcd = ceil_div(tiles, 8);
-    // Persistent grid: two workgroups per CU, each walking a run of tiles.
-    int dev = 0, cus = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    const int64_t blocks = kBPC == 0 ? 8 * per_xcd : std::min<int64_t>(tiles, kBPC * (int64_t)std::max(cus, 8));
+    const int64_t blocks = 8 * per_xcd;   // one workgroup per tile (the last XCD's run may be short)
     hipLaunchKernelGGL((dw1d_btc_tile<T, K, VE>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                        (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)a.T, (int)a.C,
                        (int)a.To, a.p, tblocks, cblocks, (int)tiles, (int)per_xcd);
@@ -286,9 +286,11 @@ template <typename T>
 hipError_t run_typed(const Dw1dArgs &a, const char **kname)
 {
     // Tile kernel: stride 1, dilation 1, one batch's input addressable by a 31-bit
-    // byte offset, tile indices in int.
+    // byte offset, tile indices in int, w 16-byte aligned (its filter loads are 16
+    // bytes wide).
     const int64_t tiles = a.B * ceil_div(a.To, kTT) * ceil_div(a.C, kCT);
     if (a.s == 1 && a.d == 1 && a.B * a.T * a.C * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
+        (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && a.C * a.K * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
         8 * ceil_div(tiles, 8) < (int64_t(1) << 31) && a.T + a.K < (int64_t(1) << 30)) {
         *kname = "dw1d_btc_tile";
         switch (a.K) {
