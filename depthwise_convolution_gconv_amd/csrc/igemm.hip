@@ -39,6 +39,7 @@
 // the output dtype; the tile is staged through LDS and written 16 bytes per lane
 // along W, while the next tile's first chunk is still in flight.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "fastdiv.hpp"
@@ -84,9 +85,18 @@ template <> __device__ __forceinline__ float half_bits_to_f32<__bf16>(uint32_t h
 {
     return __builtin_bit_cast(float, h << 16);
 }
-template <typename T> __device__ __forceinline__ uint32_t f32_to_half_bits(float v)
+// Two fp32 values rounded (to nearest even) into one dword of T, a in the low half:
+// one v_cvt_pk_{f16,bf16}_f32.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b)
 {
-    return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(v));
+    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+}
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
 }
 
 // Copy of one accumulator (held in an accumulation register) into a VGPR, at this
@@ -587,26 +597,31 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         if (!kCanDefer && bias) load_bias(ts, bz);
         T *ct = reinterpret_cast<T *>(lds + (kCanDefer ? ctu : 0));
         // Converted 16 accumulators at a time (the fences stop the scheduler from
-        // moving every accumulator into VGPRs at once).
+        // moving every accumulator into VGPRs at once), two per packed conversion;
+        // the bias add is compiled only into the loop that has a bias.
+        auto write_ct = [&](auto has_bias) {
 #pragma unroll
-        for (int nb = 0; nb < WN; ++nb)
+            for (int nb = 0; nb < WN; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if ((r & 3) == 0) __builtin_amdgcn_sched_barrier(0);
-                const int row = nb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-                float b0 = 0.0f;
-                if (bias) {
-                    const uint32_t dw = (r & 2) ? bz[nb][r >> 2].y : bz[nb][r >> 2].x;
-                    b0 = half_bits_to_f32<T>((r & 1) ? (dw >> 16) : (dw & 0xffffu));
+                for (int r = 0; r < 16; ++r) {
+                    if ((r & 3) == 0) __builtin_amdgcn_sched_barrier(0);
+                    const int row = nb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+                    float v0 = acc_read(acc[nb][0][r]), v1 = acc_read(acc[nb][1][r]);
+                    float v2 = acc_read(acc[nb][2][r]), v3 = acc_read(acc[nb][3][r]);
+                    if constexpr (decltype(has_bias)::value) {
+                        const uint32_t dw = (r & 2) ? bz[nb][r >> 2].y : bz[nb][r >> 2].x;
+                        const float b0 = half_bits_to_f32<T>((r & 1) ? (dw >> 16) : (dw & 0xffffu));
+                        v0 += b0; v1 += b0; v2 += b0; v3 += b0;
+                    }
+                    *reinterpret_cast<uint2 *>(ct + row * kCStride + pbase) =
+                        make_uint2(pack2<T>(v0, v1), pack2<T>(v2, v3));
                 }
-                uint2 v;
-                v.x = f32_to_half_bits<T>(acc_read(acc[nb][0][r]) + b0) |
-                      (f32_to_half_bits<T>(acc_read(acc[nb][1][r]) + b0) << 16);
-                v.y = f32_to_half_bits<T>(acc_read(acc[nb][2][r]) + b0) |
-                      (f32_to_half_bits<T>(acc_read(acc[nb][3][r]) + b0) << 16);
-                *reinterpret_cast<uint2 *>(ct + row * kCStride + pbase) = v;
-            }
-        __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        if (bias)
+            write_ct(std::true_type{});
+        else
+            write_ct(std::false_type{});
         if (kCanDefer && g.defer && has_next_tile) {
             // Stage the next tile's first chunk (its loads were issued during the last
             // chunk) and leave this tile's outputs for the next tile's taps.
