@@ -644,19 +644,28 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         // the stores from waiting for the stores to drain (the counter is in order).
         __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
         __syncthreads();
-        for (int c = tid; c < BN * (kBM / 8); c += kIgThreads) {
-            const int row = c / (kBM / 8), p8 = c % (kBM / 8);
-            const int on = ts.nt * BN + row;
-            const int p = ts.p0 + p8 * 8;
-            if (on >= g.Ng || p >= g.P) continue;
-            const int co = ts.k * g.Ng + on;
-            const T *srcp = ct + row * kCStride + p8 * 8;
-            if (g.y_vec) {
-                const int n = fdiv(p, g.fd_ohw);
-                const int q = fmod_q(p, n, g.fd_ohw);
-                *reinterpret_cast<uint4 *>(y + ((int64_t)n * g.Cout + co) * OHW + q) =
-                    *reinterpret_cast<const uint4 *>(srcp);
-            } else {
+        if (g.y_vec) {
+            // A thread stores the same 8 positions (one 16-byte run of y) of every
+            // kRowStep-th filter row, so the position arithmetic is done once.
+            constexpr int kRowStep = kIgThreads / (kBM / 8);
+            const int p = ts.p0 + (tid % (kBM / 8)) * 8;
+            const int nrow = p < g.P ? min(BN, g.Ng - ts.nt * BN) : 0;
+            const int n = fdiv(min(p, g.P - 1), g.fd_ohw);
+            const int q = fmod_q(min(p, g.P - 1), n, g.fd_ohw);
+            T *yp = y + ((int64_t)n * g.Cout + ts.k * g.Ng + ts.nt * BN) * OHW + q;
+            const T *cp = ct + (tid % (kBM / 8)) * 8;
+#pragma unroll 4
+            for (int row = tid / (kBM / 8); row < nrow; row += kRowStep)
+                *reinterpret_cast<uint4 *>(yp + (int64_t)row * OHW) =
+                    *reinterpret_cast<const uint4 *>(cp + row * kCStride);
+        } else {
+            for (int c = tid; c < BN * (kBM / 8); c += kIgThreads) {
+                const int row = c / (kBM / 8), p8 = c % (kBM / 8);
+                const int on = ts.nt * BN + row;
+                const int p = ts.p0 + p8 * 8;
+                if (on >= g.Ng || p >= g.P) continue;
+                const int co = ts.k * g.Ng + on;
+                const T *srcp = ct + row * kCStride + p8 * 8;
                 for (int e = 0; e < 8 && p + e < g.P; ++e) {
                     const int n = fdiv(p + e, g.fd_ohw);
                     const int q = fmod_q(p + e, n, g.fd_ohw);
