@@ -114,7 +114,7 @@ struct IgemmGeom {
     int sh, sw, ph, pw, dh, dw;
     int Hp;              // H + 2*ph: height of one zero-padded image in the virtual row space
     int NR, WL;          // LDS halo: rows, columns (padded coordinates)
-    int xslots;          // NR*WL rounded up to whole 8-slot rows of lds_unit
+    int xslots;          // NR*WL rounded up to a multiple of 8
     int padl, npad;      // halo columns left of the image; all halo columns outside it
     int nseg;            // W / VW: vector segments per input row
     int xtasks;          // 2 channel octets * NR * nseg
@@ -128,17 +128,16 @@ struct IgemmGeom {
 };
 
 // LDS placement of the 16-byte half `half` (channels 0-7 or 8-15) of 32-byte slot
-// `s`, in 16-byte units.  The LDS has 64 banks of 4 bytes, so a 16-byte access by 16
-// lanes is conflict-free when the lanes hit 16 distinct units modulo 16.  Each
-// 256-byte row (8 slots) XORs its unit column with the row number, so 16 slots that
-// lie 8 apart -- in 16 consecutive rows -- land in 16 different columns.  Both hot
-// patterns are of that kind: the staging writes (one slot per 8-wide row segment)
-// and the MFMA operand reads (lanes own positions 8 apart).
-__device__ __forceinline__ int lds_unit(int s, int half)
-{
-    const int r = s >> 3;
-    return (r << 4) + ((2 * (s & 7) + half) ^ (r & 15));
-}
+// `s`, in 16-byte units: slots in order, with one spare unit after every 8 slots.
+// The LDS has 64 banks of 4 bytes, so a 16-byte access by 16 lanes is conflict-free
+// when the lanes hit 16 distinct units modulo 16.  Slots 8 apart are 17 units apart,
+// so 16 such slots land on 16 different units modulo 16; slots 4 apart alternate
+// between +8 and +9.  The hot patterns are of those kinds: the staging writes (one
+// slot per row segment of 8 or 4) and the MFMA operand reads (lanes own positions 8
+// apart).  Reading a tap's operand costs an add, a shift and a multiply-add.
+__device__ __forceinline__ int lds_unit(int s, int half) { return 2 * s + half + (s >> 3); }
+// 16-byte units of a halo of `slots` slots (a multiple of 8).
+__host__ __device__ inline int halo_units(int slots) { return 2 * slots + slots / 8; }
 
 // Filter image: per tap, two planes of BN units (channels 0-7, then 8-15 of the
 // chunk), one unit per filter, and one spare unit, so that a tap's operand addresses
@@ -250,7 +249,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     extern __shared__ uint4 lds[];
     // LDS: two pipeline stages [input halo | filter image] and one spare unit for
     // masked-off writes.  Between tiles the epilogue reuses the whole area.
-    const int XU = g.xslots * 2;
+    const int XU = halo_units(g.xslots);
     const int SU = XU + WCHUNK;
     const int dummy = 2 * SU;
 
@@ -753,7 +752,7 @@ Plan make_plan(const Conv2dArgs &a)
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 2 >= (int64_t(1) << 31)) return pl;
     // Two pipeline stages + spare unit; the epilogue reuses the same area.
-    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * (2 * BN + 1)) * sizeof(uint4);
+    const size_t stage_bytes = (size_t)((int64_t)halo_units(g.xslots) + KT * (2 * BN + 1)) * sizeof(uint4);
     pl.lds = 2 * stage_bytes + sizeof(uint4);
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
