@@ -139,12 +139,15 @@ __device__ __forceinline__ int lds_unit(int s, int half) { return 2 * s + half +
 // 16-byte units of a halo of `slots` slots (a multiple of 8).
 __host__ __device__ inline int halo_units(int slots) { return 2 * slots + slots / 8; }
 
-// Filter image: per tap, two planes of BN units (channels 0-7, then 8-15 of the
-// chunk), one unit per filter, and one spare unit, so that a tap's operand addresses
-// are the tap-0 addresses plus a constant.  The A-operand reads (32 consecutive
-// filters) are conflict-free; the spare unit staggers the taps across the banks for
-// the 2-byte staging writes.
-template <int BN> constexpr int kTapUnits = 2 * BN + 1;
+// Filter image: per tap, two planes (channels 0-7, then 8-15 of the chunk) of one
+// unit per filter, so that a tap's operand addresses are the tap-0 addresses plus a
+// constant.  The A-operand reads (32 consecutive filters of one plane) are
+// conflict-free.  The planes are BN + 4 units apart and the taps 2(BN + 4) + 1: with
+// these strides the 2-byte staging writes of a wave (about 3.5 filters x 16 channels
+// x 9 taps, each element to its (tap, channel) place) hit each bank at most twice,
+// against four times with unpadded planes and one spare unit per tap.
+template <int BN> constexpr int kPlaneUnits = BN + 4;
+template <int BN> constexpr int kTapUnits = 2 * kPlaneUnits<BN> + 1;
 
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past num_records: the load returns 0
 
@@ -245,6 +248,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     constexpr int DW = VW > 1 ? VW / 2 : 1;       // dwords per staged row segment
     constexpr int XR = 4 / DW;                    // input staging tasks per thread (<= 32 dwords)
     constexpr int TSU = kTapUnits<BN>;            // 16-byte units per tap of the filter image
+    constexpr int BP = kPlaneUnits<BN>;           // 16-byte units between its two channel planes
     constexpr int WCHUNK = KT * TSU;              // 16-byte units of one chunk's filters
     extern __shared__ uint4 lds[];
     // LDS: two pipeline stages [input halo | filter image] and one spare unit for
@@ -307,7 +311,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         const int e = 8 * fj + u, c = e / KT, t = e - c * KT;
-        wdst[u] = (uint32_t)(((t * TSU + (c >> 3) * BN + ff0) * 16) + (c & 7) * 2);
+        wdst[u] = (uint32_t)(((t * TSU + (c >> 3) * BP + ff0) * 16) + (c & 7) * 2);
     }
     const __amdgpu_buffer_rsrc_t wr_rsrc = make_rsrc(w, g.w_bytes);
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(bias, g.b_bytes);
@@ -322,7 +326,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     // Filter-image unit of this lane's A fragment of block nb at tap 0.
     int fu[WN];
 #pragma unroll
-    for (int nb = 0; nb < WN; ++nb) fu[nb] = half * BN + nb * 32 + l32;
+    for (int nb = 0; nb < WN; ++nb) fu[nb] = half * BP + nb * 32 + l32;
 
     // Per-tile state: coordinates, the input buffer resource, this thread's input
     // offset (out of range for rows outside the image, which then read as zeros),
@@ -752,7 +756,7 @@ Plan make_plan(const Conv2dArgs &a)
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 2 >= (int64_t(1) << 31)) return pl;
     // Two pipeline stages + spare unit; the epilogue reuses the same area.
-    const size_t stage_bytes = (size_t)((int64_t)halo_units(g.xslots) + KT * (2 * BN + 1)) * sizeof(uint4);
+    const size_t stage_bytes = (size_t)((int64_t)halo_units(g.xslots) + KT * (2 * (BN + 4) + 1)) * sizeof(uint4);
     pl.lds = 2 * stage_bytes + sizeof(uint4);
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
