@@ -43,7 +43,7 @@ struct GeomF32 {
     int sh, sw, ph, pw, dh, dw;
     int Hp;              // H + 2*ph: height of one zero-padded image in the virtual row space
     int NR, WL;          // LDS halo: rows, columns (padded coordinates)
-    int xslots;          // NR*WL rounded up to whole 8-slot rows of lds_unit
+    int xslots;          // NR*WL rounded up to a multiple of 8
     int padl, npad;      // halo columns left of the image; all halo columns outside it
     int nseg;            // W / VW: vector segments per input row
     int xtasks;          // NR * nseg
@@ -55,14 +55,12 @@ struct GeomF32 {
     FastDiv fd_ohw, fd_ow, fd_hp, fd_nseg, fd_mt, fd_nt;
 };
 
-// Same LDS map as the 16-bit kernel: 16-byte unit `half` of 32-byte slot `s`, with
-// the unit column XORed by the 256-byte row so that 16 slots 8 apart (and 16
-// consecutive slots, one row per parity) hit 16 different bank groups.
-__device__ __forceinline__ int lds_unit(int s, int half)
-{
-    const int r = s >> 3;
-    return (r << 4) + ((2 * (s & 7) + half) ^ (r & 15));
-}
+// Same LDS map as the 16-bit kernel: 16-byte unit `half` of 32-byte slot `s`, slots
+// in order with one spare unit after every 8 slots, so that 16 slots 8 apart (or 4
+// apart) hit 16 different bank groups.
+__device__ __forceinline__ int lds_unit(int s, int half) { return 2 * s + half + (s >> 3); }
+// 16-byte units of a halo of `slots` slots (a multiple of 8).
+__host__ __device__ inline int halo_units_f32(int slots) { return 2 * slots + slots / 8; }
 
 // Filter image: per tap, two planes of BN units (channels 0-3, then 4-7 of the
 // chunk), one unit per filter, and one spare unit that staggers the taps across the
@@ -117,7 +115,7 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
     constexpr int TSU = kTapUnitsF32<BN>;         // 16-byte units per tap of the filter image
     constexpr int WCHUNK = KT * TSU;              // 16-byte units of one chunk's filters
     extern __shared__ uint4 lds[];
-    const int XU = g.xslots * 2;
+    const int XU = halo_units_f32(g.xslots);
     const int SU = XU + WCHUNK;
     const int dummy = 2 * SU;
 
@@ -510,7 +508,7 @@ PlanF32 make_plan_f32(const Conv2dArgs &a)
     g.xtasks = (int)xtasks;
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 4 >= (int64_t(1) << 31)) return pl;
-    const size_t stage_bytes = (size_t)((int64_t)g.xslots * 2 + KT * (2 * BN + 1)) * sizeof(uint4);
+    const size_t stage_bytes = (size_t)((int64_t)halo_units_f32(g.xslots) + KT * (2 * BN + 1)) * sizeof(uint4);
     pl.lds = std::max(2 * stage_bytes + sizeof(uint4), (size_t)kERows * kCStride * sizeof(float));
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 4 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
