@@ -222,9 +222,12 @@ def cpu_baseline(wl, target_s=10.0):
             oracle.dwconv1d_btc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation)
         return time.perf_counter() - t0
 
-    probe = 4096
-    dt = run(probe)
-    n = int(min(max(probe, probe * target_s / max(dt, 1e-6)), 50_000_000))
+    # Size the sample in two steps: a tiny first probe is dominated by the thread
+    # start-up, so a second one of about a second sets the rate.
+    n, dt = 4096, 0.0
+    for goal in (1.0, target_s):
+        dt = run(n)
+        n = int(min(max(n, n * goal / max(dt, 1e-6)), 50_000_000))
     dt = run(n)
     return {"value": round(per_point * n / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
