@@ -57,6 +57,9 @@ SWEEP = [  # N, C, Cout, H, W, K(h,w), groups, stride, pad, dil, bias
     (2, 20, 20, 6, 6, (3, 3), 20, 1, 0, 1, False),      # depthwise, no padding
     (3, 16, 16, 7, 10, (3, 3), 4, 1, 1, 1, True),       # 4 in / 4 out per group, ragged (16-bit: g4 kernel)
     (2, 32, 32, 14, 14, (3, 3), 8, 1, 0, 1, True),      # 4 in / 4 out per group, no padding
+    (2, 48, 96, 9, 9, (3, 3), 2, 1, 1, 1, True),        # 24 in per group: a last chunk of 8 channels; 48 filters
+    (2, 48, 96, 6, 7, (1, 1), 2, 1, 0, 1, True),        # the same with 1x1 filters
+    (2, 24, 32, 9, 9, (3, 3), 2, 1, 1, 1, True),        # 12 in per group: a last fp32 chunk of 4 channels
 ]
 
 
@@ -135,6 +138,28 @@ def test_dw1d_sweep_vs_oracle(ci, dt):
     y = gc.dwconv1d_btc(gpu(x), gpu(w), gpu(b), stride=s, padding=p, dilation=d)
     torch.cuda.synchronize()
     assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+
+
+def test_dw1d_unaligned_filters_use_the_window_kernel():
+    # The tile kernel reads the filters 16 bytes at a time; filters that start 4 bytes
+    # past an aligned address go to the window kernel, with the same result.
+    B_, T, C, K = 2, 70, 64, 31
+    x = draw((B_, T, C), 1.0, 7600, "f32")
+    w = draw((C, 1, K), 1.0 / K, 8600, "f32")
+    b = draw((C,), 0.01, 9600, "f32")
+    r = oracle.dwconv1d_btc(as_f64(x), as_f64(w), as_f64(b), stride=1, padding=15, dilation=1)
+    buf = torch.empty(C * K + 1, device="cuda")
+    wu = buf[1:].view(C, 1, K)
+    wu.copy_(w.cuda())
+    assert wu.data_ptr() % 16 != 0
+    y = gc.dwconv1d_btc(gpu(x), wu, gpu(b), stride=1, padding=15, dilation=1)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "dw1d_btc_window"
+    assert normwise(as_f64(y.cpu()), r) <= TOL["f32"]
+    y2 = gc.dwconv1d_btc(gpu(x), gpu(w), gpu(b), stride=1, padding=15, dilation=1)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "dw1d_btc_tile"
+    assert normwise(as_f64(y2.cpu()), r) <= TOL["f32"]
 
 
 # ---------------------------------------------------------------- the five workloads at full size
