@@ -191,10 +191,15 @@ constexpr int kG4Filters = 36;    // LDS entries of a group's filters: [tap][out
 // tap (the same in every block), B = the 4 input channels of each position at the
 // tap's offset (one 8-byte LDS entry per lane), D = the 4 outputs of the lane's
 // position.
+// q / d for 0 <= q < 1024 and 1 <= d <= 339 as (q * m) >> 20 with m = ceil(2^20 / d):
+// exact on that range (checked exhaustively on the host side of the tests).
+__device__ __forceinline__ int g4_div(int q, uint32_t m) { return (int)(((uint32_t)q * m) >> 20); }
+
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
-            T *__restrict__ y, int G, int H, int W, int OH, int OW, int ph, int pw, int slabs)
+            T *__restrict__ y, int G, int H, int W, int OH, int OW, int ph, int pw, int slabs,
+            uint32_t mw, uint32_t mow)
 {
     extern __shared__ uint2 g4s[];
     const int HP = H + 2 * ph, WP = W + 2 * pw;
@@ -249,7 +254,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int p = 2 * q + e;
-                const int h = p / W, ww = p - h * W;
+                const int h = g4_div(p, mw), ww = p - h * W;
                 // half e of each channel's pair: channels (0,1) and (2,3) side by side
                 const uint32_t sel = e ? 0x07060302u : 0x05040100u;
                 xs[(h + ph) * WP + ww + pw] = make_uint2(__builtin_amdgcn_perm(xv[j][1], xv[j][0], sel),
@@ -275,7 +280,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
     T *yg = y + ((int64_t)n * C + 4 * k) * OH * OW;
     for (int p0 = 0; p0 < OH * OW; p0 += 64) {
         const int p = min(p0 + lane, OH * OW - 1);
-        const int oh = p / OW, ow = p - oh * OW;
+        const int oh = g4_div(p, mow), ow = p - oh * OW;
         const uint2 *xp = xs + oh * WP + ow;
         g4_f32x4 acc = b0;
 #pragma unroll
@@ -298,6 +303,7 @@ bool g4_applies(const Conv2dArgs &a)
         const int64_t Cg = a.C / a.groups, Ng = a.Cout / a.groups;
         return Cg == 4 && Ng == 4 && a.KH == 3 && a.KW == 3 && a.sh == 1 && a.sw == 1 && a.dh == 1 &&
                a.dw == 1 && a.ph <= 1 && a.pw <= 1 && (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= kG4MaxPos &&
+               a.W <= 339 && a.OW <= 339 &&
                (a.H * a.W) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 3) == 0 &&
                a.N * a.groups < (int64_t(1) << 30);
     }
@@ -313,7 +319,8 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
         *kname = "direct2d_g4";
         hipLaunchKernelGGL((direct2d_g4<T>), dim3((unsigned)ceil_div(slabs, kG4Waves)), dim3(kThreads), lds,
                            a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
-                           (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, slabs);
+                           (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, slabs,
+                           (uint32_t)(((1u << 20) + a.W - 1) / a.W), (uint32_t)(((1u << 20) + a.OW - 1) / a.OW));
         return hipGetLastError();
     }
 tiled:
