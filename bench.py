@@ -88,8 +88,12 @@ def source_digest(kernel_file):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-KERNEL_FILES = {"igemm": "igemm.hip", "igemm_f32": "igemm_f32.hip", "direct_nchw": "direct2d.hip",
-                "direct_ntc": "dw1d_ntc.hip"}
+# Source file of each kernel (as gconv_last_kernel names it).
+KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_fwd_f32_mfma32x32x2": "igemm_f32.hip",
+                "direct2d_g4": "direct2d.hip", "direct2d_tiled": "direct2d.hip",
+                "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip",
+                "dw1d_btc_tile": "dw1d_ntc.hip", "dw1d_btc_window": "dw1d_ntc.hip",
+                "dw1d_btc_generic": "dw1d_ntc.hip"}
 
 
 def counters_traffic(wl_name, kernel_file):
@@ -241,10 +245,20 @@ def route_of(wl):
                                  wl.layout, wl.dtype)
 
 
-def kernel_file(wl, route):
-    if route == "igemm":
-        return KERNEL_FILES["igemm_f32" if wl.dtype == "f32" else "igemm"]
-    return KERNEL_FILES["direct_ntc" if wl.layout == "ntc" else "direct_nchw"]
+def kernel_file(kernel):
+    return KERNEL_FILES[kernel]
+
+
+def measure_entry(wl, steps):
+    """Timing and roofline of one non-headline workload (a dict for the JSON line)."""
+    route = route_of(wl)
+    m = measure(wl, max(20, steps // 2), 5)
+    rf = roofline(wl, route, m["kernel_ms_avg"], counters_traffic(wl.name, kernel_file(m["kernel"])))
+    return {"route": route, "kernel": m["kernel"], "ms_per_step": round(m["step_ms"], 5),
+            "kernel_ms_avg": round(m["kernel_ms_avg"], 5),
+            "tflops": round(flops(wl) / (m["kernel_ms_avg"] * 1e-3) / 1e12, 3),
+            "gb_per_s": round(alg_bytes(wl) / (m["kernel_ms_avg"] * 1e-3) / 1e9, 1),
+            "roofline": rf}
 
 
 def main():
@@ -266,7 +280,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from depthwise_convolution_gconv_amd.workloads import HEADLINE, WORKLOADS
+    from depthwise_convolution_gconv_amd.workloads import HEADLINE, NEXT_WORKLOADS, WORKLOADS
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
@@ -283,10 +297,10 @@ def main():
         return
 
     name = args.workload or HEADLINE
-    wl = WORKLOADS[name]
+    wl = {**WORKLOADS, **NEXT_WORKLOADS}[name]
     route = route_of(wl)
     m = measure(wl, args.steps, args.warmup)
-    kfile = kernel_file(wl, route)
+    kfile = kernel_file(m["kernel"])
     f = flops(wl)
     value = f / (m["step_ms"] * 1e-3) / 1e12
     out = {
@@ -314,19 +328,11 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     if not args.no_others:
-        others = {}
-        for oname, owl in WORKLOADS.items():
-            if oname == name:
-                continue
-            oroute = route_of(owl)
-            om = measure(owl, max(20, args.steps // 2), 5)
-            rf = roofline(owl, oroute, om["kernel_ms_avg"], counters_traffic(oname, kernel_file(owl, oroute)))
-            others[oname] = {"route": oroute, "kernel": om["kernel"], "ms_per_step": round(om["step_ms"], 5),
-                             "kernel_ms_avg": round(om["kernel_ms_avg"], 5),
-                             "tflops": round(flops(owl) / (om["kernel_ms_avg"] * 1e-3) / 1e12, 3),
-                             "gb_per_s": round(alg_bytes(owl) / (om["kernel_ms_avg"] * 1e-3) / 1e9, 1),
-                             "roofline": rf}
-        out["others"] = others
+        out["others"] = {oname: measure_entry(owl, args.steps)
+                         for oname, owl in WORKLOADS.items() if oname != name}
+        # Strided depthwise layers (beyond the five workloads above).
+        out["next"] = {oname: measure_entry(owl, args.steps)
+                       for oname, owl in NEXT_WORKLOADS.items() if oname != name}
     print(json.dumps(out))
 
 

@@ -1,6 +1,6 @@
 // api.cpp -- the C ABI of libgconv: validation, output shape, route selection
 // and launch.  Everything here runs on the host; the arithmetic is in the HIP
-// kernels (direct2d.hip, dw1d_ntc.hip, igemm.hip).
+// kernels (direct2d.hip, dw2d.hip, dw1d_ntc.hip, igemm.hip, igemm_f32.hip).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -195,6 +195,8 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
                             "(3x3 or 1x1 kernels, C/g a multiple of 8 (fp16/bf16) or 4 (fp32), halo tile "
                             "within LDS)");
             err = dtype == GCONV_F32 ? gconv::launch_igemm_f32(a, &kname) : gconv::launch_igemm(a, &kname);
+        } else if (gconv::dw2d_supported(a)) {
+            err = gconv::launch_dw2d(a, &kname);   // depthwise (C/g = 1), stride 1 or 2
         } else {
             err = gconv::launch_direct2d(a, &kname);
         }

@@ -9,8 +9,9 @@
 // one load per input step instead of one per tap, the "single load" the issue's
 // author wanted in place of a loop over the kernel taps.
 //
-// dw1d_btc_tile<T, K, VE>: stride 1, dilation 1, compile-time K.  One workgroup
-//   per TT x CT tile: it stages the tile's filters and its TT + K - 1 input steps
+// dw1d_btc_tile<T, K, S, VE>: stride S (1 or 2), dilation 1, compile-time K.  One
+//   workgroup per TT x CT output tile: it stages the tile's filters and its
+//   (TT - 1) * S + K input steps
 //   in LDS once (16-byte buffer loads, zero outside [0, T)), each thread takes the
 //   K taps of its channel into registers and streams the input steps of its RT
 //   outputs through them.  Tiles are dealt to the XCDs in contiguous runs, so the
@@ -120,13 +121,14 @@ template <> __device__ __forceinline__ float elem_f32<__bf16>(const uint32_t *d,
 // grid is resident at once on the Conformer shape (at most 64 registers a thread, 8
 // workgroups per CU): the loads of all tiles are in flight together and no second
 // round of workgroups waits for the first.
-template <typename T, int K, int VE>
+template <typename T, int K, int S, int VE>
 __global__ void __launch_bounds__(kThreads, 8)
 dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
               T *__restrict__ y, int T_in, int C, int To, int pad, int tblocks, int cblocks,
               int tiles, int tiles_per_xcd)
 {
-    constexpr int NRW = kTT + K - 1;               // staged input steps
+    constexpr int NRW = (kTT - 1) * S + K;         // staged input steps
+    constexpr int NWIN = (kRT - 1) * S + K;        // input steps of one thread's outputs
     constexpr int VPR = kCT / VE;                  // loads per staged step
     constexpr int NL = (NRW * VPR + kThreads - 1) / kThreads;   // input loads per thread
     constexpr int DW = (VE * sizeof(T) + 3) / 4;
@@ -170,7 +172,7 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
     for (int j = 0; j < NL; ++j) {
         const int i = tid + j * kThreads;
         const int r = i / VPR, v = i - r * VPR;
-        const int ti = t0 - pad + r, c = c0 + v * VE;
+        const int ti = t0 * S - pad + r, c = c0 + v * VE;
         const bool ok = i < NRW * VPR && ti >= 0 && ti < T_in && c < C;
         RawLoad<VE * sizeof(T)>::run(xr, ok ? (uint32_t)((xbase + (int64_t)ti * C + c) * sizeof(T)) : kOOB, d[j]);
     }
@@ -205,18 +207,18 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
     __syncthreads();
 
     // kRT outputs of channel c: input step i of the thread's window feeds output r
-    // through tap i - r.
+    // through tap i - r*S.
     float acc[kRT];
 #pragma unroll
     for (int r = 0; r < kRT; ++r) acc[r] = b0;
 #pragma unroll
-    for (int i = 0; i < kRT + K - 1; ++i) {
+    for (int i = 0; i < NWIN; ++i) {
         // Input steps are read a few at a time (the other resident waves cover the
         // LDS latency), which keeps the thread within its 64 registers.
-        const float xv = xs[rg * kRT + i][lane];
+        const float xv = xs[rg * kRT * S + i][lane];
 #pragma unroll
         for (int r = 0; r < kRT; ++r)
-            if (i - r >= 0 && i - r < K) acc[r] = fmaf(xv, wr[i - r], acc[r]);
+            if (i - r * S >= 0 && i - r * S < K) acc[r] = fmaf(xv, wr[i - r * S], acc[r]);
         // Each step's products are taken here (not sunk to the stores, which would
         // keep every input step live at once).
 #pragma unroll
@@ -261,45 +263,51 @@ hipError_t run_window(const Dw1dArgs &a)
     return hipGetLastError();
 }
 
-template <typename T, int K, int VE>
+template <typename T, int K, int S, int VE>
 hipError_t run_tile(const Dw1dArgs &a)
 {
     const int tblocks = (int)ceil_div(a.To, kTT), cblocks = (int)ceil_div(a.C, kCT);
     const int64_t tiles = a.B * tblocks * cblocks;
     const int64_t per_xcd = ceil_div(tiles, 8);
     const int64_t blocks = 8 * per_xcd;   // one workgroup per tile (the last XCD's run may be short)
-    hipLaunchKernelGGL((dw1d_btc_tile<T, K, VE>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((dw1d_btc_tile<T, K, S, VE>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                        (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)a.T, (int)a.C,
                        (int)a.To, a.p, tblocks, cblocks, (int)tiles, (int)per_xcd);
     return hipGetLastError();
 }
 
-template <typename T, int K>
+template <typename T, int K, int S>
 hipError_t run_tile_ve(const Dw1dArgs &a)
 {
     constexpr int VE = 16 / sizeof(T);
-    if (a.C % VE == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0) return run_tile<T, K, VE>(a);
-    return run_tile<T, K, 1>(a);
+    if (a.C % VE == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0) return run_tile<T, K, S, VE>(a);
+    return run_tile<T, K, S, 1>(a);
+}
+
+template <typename T, int K>
+hipError_t run_tile_s(const Dw1dArgs &a)
+{
+    return a.s == 2 ? run_tile_ve<T, K, 2>(a) : run_tile_ve<T, K, 1>(a);
 }
 
 template <typename T>
 hipError_t run_typed(const Dw1dArgs &a, const char **kname)
 {
-    // Tile kernel: stride 1, dilation 1, one batch's input addressable by a 31-bit
+    // Tile kernel: stride 1 or 2, dilation 1, the input addressable by a 31-bit
     // byte offset, tile indices in int, w 16-byte aligned (its filter loads are 16
     // bytes wide).
     const int64_t tiles = a.B * ceil_div(a.To, kTT) * ceil_div(a.C, kCT);
-    if (a.s == 1 && a.d == 1 && a.B * a.T * a.C * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
+    if ((a.s == 1 || a.s == 2) && a.d == 1 && a.B * a.T * a.C * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
         (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && a.C * a.K * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
         8 * ceil_div(tiles, 8) < (int64_t(1) << 31) && a.T + a.K < (int64_t(1) << 30)) {
         *kname = "dw1d_btc_tile";
         switch (a.K) {
-        case 3: return run_tile_ve<T, 3>(a);
-        case 5: return run_tile_ve<T, 5>(a);
-        case 7: return run_tile_ve<T, 7>(a);
-        case 9: return run_tile_ve<T, 9>(a);
-        case 15: return run_tile_ve<T, 15>(a);
-        case 31: return run_tile_ve<T, 31>(a);
+        case 3: return run_tile_s<T, 3>(a);
+        case 5: return run_tile_s<T, 5>(a);
+        case 7: return run_tile_s<T, 7>(a);
+        case 9: return run_tile_s<T, 9>(a);
+        case 15: return run_tile_s<T, 15>(a);
+        case 31: return run_tile_s<T, 31>(a);
         default: break;
         }
     }

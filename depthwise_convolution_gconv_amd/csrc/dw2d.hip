@@ -1,0 +1,373 @@
+// dw2d.hip -- depthwise conv2d (NCHW, groups = C) on the vector ALUs, stride 1 or 2.
+//
+// The depthwise extreme of grouped convolution: every output channel reads one
+// input channel (C/g = 1; Cout/g = M filters per channel, M = 1 being the plain
+// depthwise layer).  The work per output is K*K multiply-adds, so the layer is
+// bound by HBM traffic, not arithmetic: the kernel's job is to read x once and
+// write y once, both coalesced.  Stride 2 is the depthwise-separable downsampling
+// layer that speechbrain issue #2733 names as the next candidate after the
+// Conformer's 1-D depthwise conv (Fast Conformer's subsampling CNN, which needs
+// stride).
+//
+// dw2d_rows<T, K, S, R, VI>: K x K filters, stride S, dilation 1.
+//  * Work unit: a run of R consecutive outputs of one output row (R*sizeof(T) =
+//    16 or 8 bytes, or R = 1).  Runs are numbered over (output plane, row, run),
+//    i.e. in the memory order of y, and workgroup b takes runs_per_wg consecutive
+//    ones, so a workgroup's stores cover one contiguous stretch of y.
+//  * Staging: the zero-padded input rows those runs read (virtual rows of the
+//    padded planes, so a workgroup may span plane boundaries) go to LDS as fp32,
+//    one row every WP floats, with 16-byte buffer loads along W (out-of-range
+//    offsets read as zero, which supplies the padding rows).  The filters of the
+//    planes the workgroup touches go next to them.
+//  * Compute: each thread slides its run's window ((R-1)*S + K input columns,
+//    16-byte LDS reads) down the K filter rows, R fp32 accumulators, bias added
+//    in fp32, one rounding to T, one R-element vector store.
+//  * Workgroups are dealt to the XCDs in contiguous runs (workgroup b runs on XCD
+//    b % 8), so the halo rows that neighbouring workgroups share come from one L2.
+#include <algorithm>
+
+#include "common.hpp"
+#include "fastdiv.hpp"
+
+namespace gconv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLdsBudget = 40 * 1024;     // bytes of LDS per workgroup (>= 4 resident per CU)
+constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past num_records: the load returns 0
+
+struct Dw2dGeom {
+    int C, H, W, Cout, OH, OW;
+    int ph, pw;
+    int Hp;            // H + 2*ph: rows of one padded plane in the virtual row space
+    int planes;        // N * Cout output planes
+    int WP;            // LDS row stride (floats, multiple of 4)
+    int RPR;           // runs per output row (OW / R)
+    int CPR;           // staging loads per input row (W / VI)
+    int npad;          // LDS columns of a row outside the image (WP - W)
+    int runs_per_wg, total_runs, wgs, wgs_per_xcd;
+    int NRmax;         // LDS rows reserved for the input (bound on any workgroup's rows)
+    FastDiv fd_rpr, fd_oh, fd_hp, fd_cpr, fd_cout, fd_m, fd_npad;
+};
+
+template <int BYTES> struct Load;
+template <> struct Load<16> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d)
+    {
+        const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
+    }
+};
+template <> struct Load<4> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d)
+    {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+};
+template <> struct Load<2> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *d)
+    {
+        d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+};
+
+// Element e of a staged vector of T held in dwords.
+template <typename T> __device__ __forceinline__ float elem(const uint32_t *d, int e);
+template <> __device__ __forceinline__ float elem<float>(const uint32_t *d, int e)
+{
+    return __builtin_bit_cast(float, d[e]);
+}
+template <> __device__ __forceinline__ float elem<_Float16>(const uint32_t *d, int e)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(d[e >> 1] >> (16 * (e & 1))));
+}
+template <> __device__ __forceinline__ float elem<__bf16>(const uint32_t *d, int e)
+{
+    return __builtin_bit_cast(float, (d[e >> 1] >> (16 * (e & 1))) << 16);
+}
+
+// Bits of one rounded T value (round to nearest even), in the low bits of a dword.
+template <typename T> __device__ __forceinline__ uint32_t bits_of(float v)
+{
+    if constexpr (sizeof(T) == 4) return __builtin_bit_cast(uint32_t, v);
+    else return (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(v));
+}
+
+// Stores R values of T (R * sizeof(T) bytes, aligned to that size) at p.
+template <typename T, int R>
+__device__ __forceinline__ void store_run(T *p, const float *v)
+{
+    constexpr int NDW = (R * (int)sizeof(T) + 3) / 4;
+    if constexpr (R * sizeof(T) < 4) {
+        *p = from_f32<T>(v[0]);
+    } else {
+        uint32_t d[NDW];
+#pragma unroll
+        for (int i = 0; i < NDW; ++i) {
+            if constexpr (sizeof(T) == 4) d[i] = bits_of<T>(v[i]);
+            else d[i] = bits_of<T>(v[2 * i]) | (bits_of<T>(v[2 * i + 1]) << 16);
+        }
+        if constexpr (NDW == 4) *reinterpret_cast<uint4 *>(p) = make_uint4(d[0], d[1], d[2], d[3]);
+        else if constexpr (NDW == 2) *reinterpret_cast<uint2 *>(p) = make_uint2(d[0], d[1]);
+        else *reinterpret_cast<uint32_t *>(p) = d[0];
+    }
+}
+
+template <typename T, int K, int S, int R, int VI>
+__global__ void __launch_bounds__(kThreads)
+dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+          T *__restrict__ y, Dw2dGeom g)
+{
+    constexpr int KK = K * K;
+    constexpr bool kVecRead = (R * S) % 4 == 0;           // window starts are 16-byte aligned
+    constexpr int NWIN = (R - 1) * S + K;                 // input columns of one run
+    constexpr int NWR = kVecRead ? (NWIN + 3) / 4 * 4 : NWIN;
+    constexpr int DW = (VI * (int)sizeof(T) + 3) / 4;     // dwords per staging load
+    constexpr int NB = 8;                                 // staging loads in flight per thread
+    extern __shared__ float lds[];
+
+    const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+    const int wg = xcd * g.wgs_per_xcd + rank;
+    if (wg >= min((xcd + 1) * g.wgs_per_xcd, g.wgs)) return;   // uniform over the workgroup
+    const int tid = threadIdx.x;
+
+    // Runs [u0, u1) of this workgroup; the output rows (virtual: plane * OH + oh) and
+    // the padded input rows (virtual: plane * Hp + hp) they cover.
+    const int u0 = wg * g.runs_per_wg;
+    const int u1 = min(u0 + g.runs_per_wg, g.total_runs);
+    const int vr_a = fdiv(u0, g.fd_rpr), vr_b = fdiv(u1 - 1, g.fd_rpr);
+    const int pa = fdiv(vr_a, g.fd_oh), pb = fdiv(vr_b, g.fd_oh);
+    const int R_lo = pa * g.Hp + (vr_a - pa * g.OH) * S;
+    const int NR = pb * g.Hp + (vr_b - pb * g.OH) * S + K - R_lo;
+    float *xs = lds;                          // [NR][WP]
+    float *ws = lds + g.NRmax * g.WP;         // [pb - pa + 1][K*K]
+
+    // Input plane read by output plane p: image n = p / Cout, channel (p % Cout) / M.
+    auto in_plane = [&](int p) {
+        const int n = fdiv(p, g.fd_cout);
+        return n * g.C + fdiv(p - n * g.Cout, g.fd_m);
+    };
+    const int pia = in_plane(pa);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(x + (int64_t)pia * g.H * g.W), (short)0, 0x7fffffff, 0x00020000);
+
+    // Stage the rows, NB loads per thread in flight at a time.
+    const int nchunks = NR * g.CPR;
+    for (int base = 0; base < nchunks; base += NB * kThreads) {
+        uint32_t d[NB][DW];
+        int dst[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            uint32_t off = kOOB;
+            dst[j] = -1;
+            if (i < nchunks) {
+                const int r = fdiv(i, g.fd_cpr), ch = i - r * g.CPR;
+                const int vrow = R_lo + r;
+                const int p = fdiv(vrow, g.fd_hp), ih = vrow - p * g.Hp - g.ph;
+                if (p < g.planes && ih >= 0 && ih < g.H)
+                    off = (uint32_t)((((int64_t)(in_plane(p) - pia) * g.H + ih) * g.W + ch * VI) * sizeof(T));
+                dst[j] = r * g.WP + g.pw + ch * VI;
+            }
+            Load<VI * sizeof(T) >= 4 ? 4 * DW : 2>::run(xr, off, d[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            if (dst[j] >= 0) {
+#pragma unroll
+                for (int q = 0; q < VI; ++q) xs[dst[j] + q] = elem<T>(d[j], q);
+            }
+    }
+    // Columns outside the image: zero.
+    for (int i = tid; i < NR * g.npad; i += kThreads) {
+        const int r = fdiv(i, g.fd_npad), c = i - r * g.npad;
+        xs[r * g.WP + (c < g.pw ? c : c + g.W)] = 0.0f;
+    }
+    // Filters of output planes pa .. pb.
+    for (int i = tid; i < (pb - pa + 1) * KK; i += kThreads) {
+        const int p = pa + i / KK, t = i - (i / KK) * KK;
+        const int o = p - fdiv(p, g.fd_cout) * g.Cout;
+        ws[i] = to_f32(w[(int64_t)o * KK + t]);
+    }
+    __syncthreads();
+
+    for (int u = u0 + tid; u < u1; u += kThreads) {
+        const int vr = fdiv(u, g.fd_rpr), rc = u - vr * g.RPR;
+        const int p = fdiv(vr, g.fd_oh), oh = vr - p * g.OH;
+        const float b0 = bias ? to_f32(bias[p - fdiv(p, g.fd_cout) * g.Cout]) : 0.0f;
+        float acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = b0;
+        const float *wt = ws + (p - pa) * KK;
+        const float *xrow = xs + (p * g.Hp + oh * S - R_lo) * g.WP + rc * (R * S);
+#pragma unroll
+        for (int kh = 0; kh < K; ++kh) {
+            float win[NWR];
+            if constexpr (kVecRead) {
+#pragma unroll
+                for (int v = 0; v < NWR / 4; ++v) {
+                    const float4 q = *reinterpret_cast<const float4 *>(xrow + kh * g.WP + 4 * v);
+                    win[4 * v] = q.x; win[4 * v + 1] = q.y; win[4 * v + 2] = q.z; win[4 * v + 3] = q.w;
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < NWR; ++v) win[v] = xrow[kh * g.WP + v];
+            }
+#pragma unroll
+            for (int kw = 0; kw < K; ++kw) {
+                const float wv = wt[kh * K + kw];
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fmaf(win[r * S + kw], wv, acc[r]);
+            }
+        }
+        store_run<T, R>(y + (int64_t)vr * g.OW + rc * R, acc);
+    }
+}
+
+struct Plan {
+    Dw2dGeom g;
+    int K, S, R, VI;
+    size_t lds;
+    bool ok;
+};
+
+Plan make_plan(const Conv2dArgs &a)
+{
+    Plan pl{};
+    pl.ok = false;
+    const int es = a.dtype == DT_F32 ? 4 : 2;
+    if (a.groups != a.C || a.KH != a.KW || (a.KH != 3 && a.KH != 5 && a.KH != 7)) return pl;
+    if (a.sh != a.sw || (a.sh != 1 && a.sh != 2) || a.dh != 1 || a.dw != 1) return pl;
+    if (a.ph > a.KH || a.pw > a.KW) return pl;
+    const int K = (int)a.KH, S = a.sh;
+    Dw2dGeom &g = pl.g;
+    // Run length: 16 or 8 bytes of y when the output rows split into such runs and y
+    // is aligned for them, else single elements.
+    const uintptr_t ya = reinterpret_cast<uintptr_t>(a.y);
+    pl.R = 1;
+    for (int R : {16 / es, 8 / es}) {
+        if (R >= 2 && a.OW % R == 0 && ya % (uintptr_t)(R * es) == 0 && (R * S) % 4 == 0) {
+            pl.R = R;
+            break;
+        }
+    }
+    const int VI16 = 16 / es;
+    pl.VI = (a.W % VI16 == 0 && reinterpret_cast<uintptr_t>(a.x) % 16 == 0) ? VI16 : 1;
+    const int64_t planes = a.N * a.Cout;
+    const int64_t Hp = a.H + 2 * (int64_t)a.ph;
+    const int64_t RPR = a.OW / pl.R;
+    const int64_t total_runs = planes * a.OH * RPR;
+    if (planes * Hp + 2 * K >= (int64_t(1) << 31) || total_runs >= (int64_t(1) << 31)) return pl;
+    const int R = pl.R;
+    const int NWIN = (R - 1) * S + K;
+    const int NWR = (R * S) % 4 == 0 ? (NWIN + 3) / 4 * 4 : NWIN;
+    const int64_t WP = (std::max<int64_t>(a.W + 2 * a.pw, (RPR - 1) * R * S + NWR) + 3) / 4 * 4;
+    // Runs per workgroup: enough for about 8 output rows per workgroup (fewer halo
+    // re-reads), as many as fit the LDS budget.
+    const int64_t gap = Hp - a.OH * S;   // >= K - S > 0: rows between two planes' windows
+    auto lds_for = [&](int64_t runs, int64_t *nr_out) {
+        const int64_t V = (runs + RPR - 1) / RPR + 1;            // output rows touched (bound)
+        const int64_t crossings = V <= 1 ? 0 : (V - 2) / a.OH + 1;
+        int64_t NR = (V - 1) * S + K + crossings * gap;
+        NR = std::min<int64_t>(NR, planes * Hp);
+        const int64_t NP = std::min<int64_t>(crossings + 1, planes);
+        *nr_out = NR;
+        return (NR * WP + NP * K * K) * (int64_t)sizeof(float);
+    };
+    int64_t passes = std::min<int64_t>(8, std::max<int64_t>(1, (8 * RPR + kThreads - 1) / kThreads));
+    int64_t nr = 0;
+    while (passes > 1 && lds_for(passes * kThreads, &nr) > kLdsBudget) --passes;
+    const int64_t bytes = lds_for(passes * kThreads, &nr);
+    if (bytes > kLdsBudget) return pl;
+    // Staging offsets (relative to the workgroup's first input plane) fit 31 bits.
+    const int64_t V = (passes * kThreads + RPR - 1) / RPR + 1;
+    const int64_t np_in = std::min<int64_t>(V <= 1 ? 1 : (V - 2) / a.OH + 2, planes);
+    if ((np_in + 1) * a.H * a.W * es >= (int64_t(1) << 31)) return pl;
+    g.C = (int)a.C; g.H = (int)a.H; g.W = (int)a.W; g.Cout = (int)a.Cout;
+    g.OH = (int)a.OH; g.OW = (int)a.OW; g.ph = a.ph; g.pw = a.pw;
+    g.Hp = (int)Hp;
+    g.planes = (int)planes;
+    g.WP = (int)WP;
+    g.RPR = (int)RPR;
+    g.CPR = (int)(a.W / pl.VI);
+    g.npad = (int)(WP - a.W);
+    g.runs_per_wg = (int)(passes * kThreads);
+    g.total_runs = (int)total_runs;
+    g.wgs = (int)ceil_div(total_runs, g.runs_per_wg);
+    g.wgs_per_xcd = (int)ceil_div(g.wgs, 8);
+    g.NRmax = (int)nr;
+    g.fd_rpr = make_fastdiv((uint32_t)RPR);
+    g.fd_oh = make_fastdiv((uint32_t)a.OH);
+    g.fd_hp = make_fastdiv((uint32_t)Hp);
+    g.fd_cpr = make_fastdiv((uint32_t)g.CPR);
+    g.fd_cout = make_fastdiv((uint32_t)a.Cout);
+    g.fd_m = make_fastdiv((uint32_t)(a.Cout / a.C));
+    g.fd_npad = make_fastdiv((uint32_t)std::max(g.npad, 1));   // npad = 0: the pad loop is empty
+    pl.K = K;
+    pl.S = S;
+    pl.lds = (size_t)bytes;
+    pl.ok = true;
+    return pl;
+}
+
+template <typename T, int K, int S, int R, int VI>
+hipError_t run(const Conv2dArgs &a, const Plan &pl)
+{
+    const unsigned blocks = (unsigned)(8 * (int64_t)pl.g.wgs_per_xcd);
+    hipLaunchKernelGGL((dw2d_rows<T, K, S, R, VI>), dim3(blocks), dim3(kThreads), pl.lds, a.stream,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, pl.g);
+    return hipGetLastError();
+}
+
+template <typename T, int K, int S, int R>
+hipError_t run_vi(const Conv2dArgs &a, const Plan &pl)
+{
+    return pl.VI > 1 ? run<T, K, S, R, 16 / sizeof(T)>(a, pl) : run<T, K, S, R, 1>(a, pl);
+}
+
+template <typename T, int K, int S>
+hipError_t run_r(const Conv2dArgs &a, const Plan &pl)
+{
+    if constexpr (sizeof(T) == 2) {
+        if (pl.R == 8) return run_vi<T, K, S, 8>(a, pl);
+    }
+    if (pl.R == 4) return run_vi<T, K, S, 4>(a, pl);
+    if constexpr (S == 2) {
+        if (pl.R == 2) return run_vi<T, K, S, 2>(a, pl);
+    }
+    return run_vi<T, K, S, 1>(a, pl);
+}
+
+template <typename T, int K>
+hipError_t run_s(const Conv2dArgs &a, const Plan &pl)
+{
+    return pl.S == 2 ? run_r<T, K, 2>(a, pl) : run_r<T, K, 1>(a, pl);
+}
+
+template <typename T>
+hipError_t run_typed(const Conv2dArgs &a, const Plan &pl)
+{
+    switch (pl.K) {
+    case 3: return run_s<T, 3>(a, pl);
+    case 5: return run_s<T, 5>(a, pl);
+    default: return run_s<T, 7>(a, pl);
+    }
+}
+
+}  // namespace
+
+bool dw2d_supported(const Conv2dArgs &a) { return make_plan(a).ok; }
+
+hipError_t launch_dw2d(const Conv2dArgs &a, const char **kname)
+{
+    const Plan pl = make_plan(a);
+    if (!pl.ok) return hipErrorInvalidValue;
+    *kname = "dw2d_rows";
+    switch (a.dtype) {
+    case DT_F32: return run_typed<float>(a, pl);
+    case DT_F16: return run_typed<_Float16>(a, pl);
+    default: return run_typed<__bf16>(a, pl);
+    }
+}
+
+}  // namespace gconv

@@ -83,6 +83,27 @@ WORKLOADS = {
 
 HEADLINE = "c2_p2layer_f16"
 
+# Strided depthwise layers (the depthwise-separable downsampling that speechbrain
+# issue #2733 names as the next candidate: Fast Conformer's subsampling CNN, which
+# needs stride).  Shapes of a Fast Conformer subsampling stage on 8 utterances:
+# 256 channels, 512 frames x 40 frequency bins in, a 3x3 depthwise filter with
+# stride 2 and padding 1; the stride-1 layer on the same input; and the
+# Conformer's 1-D depthwise conv with stride 2.
+NEXT_WORKLOADS = {
+    "n1_dw2d_s2_f32": Workload(
+        "n1_dw2d_s2_f32", 11, "nchw", (8, 256, 512, 40), (256, 1, 3, 3), 256, 2, 1, 1, "f32",
+        1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d, stride 2 (subsampling stage)"),
+    "n2_dw2d_s2_bf16": Workload(
+        "n2_dw2d_s2_bf16", 12, "nchw", (8, 256, 512, 40), (256, 1, 3, 3), 256, 2, 1, 1, "bf16",
+        1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d, stride 2, bf16"),
+    "n3_dw2d_s1_f32": Workload(
+        "n3_dw2d_s1_f32", 13, "nchw", (8, 256, 512, 40), (256, 1, 3, 3), 256, 1, 1, 1, "f32",
+        1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d, stride 1"),
+    "n4_dw1d_s2_f32": Workload(
+        "n4_dw1d_s2_f32", 14, "ntc", (8, 1024, 512), (512, 1, 31), 512, 2, 15, 1, "f32",
+        1.0, 1 / 31, 0.01, "depthwise conv1d, (batch, steps, channels), stride 2"),
+}
+
 
 def draw(shape, var: float, seed: int, dtype: str) -> torch.Tensor:
     """Seeded N(0, var) draw in fp32, rounded to `dtype` (RNE), as a CPU tensor."""

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import depthwise_convolution_gconv_amd as gc
-from depthwise_convolution_gconv_amd.workloads import WORKLOADS, as_f64, draw, make_inputs
+from depthwise_convolution_gconv_amd.workloads import NEXT_WORKLOADS, WORKLOADS, as_f64, draw, make_inputs
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -119,7 +119,10 @@ DW_SWEEP = [  # B, T, C, K, stride, pad, dil, bias
     (2, 100, 64, 31, 1, 15, 1, True),
     (3, 37, 300, 3, 1, 1, 1, False),
     (1, 257, 40, 9, 1, 4, 1, True),
-    (2, 50, 24, 7, 2, 3, 1, True),        # stride 2 (generic kernel)
+    (2, 50, 24, 7, 2, 3, 1, True),        # stride 2 (tile kernel)
+    (2, 300, 64, 31, 2, 15, 1, True),     # stride 2, K = 31, several tiles and a ragged last one
+    (3, 33, 40, 3, 2, 1, 1, False),       # stride 2, odd length
+    (1, 97, 20, 9, 2, 0, 1, True),        # stride 2, no padding, C not a multiple of 64
     (2, 45, 16, 5, 1, 4, 2, True),        # dilation 2 (generic kernel)
     (1, 5, 8, 31, 1, 15, 1, True),        # sequence shorter than the kernel
     (2, 64, 33, 6, 1, 0, 1, True),        # even K, no padding (generic kernel)
@@ -138,6 +141,60 @@ def test_dw1d_sweep_vs_oracle(ci, dt):
     y = gc.dwconv1d_btc(gpu(x), gpu(w), gpu(b), stride=s, padding=p, dilation=d)
     torch.cuda.synchronize()
     assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+
+
+# Depthwise conv2d (C/g = 1): the dw2d_rows kernel where its plan applies (K in
+# {3, 5, 7}, square stride 1 or 2, dilation 1), the tiled kernel otherwise.
+DW2D_SWEEP = [  # N, C, M (filters per channel), H, W, K, stride, pad, bias
+    (2, 3, 1, 9, 8, 3, 1, 1, True),       # planes smaller than a workgroup's runs
+    (2, 3, 1, 9, 8, 3, 2, 1, False),
+    (1, 4, 2, 11, 12, 5, 2, 2, True),     # two filters per channel
+    (3, 2, 1, 7, 7, 7, 1, 3, True),       # 7x7, odd width (single-element runs and loads)
+    (2, 5, 1, 6, 16, 3, 2, 0, True),      # no padding, odd output width
+    (1, 3, 3, 13, 24, 3, 1, 1, False),    # three filters per channel
+    (1, 2, 1, 64, 40, 3, 2, 1, True),     # several workgroups per plane
+    (1, 2, 1, 70, 8, 5, 1, 2, True),
+    (4, 8, 1, 4, 4, 3, 1, 1, True),       # many tiny planes per workgroup
+    (1, 1, 1, 2, 2, 3, 1, 1, True),       # image smaller than the filter
+    (2, 3, 1, 20, 20, 7, 2, 3, True),
+    (2, 16, 1, 30, 30, 3, 1, 1, True),    # 30 columns: 8-byte runs in 16-bit
+    (1, 8, 1, 33, 35, 3, 2, 1, True),     # odd sizes throughout
+    (1, 4, 1, 9, 9, 3, 3, 1, True),       # stride 3: not this kernel (tiled)
+    (1, 4, 1, 9, 9, 4, 1, 1, True),       # even filter: not this kernel (tiled)
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(DW2D_SWEEP)))
+def test_dw2d_sweep_vs_oracle(ci, dt):
+    N, C, M, H, W, K, s, p, has_b = DW2D_SWEEP[ci]
+    seed = 60 * ci + {"f32": 0, "f16": 1, "bf16": 2}[dt]
+    x = draw((N, C, H, W), 1.0, 7700 + seed, dt)
+    w = draw((C * M, 1, K, K), 1.0 / (K * K), 8700 + seed, dt)
+    b = draw((C * M,), 0.01, 9700 + seed, dt) if has_b else None
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=p, dilation=1, groups=C)
+    y = run_conv2d(x, w, b, s, p, 1, C, "auto")
+    expect = "dw2d_rows" if K in (3, 5, 7) and s in (1, 2) else "direct2d_tiled"
+    assert gc.gconv_last_kernel() == expect
+    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+
+
+def test_dw2d_unaligned_output_and_input():
+    # y and x that start 4 bytes past a 16-byte boundary: single-element runs and loads.
+    N, C, H, W, K = 2, 6, 24, 24, 3
+    x = draw((N, C, H, W), 1.0, 7790, "f32")
+    w = draw((C, 1, K, K), 1.0 / 9, 8790, "f32")
+    b = draw((C,), 0.01, 9790, "f32")
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=2, padding=1, dilation=1, groups=C)
+    xb = torch.empty(x.numel() + 1, device="cuda")
+    xu = xb[1:].view(N, C, H, W)
+    xu.copy_(x.cuda())
+    yb = torch.empty(N * C * 12 * 12 + 1, device="cuda")
+    yu = yb[1:].view(N, C, 12, 12)
+    gc.gconv_fwd(xu, gpu(w), gpu(b), 2, 1, 1, C, "nchw", y=yu)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "dw2d_rows"
+    assert normwise(as_f64(yu.cpu()), r) <= TOL["f32"]
 
 
 def test_dw1d_unaligned_filters_use_the_window_kernel():
@@ -192,6 +249,28 @@ def test_workload_full_size(name):
         idx = _sample_idx(yc.size, 20000, 4242 + wl.index)
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         err = normwise(yc.ravel()[idx], r)
+    print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e}")
+    assert err <= TOL[wl.dtype]
+
+
+@pytest.mark.parametrize("name", sorted(NEXT_WORKLOADS))
+def test_next_workload_full_size(name):
+    # The strided depthwise layers at full size, on 20 000 sampled outputs (plus the
+    # first and the last), each evaluated one by one by the oracle.
+    wl = NEXT_WORKLOADS[name]
+    x, w, b = make_inputs(wl)
+    y = gc.gconv_fwd(gpu(x), gpu(w), gpu(b), wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
+    torch.cuda.synchronize()
+    yc = as_f64(y.cpu())
+    xd, wd, bd = as_f64(x), as_f64(w), as_f64(b)
+    idx = _sample_idx(yc.size, 20000, 4343 + wl.index)
+    if wl.layout == "ntc":
+        r = oracle.dwconv1d_btc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation)
+        assert gc.gconv_last_kernel() == "dw1d_btc_tile"
+    else:
+        r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
+        assert gc.gconv_last_kernel() == "dw2d_rows"
+    err = normwise(yc.ravel()[idx], r)
     print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e}")
     assert err <= TOL[wl.dtype]
 
