@@ -159,6 +159,9 @@ DW2D_SWEEP = [  # N, C, M (filters per channel), H, W, K, stride, pad, bias
     (2, 3, 1, 20, 20, 7, 2, 3, True),
     (2, 16, 1, 30, 30, 3, 1, 1, True),    # 30 columns: 8-byte runs in 16-bit
     (1, 8, 1, 33, 35, 3, 2, 1, True),     # odd sizes throughout
+    (4, 16, 1, 50, 40, 3, 1, 1, True),    # tens of workgroups, each crossing plane boundaries
+    (2, 32, 1, 64, 44, 3, 2, 1, True),
+    (3, 24, 2, 30, 28, 5, 1, 2, True),    # two filters per channel over many workgroups
     (1, 4, 1, 9, 9, 3, 3, 1, True),       # stride 3: not this kernel (tiled)
     (1, 4, 1, 9, 9, 4, 1, 1, True),       # even filter: not this kernel (tiled)
 ]
