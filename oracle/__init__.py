@@ -20,7 +20,9 @@ Sources followed (cited by page title and the reply or code block on it):
   -- cross-correlation with symmetric zero padding.
 * speechbrain issue #2733 "Investigate custom Triton kernels for
   depthwise-separable convolutions in Conformer": depthwise conv with groups equal
-  to the channel count, over a (batch, steps, channels) tensor.
+  to the channel count, over a (batch, steps, channels) tensor; in its follow-up
+  comments the author also writes the backward pass of that conv (the gradients
+  with respect to the input, the filters and the bias, ``dwconv1d_btc_bwd_*``).
 """
 from __future__ import annotations
 
@@ -72,6 +74,13 @@ def _load():
         lib.gconv_oracle_dwconv1d_btc.argtypes = dw_args + [_dp]
         lib.gconv_oracle_dwconv1d_btc_at.restype = ctypes.c_int
         lib.gconv_oracle_dwconv1d_btc_at.argtypes = dw_args + [_ip, _i64, _dp]
+        bwd_args = [_dp, _i64, _i64, _i64, _dp, _i64, _i64, _i64, _i64]
+        lib.gconv_oracle_dwconv1d_btc_bwd_data.restype = ctypes.c_int
+        lib.gconv_oracle_dwconv1d_btc_bwd_data.argtypes = bwd_args + [_dp]
+        lib.gconv_oracle_dwconv1d_btc_bwd_data_at.restype = ctypes.c_int
+        lib.gconv_oracle_dwconv1d_btc_bwd_data_at.argtypes = bwd_args + [_ip, _i64, _dp]
+        lib.gconv_oracle_dwconv1d_btc_bwd_filter.restype = ctypes.c_int
+        lib.gconv_oracle_dwconv1d_btc_bwd_filter.argtypes = [_dp, _dp] + [_i64] * 7 + [_dp, _dp]
         _lib = lib
     return _lib
 
@@ -182,3 +191,51 @@ def dwconv1d_btc_at(x, w, flat_idx, bias=None, stride=1, padding=0, dilation=1) 
                                          int(dilation), idx.ctypes.data_as(_ip), idx.size,
                                          out.ctypes.data_as(_dp)))
     return out
+
+
+def dwconv1d_btc_bwd_data(dy, w, T: int, stride=1, padding=0, dilation=1) -> np.ndarray:
+    """Gradient of dwconv1d_btc with respect to x [B,T,C], given dy [B,To,C] and w [C,1,K]."""
+    lib = _load()
+    dy, dyp = _f64(dy)
+    w, wp = _f64(w)
+    B, To, C = dy.shape
+    K = w.shape[2]
+    if out_len(T, K, stride, padding, dilation) != To:
+        raise ValueError("oracle: dy length does not match T")
+    dx = np.zeros((B, T, C), dtype=np.float64)
+    _rc(lib.gconv_oracle_dwconv1d_btc_bwd_data(dyp, B, int(T), C, wp, K, int(stride), int(padding),
+                                               int(dilation), dx.ctypes.data_as(_dp)))
+    return dx
+
+
+def dwconv1d_btc_bwd_data_at(dy, w, T: int, flat_idx, stride=1, padding=0, dilation=1) -> np.ndarray:
+    """The elements dx.flat[flat_idx] of dwconv1d_btc_bwd_data(...), evaluated one by one."""
+    lib = _load()
+    dy, dyp = _f64(dy)
+    w, wp = _f64(w)
+    B, To, C = dy.shape
+    K = w.shape[2]
+    if out_len(T, K, stride, padding, dilation) != To:
+        raise ValueError("oracle: dy length does not match T")
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    out = np.zeros(idx.shape, dtype=np.float64)
+    _rc(lib.gconv_oracle_dwconv1d_btc_bwd_data_at(dyp, B, int(T), C, wp, K, int(stride), int(padding),
+                                                  int(dilation), idx.ctypes.data_as(_ip), idx.size,
+                                                  out.ctypes.data_as(_dp)))
+    return out
+
+
+def dwconv1d_btc_bwd_filter(x, dy, K: int, stride=1, padding=0, dilation=1):
+    """Gradients of dwconv1d_btc with respect to w [C,1,K] and bias [C], given x [B,T,C]
+    and dy [B,To,C].  Returns (dw, db)."""
+    lib = _load()
+    x, xp = _f64(x)
+    dy, dyp = _f64(dy)
+    B, T, C = x.shape
+    if dy.shape != (B, out_len(T, K, stride, padding, dilation), C):
+        raise ValueError("oracle: dy shape does not match x and K")
+    dw = np.zeros((C, 1, K), dtype=np.float64)
+    db = np.zeros((C,), dtype=np.float64)
+    _rc(lib.gconv_oracle_dwconv1d_btc_bwd_filter(xp, dyp, B, T, C, int(K), int(stride), int(padding),
+                                                 int(dilation), dw.ctypes.data_as(_dp), db.ctypes.data_as(_dp)))
+    return dw, db

@@ -1,5 +1,6 @@
 /*
- * gconv_oracle.c -- plain, slow, fp64 CPU oracle for grouped convolution forward.
+ * gconv_oracle.c -- plain, slow, fp64 CPU oracle for grouped convolution forward
+ * (and the backward of the depthwise 1-D convolution).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or calls
  * this file; only the test suite, the smoke check and the CPU-baseline leg of the
@@ -22,6 +23,9 @@
  *    speechbrain issue "Investigate custom Triton kernels for depthwise-separable
  *    convolutions in Conformer" (#2733): groups equal to the channel count, one
  *    K-tap filter per channel, data laid out (batch, steps, channels).
+ *  - The backward pass of that depthwise 1-D convolution (the same issue's
+ *    follow-up comments): the gradients with respect to x, w and the bias, the
+ *    chain-rule sums of the forward definition.
  *
  * Every input is fp64 (callers pass fp16/bf16/fp32 values widened exactly), every
  * product and sum is fp64, and results are returned in fp64.
@@ -215,6 +219,109 @@ int gconv_oracle_dwconv1d_btc_at(const double *x, int64_t B, int64_t T, int64_t 
         const int64_t t = (idx[i] / C) % To;
         const int64_t b = idx[i] / (C * To);
         out[i] = dw1d_one(x, T, C, w, K, bias, s, p, d, b, t, c);
+    }
+    return 0;
+}
+
+/* ---- backward of the depthwise 1-D convolution -----------------------------
+ *
+ * The speechbrain issue #2733 follow-up comments: its author went on to write the
+ * backward pass of the (batch, steps, channels) depthwise convolution.  With
+ * y = dwconv1d_btc(x, w, bias) and an upstream gradient dy [B][To][C], the chain
+ * rule gives, term by term of the forward sum:
+ *   dx[b][i][c] = sum over taps k and outputs t with t*s - p + k*d == i of
+ *                 dy[b][t][c] * w[c][k];
+ *   dw[c][0][k] = sum over b and t with 0 <= t*s - p + k*d < T of
+ *                 dy[b][t][c] * x[b][t*s - p + k*d][c];
+ *   db[c]       = sum over b and t of dy[b][t][c].
+ * For dx the condition is solved for t: t = (i + p - k*d) / s when that is an
+ * integer in [0, To).
+ */
+static double dw1d_bwd_data_one(const double *dy, int64_t To, int64_t C, const double *w, int64_t K,
+                                int64_t s, int64_t p, int64_t d, int64_t b, int64_t i, int64_t c)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t ts = i + p - k * d;        /* = t * s */
+        if (ts < 0 || ts % s != 0) continue;
+        const int64_t t = ts / s;
+        if (t >= To) continue;
+        acc += dy[(b * To + t) * C + c] * w[c * K + k];
+    }
+    return acc;
+}
+
+static int dw1d_bwd_check(int64_t B, int64_t T, int64_t C, int64_t K, int64_t s, int64_t p, int64_t d)
+{
+    if (B < 0 || T < 1 || C < 1 || K < 1 || s < 1 || p < 0 || d < 1) return 1;
+    if (gconv_oracle_out_len(T, K, s, p, d) < 1) return 2;
+    return 0;
+}
+
+/* dy: [B][To][C] with To = gconv_oracle_out_len(T, K, s, p, d); w: [C][1][K];
+ * dx: [B][T][C]. */
+int gconv_oracle_dwconv1d_btc_bwd_data(const double *dy, int64_t B, int64_t T, int64_t C,
+                                       const double *w, int64_t K, int64_t s, int64_t p, int64_t d,
+                                       double *dx)
+{
+    const int rc = dw1d_bwd_check(B, T, C, K, s, p, d);
+    if (rc) return rc;
+    const int64_t To = gconv_oracle_out_len(T, K, s, p, d);
+#pragma omp parallel for schedule(static)
+    for (int64_t bi = 0; bi < B * T; ++bi) {
+        const int64_t b = bi / T, i = bi % T;
+        for (int64_t c = 0; c < C; ++c)
+            dx[(b * T + i) * C + c] = dw1d_bwd_data_one(dy, To, C, w, K, s, p, d, b, i, c);
+    }
+    return 0;
+}
+
+/* Selected elements of dx; idx[j] is a flat index into dx[B][T][C]. */
+int gconv_oracle_dwconv1d_btc_bwd_data_at(const double *dy, int64_t B, int64_t T, int64_t C,
+                                          const double *w, int64_t K, int64_t s, int64_t p, int64_t d,
+                                          const int64_t *idx, int64_t n_idx, double *out)
+{
+    const int rc = dw1d_bwd_check(B, T, C, K, s, p, d);
+    if (rc) return rc;
+    const int64_t To = gconv_oracle_out_len(T, K, s, p, d);
+    for (int64_t j = 0; j < n_idx; ++j)
+        if (idx[j] < 0 || idx[j] >= B * T * C) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n_idx; ++j) {
+        const int64_t c = idx[j] % C, i = (idx[j] / C) % T, b = idx[j] / (C * T);
+        out[j] = dw1d_bwd_data_one(dy, To, C, w, K, s, p, d, b, i, c);
+    }
+    return 0;
+}
+
+/* x: [B][T][C]; dy: [B][To][C]; dw: [C][1][K]; db: [C] or NULL. */
+int gconv_oracle_dwconv1d_btc_bwd_filter(const double *x, const double *dy, int64_t B, int64_t T,
+                                         int64_t C, int64_t K, int64_t s, int64_t p, int64_t d,
+                                         double *dw, double *db)
+{
+    const int rc = dw1d_bwd_check(B, T, C, K, s, p, d);
+    if (rc) return rc;
+    const int64_t To = gconv_oracle_out_len(T, K, s, p, d);
+#pragma omp parallel for schedule(static)
+    for (int64_t ck = 0; ck < C * K; ++ck) {
+        const int64_t c = ck / K, k = ck % K;
+        double acc = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t t = 0; t < To; ++t) {
+                const int64_t ti = t * s - p + k * d;
+                if (ti < 0 || ti >= T) continue;
+                acc += dy[(b * To + t) * C + c] * x[(b * T + ti) * C + c];
+            }
+        dw[c * K + k] = acc;
+    }
+    if (db) {
+#pragma omp parallel for schedule(static)
+        for (int64_t c = 0; c < C; ++c) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                for (int64_t t = 0; t < To; ++t) acc += dy[(b * To + t) * C + c];
+            db[c] = acc;
+        }
     }
     return 0;
 }
