@@ -1,4 +1,5 @@
-"""Grouped-convolution forward engine for AMD Instinct MI355X (gfx950).
+"""Grouped-convolution forward engine for AMD Instinct MI355X (gfx950), with the
+backward of the (batch, steps, channels) depthwise conv1d.
 
 The compute runs in libgconv.so (hand-written HIP kernels behind the C ABI in
 include/gconv.h); this package is its Python binding.  Importing the package
@@ -11,6 +12,10 @@ from ._binding import (  # noqa: F401
     PreparedCall,
     conv2d,
     dwconv1d_btc,
+    dwconv1d_btc_backward,
+    gconv_dw1d_bwd_data,
+    gconv_dw1d_bwd_filter,
+    gconv_dw1d_bwd_filter_workspace,
     gconv_fwd,
     gconv_fwd_route,
     gconv_last_error,

@@ -25,6 +25,7 @@ ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
 
 # Every symbol include/gconv.h declares.
 EXPORTS = ("gconv_out_shape", "gconv_select_route", "gconv_fwd", "gconv_fwd_route",
+           "gconv_dw1d_bwd_data", "gconv_dw1d_bwd_filter_workspace", "gconv_dw1d_bwd_filter",
            "gconv_last_kernel", "gconv_status_string", "gconv_last_error")
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -70,6 +71,14 @@ def lib() -> ctypes.CDLL:
         L.gconv_out_shape.restype = _i32
         L.gconv_select_route.argtypes = [_i64p, _i64p, _i32p, _i32p, _i32p, _i32, _i32, _i32, _i32p]
         L.gconv_select_route.restype = _i32
+        L.gconv_dw1d_bwd_data.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _i32p, _i32p, _i32p, _i32, _vp]
+        L.gconv_dw1d_bwd_data.restype = _i32
+        L.gconv_dw1d_bwd_filter_workspace.argtypes = [_i64p, _i64p, _i32p, _i32p, _i32p, _i32,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+        L.gconv_dw1d_bwd_filter_workspace.restype = _i32
+        L.gconv_dw1d_bwd_filter.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _vp, _i32p, _i32p, _i32p, _i32,
+                                            _vp, ctypes.c_size_t, _vp]
+        L.gconv_dw1d_bwd_filter.restype = _i32
         L.gconv_last_kernel.argtypes = []
         L.gconv_last_kernel.restype = ctypes.c_char_p
         L.gconv_status_string.argtypes = [_i32]
@@ -213,6 +222,92 @@ def conv2d(x, weight, bias=None, stride=1, padding=0, dilation=1, groups: int = 
 def dwconv1d_btc(x, weight, bias=None, stride=1, padding=0, dilation=1):
     """Depthwise conv1d over x [B,T,C] (batch, steps, channels), weight [C,1,K]."""
     return _call(x, weight, bias, None, stride, padding, dilation, x.shape[-1], "ntc", None, None)
+
+
+# ---- backward of the depthwise conv1d over (batch, steps, channels) -----------
+
+def _check_tensors(ref: torch.Tensor, **ts):
+    for name, t in ts.items():
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise GconvError(ERR_INVALID_ARG, f"{name} must be a contiguous GPU tensor")
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise GconvError(ERR_INVALID_ARG, f"{name} must match the dtype and device of the other tensors")
+    if ref.dtype not in DTYPES:
+        raise GconvError(ERR_INVALID_ARG, f"unsupported dtype {ref.dtype}")
+
+
+def gconv_dw1d_bwd_data(dy, w, T: int, stride=1, pad=0, dilation=1, dx=None, stream=None) -> torch.Tensor:
+    """Input gradient [B,T,C] of the (batch, steps, channels) depthwise conv1d, from
+    dy [B,To,C] and w [C,1,K].  Returns dx."""
+    _check_tensors(dy, w=w, dx=dx)
+    B, _, C = dy.shape
+    x_shape = (B, int(T), C)
+    if dx is None:
+        dx = torch.empty(x_shape, dtype=dy.dtype, device=dy.device)
+    elif tuple(dx.shape) != x_shape:
+        raise GconvError(ERR_SHAPE, f"dx has shape {tuple(dx.shape)}, expected {x_shape}")
+    yshape = gconv_out_shape(x_shape, tuple(w.shape), stride, pad, dilation, C, "ntc")
+    if tuple(dy.shape) != yshape:
+        raise GconvError(ERR_SHAPE, f"dy has shape {tuple(dy.shape)}, expected {yshape}")
+    s, p, d = _geom("ntc", stride, pad, dilation)
+    with torch.cuda.device(dy.device):
+        st = stream if stream is not None else torch.cuda.current_stream(dy.device)
+        _check(lib().gconv_dw1d_bwd_data(_vp(dy.data_ptr()), _arr(_i64, x_shape), _vp(w.data_ptr()),
+                                         _arr(_i64, w.shape), _vp(dx.data_ptr()), s, p, d, DTYPES[dy.dtype],
+                                         _vp(st.cuda_stream)))
+    return dx
+
+
+def gconv_dw1d_bwd_filter_workspace(x_shape, w_shape, stride=1, pad=0, dilation=1, dtype="f32") -> int:
+    """Workspace bytes gconv_dw1d_bwd_filter needs (no device work)."""
+    s, p, d = _geom("ntc", stride, pad, dilation)
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else DTYPE_NAMES[dtype]
+    n = ctypes.c_size_t(0)
+    _check(lib().gconv_dw1d_bwd_filter_workspace(_arr(_i64, x_shape), _arr(_i64, w_shape), s, p, d, dt,
+                                                 ctypes.byref(n)))
+    return int(n.value)
+
+
+def gconv_dw1d_bwd_filter(x, dy, K: int, stride=1, pad=0, dilation=1, bias: bool = True, dw=None, db=None,
+                          workspace=None, stream=None):
+    """Filter gradient [C,1,K] (and bias gradient [C] if `bias`) of the (batch, steps,
+    channels) depthwise conv1d, from x [B,T,C] and dy [B,To,C].  The fp32 workspace is
+    allocated with torch.empty when not given.  Returns (dw, db or None)."""
+    _check_tensors(x, dy=dy, dw=dw, db=db)
+    B, T, C = x.shape
+    w_shape = (C, 1, int(K))
+    yshape = gconv_out_shape(tuple(x.shape), w_shape, stride, pad, dilation, C, "ntc")
+    if tuple(dy.shape) != yshape:
+        raise GconvError(ERR_SHAPE, f"dy has shape {tuple(dy.shape)}, expected {yshape}")
+    if dw is None:
+        dw = torch.empty(w_shape, dtype=x.dtype, device=x.device)
+    if bias and db is None:
+        db = torch.empty((C,), dtype=x.dtype, device=x.device)
+    if tuple(dw.shape) != w_shape or (db is not None and tuple(db.shape) != (C,)):
+        raise GconvError(ERR_SHAPE, "dw must be [C,1,K] and db [C]")
+    need = gconv_dw1d_bwd_filter_workspace(tuple(x.shape), w_shape, stride, pad, dilation, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise GconvError(ERR_INVALID_ARG, "workspace must be a contiguous GPU tensor")
+    s, p, d = _geom("ntc", stride, pad, dilation)
+    with torch.cuda.device(x.device):
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        _check(lib().gconv_dw1d_bwd_filter(_vp(x.data_ptr()), _arr(_i64, x.shape), _vp(dy.data_ptr()),
+                                           _arr(_i64, w_shape), _vp(dw.data_ptr()),
+                                           _vp(db.data_ptr() if db is not None else 0), s, p, d,
+                                           DTYPES[x.dtype], _vp(workspace.data_ptr()),
+                                           workspace.numel() * workspace.element_size(), _vp(st.cuda_stream)))
+    return dw, db
+
+
+def dwconv1d_btc_backward(x, weight, dy, stride=1, padding=0, dilation=1, bias: bool = True):
+    """(dx, dw, db) of dwconv1d_btc: the input, filter and bias gradients."""
+    dx = gconv_dw1d_bwd_data(dy, weight, x.shape[1], stride, padding, dilation)
+    dw, db = gconv_dw1d_bwd_filter(x, dy, weight.shape[2], stride, padding, dilation, bias=bias)
+    return dx, dw, db
 
 
 class PreparedCall:

@@ -218,6 +218,30 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
     return GCONV_OK;
 }
 
+// Geometry of a depthwise conv1d over (batch, steps, channels) from the forward
+// call's shapes (groups = C).
+gconv_status_t dw1d_geometry(const int64_t *x_shape, const int64_t *w_shape, const int32_t *stride,
+                             const int32_t *pad, const int32_t *dilation, gconv_dtype_t dtype, Geometry *g)
+{
+    if (dtype != GCONV_F32 && dtype != GCONV_F16 && dtype != GCONV_BF16)
+        return fail(GCONV_ERR_INVALID_ARG, "unknown dtype %lld", (long long)dtype);
+    if (!x_shape) return fail(GCONV_ERR_INVALID_ARG, "NULL x_shape");
+    if (x_shape[2] < 1 || x_shape[2] > kDimMax)
+        return fail(GCONV_ERR_INVALID_ARG, "x_shape[2] (channels) must be in [1, 2^31)");
+    return validate(x_shape, w_shape, stride, pad, dilation, (int32_t)x_shape[2], GCONV_LAYOUT_NTC, g);
+}
+
+gconv::Dw1dArgs dw1d_args(const Geometry &g, const void *w, gconv_dtype_t dtype, void *stream)
+{
+    gconv::Dw1dArgs a;
+    a.x = nullptr; a.w = w; a.bias = nullptr; a.y = nullptr;
+    a.B = g.B; a.T = g.T; a.C = g.C; a.K = g.K; a.To = g.To;
+    a.s = g.s; a.p = g.p; a.d = g.d;
+    a.dtype = (int)dtype;
+    a.stream = (hipStream_t)stream;
+    return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,6 +301,87 @@ gconv_status_t gconv_fwd_route(const void *x, const int64_t *x_shape, const void
 {
     return run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype, route,
                hip_stream);
+}
+
+gconv_status_t gconv_dw1d_bwd_data(const void *dy, const int64_t *x_shape, const void *w,
+                                   const int64_t *w_shape, void *dx, const int32_t *stride,
+                                   const int32_t *pad, const int32_t *dilation, gconv_dtype_t dtype,
+                                   void *hip_stream)
+{
+    g_last_error[0] = '\0';
+    Geometry g;
+    const gconv_status_t st = dw1d_geometry(x_shape, w_shape, stride, pad, dilation, dtype, &g);
+    if (st != GCONV_OK) return st;
+    if (!w) return fail(GCONV_ERR_INVALID_ARG, "NULL w pointer");
+    if (g.B == 0) {
+        g_last_kernel = "";
+        return GCONV_OK;
+    }
+    if (!dy || !dx) return fail(GCONV_ERR_INVALID_ARG, "NULL dy or dx pointer");
+    const size_t es = elem_size(dtype);
+    const size_t ndy = es * (size_t)(g.B * g.To * g.C), ndx = es * (size_t)(g.B * g.T * g.C);
+    if (overlaps(dx, ndx, dy, ndy) || overlaps(dx, ndx, w, es * (size_t)(g.C * g.K)))
+        return fail(GCONV_ERR_INVALID_ARG, "dx overlaps dy or w");
+    const char *kname = "";
+    const hipError_t err = gconv::launch_dw1d_bwd_data(dw1d_args(g, w, dtype, hip_stream), dy, dx, &kname);
+    if (err != hipSuccess)
+        return fail(GCONV_ERR_LAUNCH, "kernel launch failed: HIP error %lld", (long long)err);
+    g_last_kernel = kname;
+    return GCONV_OK;
+}
+
+gconv_status_t gconv_dw1d_bwd_filter_workspace(const int64_t *x_shape, const int64_t *w_shape,
+                                               const int32_t *stride, const int32_t *pad,
+                                               const int32_t *dilation, gconv_dtype_t dtype, size_t *bytes)
+{
+    g_last_error[0] = '\0';
+    if (!bytes) return fail(GCONV_ERR_INVALID_ARG, "NULL bytes");
+    Geometry g;
+    const gconv_status_t st = dw1d_geometry(x_shape, w_shape, stride, pad, dilation, dtype, &g);
+    if (st != GCONV_OK) return st;
+    size_t ws = 0;
+    if (!gconv::dw1d_wgrad_plan(dw1d_args(g, nullptr, dtype, nullptr), &ws))
+        return fail(GCONV_ERR_UNSUPPORTED, "filter gradient: filter length above 64 or sizes beyond the "
+                    "library's index range");
+    *bytes = ws;
+    return GCONV_OK;
+}
+
+gconv_status_t gconv_dw1d_bwd_filter(const void *x, const int64_t *x_shape, const void *dy,
+                                     const int64_t *w_shape, void *dw, void *db, const int32_t *stride,
+                                     const int32_t *pad, const int32_t *dilation, gconv_dtype_t dtype,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream)
+{
+    g_last_error[0] = '\0';
+    Geometry g;
+    const gconv_status_t st = dw1d_geometry(x_shape, w_shape, stride, pad, dilation, dtype, &g);
+    if (st != GCONV_OK) return st;
+    const gconv::Dw1dArgs a = dw1d_args(g, nullptr, dtype, hip_stream);
+    size_t need = 0;
+    if (!gconv::dw1d_wgrad_plan(a, &need))
+        return fail(GCONV_ERR_UNSUPPORTED, "filter gradient: filter length above 64 or sizes beyond the "
+                    "library's index range");
+    if (!dw) return fail(GCONV_ERR_INVALID_ARG, "NULL dw pointer");
+    if (g.B > 0 && (!x || !dy)) return fail(GCONV_ERR_INVALID_ARG, "NULL x or dy pointer");
+    if (need > 0 && !workspace) return fail(GCONV_ERR_INVALID_ARG, "NULL workspace");
+    if (((uintptr_t)workspace & 3) != 0) return fail(GCONV_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    if (workspace_bytes < need)
+        return fail(GCONV_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                    (long long)need);
+    const size_t es = elem_size(dtype);
+    const size_t nx = es * (size_t)(g.B * g.T * g.C), ndy = es * (size_t)(g.B * g.To * g.C);
+    const size_t ndw = es * (size_t)(g.C * g.K), ndb = db ? es * (size_t)g.C : 0;
+    if (overlaps(dw, ndw, x, nx) || overlaps(dw, ndw, dy, ndy) || overlaps(dw, ndw, workspace, need) ||
+        overlaps(dw, ndw, db, ndb) || overlaps(db, ndb, x, nx) || overlaps(db, ndb, dy, ndy) ||
+        overlaps(db, ndb, workspace, need) || overlaps(workspace, need, x, nx) ||
+        overlaps(workspace, need, dy, ndy))
+        return fail(GCONV_ERR_INVALID_ARG, "dw, db, the workspace, x and dy must not overlap");
+    const char *kname = "";
+    const hipError_t err = gconv::launch_dw1d_bwd_filter(a, x, dy, dw, db, workspace, &kname);
+    if (err != hipSuccess)
+        return fail(GCONV_ERR_LAUNCH, "kernel launch failed: HIP error %lld", (long long)err);
+    g_last_kernel = kname;
+    return GCONV_OK;
 }
 
 const char *gconv_last_kernel(void) { return g_last_kernel; }

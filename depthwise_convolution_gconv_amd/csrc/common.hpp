@@ -55,6 +55,11 @@ hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);
 bool igemm_f32_supported(const Conv2dArgs &a);        // fp32
 hipError_t launch_igemm_f32(const Conv2dArgs &a, const char **kname);
 hipError_t launch_dw1d(const Dw1dArgs &a, const char **kname);
+// Backward of the depthwise conv1d (a: the forward geometry; a.x, a.y, a.bias unused).
+hipError_t launch_dw1d_bwd_data(const Dw1dArgs &a, const void *dy, void *dx, const char **kname);
+bool dw1d_wgrad_plan(const Dw1dArgs &a, size_t *ws_bytes);
+hipError_t launch_dw1d_bwd_filter(const Dw1dArgs &a, const void *x, const void *dy, void *dw, void *db,
+                                  void *ws, const char **kname);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -121,7 +121,9 @@ template <> __device__ __forceinline__ float elem_f32<__bf16>(const uint32_t *d,
 // grid is resident at once on the Conformer shape (at most 64 registers a thread, 8
 // workgroups per CU): the loads of all tiles are in flight together and no second
 // round of workgroups waits for the first.
-template <typename T, int K, int S, int VE>
+// FLIP: the taps are applied in reverse order (the input gradient at stride 1 is
+// this convolution of dy with the filter reversed).
+template <typename T, int K, int S, int VE, bool FLIP>
 __global__ void __launch_bounds__(kThreads, 8)
 dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
               T *__restrict__ y, int T_in, int C, int To, int pad, int tblocks, int cblocks,
@@ -189,7 +191,7 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
     __syncthreads();
     float wr[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) wr[k] = ws[lane * K + k];
+    for (int k = 0; k < K; ++k) wr[k] = ws[lane * K + (FLIP ? K - 1 - k : k)];
     const int c = c0 + lane;
     const bool cok = c < C;
     const float b0 = (bias && cok) ? to_f32(bias[c]) : 0.0f;
@@ -263,25 +265,25 @@ hipError_t run_window(const Dw1dArgs &a)
     return hipGetLastError();
 }
 
-template <typename T, int K, int S, int VE>
+template <typename T, int K, int S, int VE, bool FLIP = false>
 hipError_t run_tile(const Dw1dArgs &a)
 {
     const int tblocks = (int)ceil_div(a.To, kTT), cblocks = (int)ceil_div(a.C, kCT);
     const int64_t tiles = a.B * tblocks * cblocks;
     const int64_t per_xcd = ceil_div(tiles, 8);
     const int64_t blocks = 8 * per_xcd;   // one workgroup per tile (the last XCD's run may be short)
-    hipLaunchKernelGGL((dw1d_btc_tile<T, K, S, VE>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((dw1d_btc_tile<T, K, S, VE, FLIP>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                        (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)a.T, (int)a.C,
                        (int)a.To, a.p, tblocks, cblocks, (int)tiles, (int)per_xcd);
     return hipGetLastError();
 }
 
-template <typename T, int K, int S>
+template <typename T, int K, int S, bool FLIP = false>
 hipError_t run_tile_ve(const Dw1dArgs &a)
 {
     constexpr int VE = 16 / sizeof(T);
-    if (a.C % VE == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0) return run_tile<T, K, S, VE>(a);
-    return run_tile<T, K, S, 1>(a);
+    if (a.C % VE == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0) return run_tile<T, K, S, VE, FLIP>(a);
+    return run_tile<T, K, S, 1, FLIP>(a);
 }
 
 template <typename T, int K>
@@ -290,16 +292,74 @@ hipError_t run_tile_s(const Dw1dArgs &a)
     return a.s == 2 ? run_tile_ve<T, K, 2>(a) : run_tile_ve<T, K, 1>(a);
 }
 
+// The tile kernel applies: stride 1 or 2, dilation 1, the input addressable by a
+// 31-bit byte offset, tile indices in int, w 16-byte aligned (its filter loads are
+// 16 bytes wide), a filter length it is compiled for.
+template <typename T>
+bool tile_applies(const Dw1dArgs &a)
+{
+    const int64_t tiles = a.B * ceil_div(a.To, kTT) * ceil_div(a.C, kCT);
+    const bool k_ok = a.K == 3 || a.K == 5 || a.K == 7 || a.K == 9 || a.K == 15 || a.K == 31;
+    return k_ok && (a.s == 1 || a.s == 2) && a.d == 1 && a.B * a.T * a.C * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
+           (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && a.C * a.K * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
+           8 * ceil_div(tiles, 8) < (int64_t(1) << 31) && a.T + a.K < (int64_t(1) << 30);
+}
+
+// Input gradient, any stride and dilation: one thread per element of dx.  Output
+// step t reads input step t*s - p + k*d, so input step i receives dy[t] * w[k] for
+// every tap k with i + p - k*d = t*s, 0 <= t < To.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+dw1d_btc_bwd_data_generic(const T *__restrict__ dy, const T *__restrict__ w, T *__restrict__ dx,
+                          int64_t total, int T_in, int C, int To, int K, int s, int p, int d)
+{
+    for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < total;
+         j += (int64_t)gridDim.x * kThreads) {
+        const int c = (int)(j % C);
+        const int i = (int)((j / C) % T_in);
+        const int64_t bi = j / ((int64_t)C * T_in);
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int ts = i + p - k * d;
+            if (ts < 0 || ts % s != 0 || ts / s >= To) continue;
+            acc = fmaf(to_f32(dy[(bi * To + ts / s) * C + c]), to_f32(w[(int64_t)c * K + k]), acc);
+        }
+        dx[j] = from_f32<T>(acc);
+    }
+}
+
+template <typename T>
+hipError_t run_bwd_data(const Dw1dArgs &a, const void *dy, void *dx, const char **kname)
+{
+    // Stride 1, dilation 1, p <= K - 1: dx is the forward convolution of dy (To
+    // steps) with the filter reversed and padding K - 1 - p, which has T outputs.
+    Dw1dArgs f = a;
+    f.x = dy; f.y = dx; f.bias = nullptr;
+    f.T = a.To; f.To = a.T; f.p = (int32_t)(a.K - 1 - a.p);
+    if (a.s == 1 && a.d == 1 && a.p <= a.K - 1 && tile_applies<T>(f)) {
+        *kname = "dw1d_btc_tile_flip";
+        switch (a.K) {
+        case 3: return run_tile_ve<T, 3, 1, true>(f);
+        case 5: return run_tile_ve<T, 5, 1, true>(f);
+        case 7: return run_tile_ve<T, 7, 1, true>(f);
+        case 9: return run_tile_ve<T, 9, 1, true>(f);
+        case 15: return run_tile_ve<T, 15, 1, true>(f);
+        default: return run_tile_ve<T, 31, 1, true>(f);
+        }
+    }
+    *kname = "dw1d_btc_bwd_data_generic";
+    const int64_t total = a.B * a.T * a.C;
+    const int64_t blocks = std::min<int64_t>(ceil_div(total, kThreads), 1 << 20);
+    hipLaunchKernelGGL((dw1d_btc_bwd_data_generic<T>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                       (const T *)dy, (const T *)a.w, (T *)dx, total, (int)a.T, (int)a.C, (int)a.To,
+                       (int)a.K, a.s, a.p, a.d);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t run_typed(const Dw1dArgs &a, const char **kname)
 {
-    // Tile kernel: stride 1 or 2, dilation 1, the input addressable by a 31-bit
-    // byte offset, tile indices in int, w 16-byte aligned (its filter loads are 16
-    // bytes wide).
-    const int64_t tiles = a.B * ceil_div(a.To, kTT) * ceil_div(a.C, kCT);
-    if ((a.s == 1 || a.s == 2) && a.d == 1 && a.B * a.T * a.C * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
-        (reinterpret_cast<uintptr_t>(a.w) & 15) == 0 && a.C * a.K * (int64_t)sizeof(T) < (int64_t(1) << 31) &&
-        8 * ceil_div(tiles, 8) < (int64_t(1) << 31) && a.T + a.K < (int64_t(1) << 30)) {
+    if (tile_applies<T>(a)) {
         *kname = "dw1d_btc_tile";
         switch (a.K) {
         case 3: return run_tile_s<T, 3>(a);
@@ -341,6 +401,15 @@ hipError_t launch_dw1d(const Dw1dArgs &a, const char **kname)
     case DT_F32: return run_typed<float>(a, kname);
     case DT_F16: return run_typed<_Float16>(a, kname);
     default: return run_typed<__bf16>(a, kname);
+    }
+}
+
+hipError_t launch_dw1d_bwd_data(const Dw1dArgs &a, const void *dy, void *dx, const char **kname)
+{
+    switch (a.dtype) {
+    case DT_F32: return run_bwd_data<float>(a, dy, dx, kname);
+    case DT_F16: return run_bwd_data<_Float16>(a, dy, dx, kname);
+    default: return run_bwd_data<__bf16>(a, dy, dx, kname);
     }
 }
 

@@ -49,6 +49,7 @@
 #ifndef GCONV_H
 #define GCONV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -118,9 +119,56 @@ gconv_status_t gconv_fwd_route(const void *x, const int64_t *x_shape,
                                int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
                                gconv_route_t route, void *hip_stream);
 
-/* Name of the kernel the last successful gconv_fwd / gconv_fwd_route call on
- * this host thread launched ("" before the first call or after an empty batch).
- * The string has static storage. */
+/* ---- backward of the depthwise 1-D convolution over (batch, steps, channels) --
+ *
+ * speechbrain issue #2733 ("Investigate custom Triton kernels for depthwise-
+ * separable convolutions in Conformer"), its author's follow-up comments: the
+ * backward pass of the (batch, steps, channels) depthwise conv.  For the forward
+ *     y[b][t][c] = bias[c] + sum_k x[b][t*s - p + k*d][c] * w[c][0][k]
+ * (gconv_fwd with layout GCONV_LAYOUT_NTC, groups = C) and an upstream gradient
+ * dy[b][t][c] of y's shape [B][To][C], the gradients are
+ *     dx[b][i][c] = sum over (t, k) with t*s - p + k*d == i of dy[b][t][c] * w[c][0][k]
+ *     dw[c][0][k] = sum over (b, t), 0 <= t*s - p + k*d < T, of dy[b][t][c] * x[b][t*s-p+k*d][c]
+ *     db[c]       = sum over (b, t) of dy[b][t][c]
+ * Shapes are the forward call's: x_shape = {B, T, C}, w_shape = {C, 1, K};
+ * stride, pad and dilation each point to one int32.  All tensors are contiguous
+ * device buffers of `dtype`, owned by the caller; accumulation is fp32 and each
+ * result is rounded once to `dtype`.  Validation errors (the forward's, plus
+ * the overlaps named below) return before anything is enqueued and leave the
+ * outputs untouched; work is asynchronous on hip_stream and deterministic (no
+ * atomics). */
+
+/* Input gradient dx [B][T][C] from dy [B][To][C] and w [C][1][K].  dx must not
+ * overlap dy or w.  B = 0: GCONV_OK, nothing enqueued (dy, dx may be NULL). */
+gconv_status_t gconv_dw1d_bwd_data(const void *dy, const int64_t *x_shape,
+                                   const void *w, const int64_t *w_shape, void *dx,
+                                   const int32_t *stride, const int32_t *pad,
+                                   const int32_t *dilation, gconv_dtype_t dtype,
+                                   void *hip_stream);
+
+/* Bytes of device workspace gconv_dw1d_bwd_filter needs for this geometry
+ * (fp32 per-tile partial sums; 0 for B = 0).  GCONV_ERR_UNSUPPORTED for filter
+ * lengths above 64.  No device work. */
+gconv_status_t gconv_dw1d_bwd_filter_workspace(const int64_t *x_shape, const int64_t *w_shape,
+                                               const int32_t *stride, const int32_t *pad,
+                                               const int32_t *dilation, gconv_dtype_t dtype,
+                                               size_t *bytes);
+
+/* Filter gradient dw [C][1][K] and, if db is not NULL, bias gradient db [C], from
+ * x [B][T][C] and dy [B][To][C].  workspace: caller-owned device memory of at
+ * least gconv_dw1d_bwd_filter_workspace bytes (any alignment of 4 bytes or
+ * more), overwritten; fewer bytes is GCONV_ERR_INVALID_ARG.  dw, db, workspace,
+ * x and dy must not overlap.  B = 0 writes zeros to dw and db. */
+gconv_status_t gconv_dw1d_bwd_filter(const void *x, const int64_t *x_shape, const void *dy,
+                                     const int64_t *w_shape, void *dw, void *db,
+                                     const int32_t *stride, const int32_t *pad,
+                                     const int32_t *dilation, gconv_dtype_t dtype,
+                                     void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Name of the kernel the last successful gconv_fwd / gconv_fwd_route /
+ * gconv_dw1d_bwd_data / gconv_dw1d_bwd_filter call on this host thread launched
+ * (the first of two for the filter gradient; "" before the first call or after
+ * an empty batch).  The string has static storage. */
 const char *gconv_last_kernel(void);
 
 /* Fixed English text for a status code.  Static storage. */

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "gconv.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gconv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gconv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -146,3 +146,43 @@ def test_zero_batch_enqueues_nothing():
 def test_zero_batch_accepts_null_x_and_y():
     assert _raw_fwd((0, 4, 5, 5), (4, 1, 3, 3), (1, 1), (1, 1), (1, 1), 4, 0, 0, x=0, y=0) == 0
     assert _raw_fwd((0, 4, 5, 5), (4, 1, 3, 3), (1, 1), (1, 1), (1, 1), 4, 0, 0, w=0) == 1
+
+
+# ---------------------------------------------------------------- backward of the depthwise conv1d
+
+def _bwd_filter_call(ws_bytes, K=31, workspace=16):
+    L = B.lib()
+    s, p, d = B._geom("ntc", 1, 15, 1)
+    return L.gconv_dw1d_bwd_filter(B._vp(16), B._arr(B._i64, (8, 1024, 512)), B._vp(1 << 20),
+                                   B._arr(B._i64, (512, 1, K)), B._vp(1 << 24), B._vp(0), s, p, d, 0,
+                                   B._vp(workspace), ws_bytes, B._vp(0))
+
+
+def test_bwd_filter_workspace_size_is_per_tile_partials():
+    # 8 x 1024 steps in tiles of 64: 128 tiles x (31 taps + the bias row) x 512 channels x 4 bytes.
+    assert gc.gconv_dw1d_bwd_filter_workspace((8, 1024, 512), (512, 1, 31), 1, 15, 1, "f32") == 128 * 32 * 512 * 4
+    assert gc.gconv_dw1d_bwd_filter_workspace((0, 1024, 512), (512, 1, 31), 1, 15, 1, "f32") == 0
+    with pytest.raises(gc.GconvError) as e:
+        gc.gconv_dw1d_bwd_filter_workspace((8, 1024, 512), (512, 1, 65), 1, 32, 1, "f32")
+    assert e.value.status == B.ERR_UNSUPPORTED
+
+
+def test_bwd_filter_rejects_a_short_or_misaligned_workspace_before_launch():
+    need = gc.gconv_dw1d_bwd_filter_workspace((8, 1024, 512), (512, 1, 31), 1, 15, 1, "f32")
+    assert _bwd_filter_call(need - 4) == B.ERR_INVALID_ARG
+    assert "needed" in gc.gconv_last_error()
+    assert _bwd_filter_call(need, workspace=18) == B.ERR_INVALID_ARG
+    assert "aligned" in gc.gconv_last_error()
+
+
+def test_bwd_data_rejects_bad_shapes_before_launch():
+    L = B.lib()
+    s, p, d = B._geom("ntc", 1, 1, 1)
+    # w for 4 channels against x with 5: the forward's shape check.
+    rc = L.gconv_dw1d_bwd_data(B._vp(16), B._arr(B._i64, (2, 10, 5)), B._vp(1 << 20), B._arr(B._i64, (4, 1, 3)),
+                               B._vp(1 << 24), s, p, d, 0, B._vp(0))
+    assert rc in (B.ERR_SHAPE, B.ERR_UNSUPPORTED)
+    # dx overlapping dy.
+    rc = L.gconv_dw1d_bwd_data(B._vp(1 << 20), B._arr(B._i64, (2, 10, 4)), B._vp(16), B._arr(B._i64, (4, 1, 3)),
+                               B._vp((1 << 20) + 8), s, p, d, 0, B._vp(0))
+    assert rc == B.ERR_INVALID_ARG

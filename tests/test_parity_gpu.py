@@ -222,6 +222,73 @@ def test_dw1d_unaligned_filters_use_the_window_kernel():
     assert normwise(as_f64(y2.cpu()), r) <= TOL["f32"]
 
 
+# ---------------------------------------------------------------- backward of the depthwise conv1d
+
+BWD_SWEEP = [  # B, T, C, K, stride, pad, dil
+    (2, 100, 64, 31, 1, 15, 1),     # Conformer filter; input gradient on the reversed-filter tile kernel
+    (3, 37, 300, 3, 1, 1, 1),       # C not a multiple of 64
+    (1, 257, 40, 9, 1, 4, 1),       # ragged last tile
+    (2, 50, 24, 7, 2, 3, 1),        # stride 2
+    (2, 45, 16, 5, 1, 4, 2),        # dilation 2
+    (1, 5, 8, 31, 1, 15, 1),        # sequence shorter than the filter
+    (2, 64, 33, 6, 1, 0, 1),        # even K, no padding
+    (2, 30, 16, 3, 1, 3, 1),        # padding beyond K - 1
+    (1, 70, 20, 40, 3, 20, 1),      # 40 taps, stride 3
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(BWD_SWEEP)))
+def test_dw1d_backward_vs_oracle(ci, dt):
+    B_, T, C, K, s, p, d = BWD_SWEEP[ci]
+    seed = 70 * ci + {"f32": 0, "f16": 1, "bf16": 2}[dt]
+    To = oracle.out_len(T, K, s, p, d)
+    x = draw((B_, T, C), 1.0, 7800 + seed, dt)
+    w = draw((C, 1, K), 1.0 / K, 8800 + seed, dt)
+    dy = draw((B_, To, C), 1.0, 9800 + seed, dt)
+    dx, dw, db = gc.dwconv1d_btc_backward(gpu(x), gpu(w), gpu(dy), stride=s, padding=p, dilation=d)
+    torch.cuda.synchronize()
+    rdx = oracle.dwconv1d_btc_bwd_data(as_f64(dy), as_f64(w), T, s, p, d)
+    rdw, rdb = oracle.dwconv1d_btc_bwd_filter(as_f64(x), as_f64(dy), K, s, p, d)
+    assert normwise(as_f64(dx.cpu()), rdx) <= TOL[dt]
+    assert normwise(as_f64(dw.cpu()), rdw) <= TOL[dt]
+    assert normwise(as_f64(db.cpu()), rdb) <= TOL[dt]
+
+
+def test_dw1d_backward_kernels_and_determinism():
+    wl = WORKLOADS["c3_dw1d_btc_f32"]
+    x, w, _ = make_inputs(wl)
+    dy = draw((8, 1024, 512), 1.0, 9900, "f32")
+    xg, wg, dyg = gpu(x), gpu(w), gpu(dy)
+    dx1 = gc.gconv_dw1d_bwd_data(dyg, wg, 1024, 1, 15, 1)
+    assert gc.gconv_last_kernel() == "dw1d_btc_tile_flip"
+    dw1, db1 = gc.gconv_dw1d_bwd_filter(xg, dyg, 31, 1, 15, 1)
+    assert gc.gconv_last_kernel() == "dw1d_btc_wgrad_partial"
+    dx2 = gc.gconv_dw1d_bwd_data(dyg, wg, 1024, 1, 15, 1)
+    dw2, db2 = gc.gconv_dw1d_bwd_filter(xg, dyg, 31, 1, 15, 1)
+    torch.cuda.synchronize()
+    for a, b in ((dx1, dx2), (dw1, dw2), (db1, db2)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    # Full size against the oracle: the filter and bias gradients in full, the input
+    # gradient on 20 000 sampled elements.
+    rdw, rdb = oracle.dwconv1d_btc_bwd_filter(as_f64(x), as_f64(dy), 31, 1, 15, 1)
+    assert normwise(as_f64(dw1.cpu()), rdw) <= 1e-4
+    assert normwise(as_f64(db1.cpu()), rdb) <= 1e-4
+    idx = _sample_idx(dx1.numel(), 20000, 4545)
+    rdx = oracle.dwconv1d_btc_bwd_data_at(as_f64(dy), as_f64(w), 1024, idx, 1, 15, 1)
+    assert normwise(as_f64(dx1.cpu()).ravel()[idx], rdx) <= 1e-4
+
+
+def test_dw1d_backward_empty_batch():
+    x = torch.empty(0, 16, 8, device="cuda")
+    w = torch.randn(8, 1, 3, device="cuda")
+    dy = torch.empty(0, 16, 8, device="cuda")
+    dx, dw, db = gc.dwconv1d_btc_backward(x, w, dy, stride=1, padding=1)
+    torch.cuda.synchronize()
+    assert tuple(dx.shape) == (0, 16, 8)
+    assert bool((dw == 0).all()) and bool((db == 0).all())
+
+
 # ---------------------------------------------------------------- the five workloads at full size
 
 def _sample_idx(total, n, seed):
