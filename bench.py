@@ -2,6 +2,7 @@
 """Benchmark of the grouped-convolution forward engine on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-others]
+                    [--backward data|filter]
 
 One step = one gconv_fwd call (host validation, route selection, the kernel and
 its fused epilogue) on one batch of the workload.  The default workload is the
@@ -189,6 +190,90 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20):
             "wall_s": wall, "kernel": kernel, "rotation_sets": nsets}
 
 
+def measure_dw1d_backward(wl, kind, steps, rotate_bytes=512 << 20):
+    """Per-call device time of the input gradient (kind "data") or the filter and
+    bias gradients (kind "filter", two kernels per call) of the depthwise conv1d of
+    workload `wl`, from a replayed HIP graph of one call per rotating buffer set
+    (events on the replay stream).  Returns (ms per call, kernel name)."""
+    import torch
+    import depthwise_convolution_gconv_amd as gc
+    from depthwise_convolution_gconv_amd.workloads import draw, make_inputs
+
+    dev = torch.device("cuda", 0)
+    x, w, _ = make_inputs(wl)
+    B, T, C = wl.x_shape
+    K = wl.w_shape[2]
+    To = gc.gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, "ntc")[1]
+    dy = draw((B, To, C), 1.0, 4000 + wl.index, wl.dtype)
+    x, w, dy = x.to(dev), w.to(dev), dy.to(dev)
+    nsets = min(32, max(1, math.ceil(rotate_bytes / bwd_bytes(wl, kind))))
+    sets = []
+    for i in range(nsets):
+        xi, dyi = (x, dy) if i == 0 else (x.clone(), dy.clone())
+        if kind == "data":
+            sets.append((dyi, w, torch.empty_like(xi)))
+        else:
+            ws = torch.empty(gc.gconv_dw1d_bwd_filter_workspace(wl.x_shape, wl.w_shape, wl.stride, wl.pad,
+                                                                wl.dilation, wl.dtype), dtype=torch.uint8, device=dev)
+            sets.append((xi, dyi, torch.empty_like(w), torch.empty(C, dtype=w.dtype, device=dev), ws))
+    gstream = torch.cuda.Stream(dev)
+
+    def call(st):
+        if kind == "data":
+            gc.gconv_dw1d_bwd_data(st[0], st[1], T, wl.stride, wl.pad, wl.dilation, dx=st[2], stream=gstream)
+        else:
+            gc.gconv_dw1d_bwd_filter(st[0], st[1], K, wl.stride, wl.pad, wl.dilation, dw=st[2], db=st[3],
+                                     workspace=st[4], stream=gstream)
+
+    with torch.cuda.stream(gstream):
+        for st in sets[:3]:
+            call(st)
+    kernel = gc.gconv_last_kernel()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=gstream):
+        for st in sets:
+            call(st)
+    reps = max(1, round(steps / nsets))
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(gstream):
+        graph.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(gstream):
+        g0.record(gstream)
+        for _ in range(reps):
+            graph.replay()
+        g1.record(gstream)
+    torch.cuda.synchronize()
+    return g0.elapsed_time(g1) / (reps * nsets), kernel
+
+
+def bwd_bytes(wl, kind):
+    """Algorithmic bytes of one backward call: dy + w + dx (data), x + dy + dw + db (filter)."""
+    es = 4 if wl.dtype == "f32" else 2
+    B, T, C = wl.x_shape
+    K = wl.w_shape[2]
+    To = (T + 2 * wl.pad - wl.dilation * (K - 1) - 1) // wl.stride + 1
+    if kind == "data":
+        return (B * To * C + C * K + B * T * C) * es
+    return (B * T * C + B * To * C + C * K + C) * es
+
+
+def bwd_entry(wl, kind, steps):
+    ms, kernel = measure_dw1d_backward(wl, kind, steps)
+    byts = bwd_bytes(wl, kind)
+    B, T, C = wl.x_shape
+    K = wl.w_shape[2]
+    To = (T + 2 * wl.pad - wl.dilation * (K - 1) - 1) // wl.stride + 1
+    f = 2 * B * To * C * K
+    gbs = byts / (ms * 1e-3) / 1e9
+    return {"kernel": kernel, "kernel_ms_avg": round(ms, 5), "tflops": round(f / (ms * 1e-3) / 1e12, 3),
+            "gb_per_s": round(gbs, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
 def roofline(wl, route, kernel_ms, traffic):
     f = flops(wl)
     byts = alg_bytes(wl)
@@ -270,6 +355,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--backward", choices=["data", "filter"], default=None,
+                    help="only time the backward of the Conformer depthwise conv1d (input or filter gradient)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 5 plain device copies of 256 MiB (scale for HBM byte counters)")
     args = ap.parse_args()
@@ -294,6 +381,11 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read_per_launch": nbytes, "copy_bytes_written_per_launch": nbytes,
                           "launches": 5}))
+        return
+
+    if args.backward:
+        print(json.dumps({"backward": args.backward, "workload": "c3_dw1d_btc_f32",
+                          **bwd_entry(WORKLOADS["c3_dw1d_btc_f32"], args.backward, args.steps)}))
         return
 
     name = args.workload or HEADLINE
@@ -333,6 +425,10 @@ def main():
         # Strided depthwise layers (beyond the five workloads above).
         out["next"] = {oname: measure_entry(owl, args.steps)
                        for oname, owl in NEXT_WORKLOADS.items() if oname != name}
+        # Backward of the Conformer depthwise conv1d (same shapes as its forward).
+        conf = WORKLOADS["c3_dw1d_btc_f32"]
+        out["next"]["n5_dw1d_bwd_data_f32"] = bwd_entry(conf, "data", args.steps)
+        out["next"]["n6_dw1d_bwd_filter_f32"] = bwd_entry(conf, "filter", args.steps)
     print(json.dumps(out))
 
 

@@ -11,9 +11,10 @@
 //  * dw1d_btc_wgrad_partial: one workgroup per tile of TT output steps x 64
 //    channels of one batch entry.  The tile's dy rows and the x rows they read
 //    ((TT-1)*s + (K-1)*d + 1 of them, zero outside [0, T)) are staged in LDS as
-//    fp32 with loads coalesced along C; the 4 waves split the taps (wave g takes
-//    taps g, g+4, ...; wave 0 also sums dy for the bias), lane = channel.  The
-//    tile's fp32 sums go to part[tile][k][c] (k = K holds the bias sums).
+//    fp32 with 16-byte loads along C, 8 in flight per thread; the 4 waves split
+//    the taps (wave g takes taps g, g+4, ...; wave 0 also sums dy for the bias),
+//    lane = channel.  The tile's fp32 sums go to part[tile][k][c] (k = K holds
+//    the bias sums).
 //  * dw1d_btc_wgrad_reduce: one workgroup per (tap, 64 channels); 4 slices of
 //    the tiles are summed in order, then combined in a fixed order and rounded
 //    once to the tensor dtype.
@@ -28,18 +29,40 @@ constexpr int kThreads = 256;
 constexpr int kCT = 64;                      // channels per tile (lanes)
 constexpr int kGroups = kThreads / kCT;      // waves, each taking every 4th tap
 constexpr int kMaxTT = 64;                   // output steps per tile
-constexpr int kLdsMax = 60 * 1024;
+constexpr int kLdsMax = 40 * 1024;           // 4 workgroups per CU
 
-// NT: taps per wave (K <= 4 * NT).
-template <typename T, int NT>
+// Element e of VE consecutive values of T held in dwords.
+template <typename T> __device__ __forceinline__ float elem(const uint32_t *v, int e);
+template <> __device__ __forceinline__ float elem<float>(const uint32_t *v, int e)
+{
+    return __builtin_bit_cast(float, v[e]);
+}
+template <> __device__ __forceinline__ float elem<_Float16>(const uint32_t *v, int e)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+}
+template <> __device__ __forceinline__ float elem<__bf16>(const uint32_t *v, int e)
+{
+    return __builtin_bit_cast(float, (v[e >> 1] >> (16 * (e & 1))) << 16);
+}
+
+// NT: taps per wave (K <= 4 * NT).  VE: channels per staging load (16 bytes, or one
+// element when C or the pointers do not allow that).
+// UNIT (stride 1, dilation 1): wave g takes the contiguous taps g*NT .. g*NT+NT-1
+// and slides a register window of NT input steps down the tile (one new LDS read
+// per step); otherwise wave g takes taps g, g+4, ... and reads each from LDS.
+template <typename T, int NT, int VE, bool UNIT>
 __global__ void __launch_bounds__(kThreads)
 dw1d_btc_wgrad_partial(const T *__restrict__ x, const T *__restrict__ dy, float *__restrict__ part,
                        int T_in, int C, int To, int K, int s, int p, int d, int TT, int NRW,
                        int tblocks, int cblocks)
 {
+    constexpr int DW = (VE * (int)sizeof(T) + 3) / 4;   // dwords per staging load
+    constexpr int CPR = kCT / VE;                       // staging loads per row of 64 channels
+    constexpr int NB = 8;                               // staging loads in flight per thread
     extern __shared__ float sm[];
     float *dys = sm;                  // [TT][kCT]
-    float *xs = sm + TT * kCT;        // [NRW][kCT]
+    float *xs = sm + TT * kCT;        // [NRW][kCT], directly after the dy rows
     const int tid = threadIdx.x, lane = tid % kCT, g = tid / kCT;
     int rest = blockIdx.x;
     const int cb = rest % cblocks;
@@ -49,17 +72,49 @@ dw1d_btc_wgrad_partial(const T *__restrict__ x, const T *__restrict__ dy, float 
     const int t0 = tb * TT, c0 = cb * kCT, c = c0 + lane;
     const bool cok = c < C;
 
-    // Stage dy[bi, t0 .. t0+TT) and x[bi, t0*s - p .. + NRW), zero outside the
-    // tensors (lane = channel: each row is one coalesced read of 64 channels).
+    // Stage the TT rows of dy[bi, t0 ..] and the NRW rows of x[bi, t0*s - p ..] (LDS
+    // rows 0 .. TT + NRW, in that order), zero outside the tensors, VE channels per
+    // load along C, NB loads in flight per thread.
     const T *dyb = dy + (int64_t)bi * To * C;
     const T *xb = x + (int64_t)bi * T_in * C;
-    for (int r = g; r < TT; r += kGroups) {
-        const int t = t0 + r;
-        dys[r * kCT + lane] = (cok && t < To) ? to_f32(dyb[(int64_t)t * C + c]) : 0.0f;
-    }
-    for (int r = g; r < NRW; r += kGroups) {
-        const int ti = t0 * s - p + r;
-        xs[r * kCT + lane] = (cok && ti >= 0 && ti < T_in) ? to_f32(xb[(int64_t)ti * C + c]) : 0.0f;
+    const int nchunks = (TT + NRW) * CPR;
+    for (int base = 0; base < nchunks; base += NB * kThreads) {
+        uint32_t v[NB][DW];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            const int r = i / CPR, cc = c0 + (i - r * CPR) * VE;
+            const T *src = nullptr;
+            if (i < nchunks && cc < C) {
+                if (r < TT) {
+                    if (t0 + r < To) src = dyb + (int64_t)(t0 + r) * C + cc;
+                } else {
+                    const int ti = t0 * s - p + (r - TT);
+                    if (ti >= 0 && ti < T_in) src = xb + (int64_t)ti * C + cc;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < DW; ++q) v[j][q] = 0;
+            if (src) {
+                if constexpr (DW == 4) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(src);
+                    v[j][0] = u.x; v[j][1] = u.y; v[j][2] = u.z; v[j][3] = u.w;
+                } else if constexpr (sizeof(T) == 4) {
+                    v[j][0] = __builtin_bit_cast(uint32_t, *src);
+                } else {
+                    v[j][0] = __builtin_bit_cast(uint16_t, *src);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            if (i < nchunks) {
+                const int r = i / CPR, cv = (i - r * CPR) * VE;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) sm[r * kCT + cv + e] = elem<T>(v[j], e);
+            }
+        }
     }
     __syncthreads();
 
@@ -68,21 +123,49 @@ dw1d_btc_wgrad_partial(const T *__restrict__ x, const T *__restrict__ dy, float 
     for (int j = 0; j < NT; ++j) acc[j] = 0.0f;
     float accb = 0.0f;
     const int tn = min(TT, To - t0);   // output steps of this tile that exist
-    for (int t = 0; t < tn; ++t) {
-        const float dv = dys[t * kCT + lane];
-        accb += dv;
-        const float *xr = xs + (t * s) * kCT + lane;
+    if constexpr (UNIT) {
+        // Before step t + u, slot (j + u) % NT holds x row t + u + k0 + j; after the
+        // step, the slot that held j = 0 takes row t + u + k0 + NT (rows up to
+        // TT - 1 + 4*NT, all staged).
+        const int k0 = g * NT;
+        const float *xr = xs + k0 * kCT + lane;
+        float win[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int k = g + kGroups * j;
-            if (k < K) acc[j] = fmaf(dv, xr[k * d * kCT], acc[j]);
+        for (int j = 0; j < NT; ++j) win[j] = xr[j * kCT];
+        int t = 0;
+        for (; t + NT <= tn; t += NT) {
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                const float dv = dys[(t + u) * kCT + lane];
+                accb += dv;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) acc[j] = fmaf(dv, win[(j + u) % NT], acc[j]);
+                win[u] = xr[(t + u + NT) * kCT];
+            }
+        }
+        for (; t < tn; ++t) {
+            const float dv = dys[t * kCT + lane];
+            accb += dv;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[j] = fmaf(dv, xr[(t + j) * kCT], acc[j]);
+        }
+    } else {
+        for (int t = 0; t < tn; ++t) {
+            const float dv = dys[t * kCT + lane];
+            accb += dv;
+            const float *xr = xs + (t * s) * kCT + lane;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int k = g + kGroups * j;
+                if (k < K) acc[j] = fmaf(dv, xr[k * d * kCT], acc[j]);
+            }
         }
     }
     if (!cok) return;
     float *pt = part + (int64_t)blockIdx.x / cblocks * (K + 1) * C + c;   // tile (bi, tb)
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int k = g + kGroups * j;
+        const int k = UNIT ? g * NT + j : g + kGroups * j;
         if (k < K) pt[(int64_t)k * C] = acc[j];
     }
     if (g == 0) pt[(int64_t)K * C] = accb;
@@ -97,9 +180,23 @@ dw1d_btc_wgrad_reduce(const float *__restrict__ part, T *__restrict__ dw, T *__r
     const int tid = threadIdx.x, lane = tid % kCT, q = tid / kCT;
     const int kk = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;   // kk == K: the bias row
     const int c = cb * kCT + lane;
+    // Tiles q, q + 4, q + 8, ... in order, 8 loads in flight at a time.
+    constexpr int NB = 8;
     float acc = 0.0f;
-    if (c < C)
-        for (int i = q; i < ntiles; i += kGroups) acc += part[((int64_t)i * (K + 1) + kk) * C + c];
+    if (c < C) {
+        const float *src = part + (int64_t)kk * C + c;
+        const int64_t step = (int64_t)(K + 1) * C;
+        for (int i0 = q; i0 < ntiles; i0 += NB * kGroups) {
+            float v[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int i = i0 + j * kGroups;
+                v[j] = i < ntiles ? src[i * step] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc += v[j];
+        }
+    }
     red[q][lane] = acc;
     __syncthreads();
     if (q != 0 || c >= C) return;
@@ -110,6 +207,7 @@ dw1d_btc_wgrad_reduce(const float *__restrict__ part, T *__restrict__ dw, T *__r
 
 struct Plan {
     int TT, NRW, NT, tblocks, cblocks, ntiles;
+    bool unit;
     size_t lds, ws_bytes;
     bool ok;
 };
@@ -118,11 +216,18 @@ Plan make_plan(const Dw1dArgs &a)
 {
     Plan pl{};
     pl.ok = false;
-    pl.NT = (int)ceil_div(a.K, kGroups);
-    if (pl.NT > 16) return pl;                           // K <= 64
+    // Taps per wave, as compiled: the next power of two (the window of the unit
+    // path spans that many taps per wave).
+    const int64_t nt = ceil_div(a.K, kGroups);
+    if (nt > 16) return pl;                              // K <= 64
+    pl.NT = nt <= 1 ? 1 : nt <= 2 ? 2 : nt <= 4 ? 4 : nt <= 8 ? 8 : 16;
+    // Staged x rows: those the tile reads, and with unit stride and dilation the
+    // window's reach (TT - 1 + 4*NT: the taps are rounded up to 4 waves of NT).
+    pl.unit = a.s == 1 && a.d == 1;
     int64_t TT = kMaxTT, NRW = 0;
     for (; TT >= 1; TT /= 2) {
         NRW = (TT - 1) * a.s + (a.K - 1) * a.d + 1;
+        if (pl.unit) NRW = std::max<int64_t>(NRW, TT + kGroups * pl.NT);
         if ((TT + NRW) * kCT * (int64_t)sizeof(float) <= kLdsMax) break;
     }
     if (TT < 1) return pl;
@@ -139,13 +244,26 @@ Plan make_plan(const Dw1dArgs &a)
     return pl;
 }
 
-template <typename T, int NT>
-hipError_t run_partial(const Dw1dArgs &a, const Plan &pl, const void *x, const void *dy, float *part)
+template <typename T, int NT, int VE, bool UNIT>
+hipError_t run_partial_ve(const Dw1dArgs &a, const Plan &pl, const void *x, const void *dy, float *part)
 {
-    hipLaunchKernelGGL((dw1d_btc_wgrad_partial<T, NT>), dim3((unsigned)(pl.ntiles * (int64_t)pl.cblocks)),
+    hipLaunchKernelGGL((dw1d_btc_wgrad_partial<T, NT, VE, UNIT>), dim3((unsigned)(pl.ntiles * (int64_t)pl.cblocks)),
                        dim3(kThreads), pl.lds, a.stream, (const T *)x, (const T *)dy, part, (int)a.T,
                        (int)a.C, (int)a.To, (int)a.K, a.s, a.p, a.d, pl.TT, pl.NRW, pl.tblocks, pl.cblocks);
     return hipGetLastError();
+}
+
+template <typename T, int NT>
+hipError_t run_partial(const Dw1dArgs &a, const Plan &pl, const void *x, const void *dy, float *part)
+{
+    constexpr int VE = 16 / sizeof(T);
+    const bool vec = a.C % VE == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(dy) & 15) == 0;
+    if (pl.unit)
+        return vec ? run_partial_ve<T, NT, VE, true>(a, pl, x, dy, part)
+                   : run_partial_ve<T, NT, 1, true>(a, pl, x, dy, part);
+    return vec ? run_partial_ve<T, NT, VE, false>(a, pl, x, dy, part)
+               : run_partial_ve<T, NT, 1, false>(a, pl, x, dy, part);
 }
 
 template <typename T>
