@@ -260,7 +260,7 @@ def bwd_bytes(wl, kind):
     return (B * T * C + B * To * C + C * K + C) * es
 
 
-def bwd_entry(wl, kind, steps):
+def bwd_entry(wl, kind, steps, name=None):
     ms, kernel = measure_dw1d_backward(wl, kind, steps)
     byts = bwd_bytes(wl, kind)
     B, T, C = wl.x_shape
@@ -271,7 +271,9 @@ def bwd_entry(wl, kind, steps):
     return {"kernel": kernel, "kernel_ms_avg": round(ms, 5), "tflops": round(f / (ms * 1e-3) / 1e12, 3),
             "gb_per_s": round(gbs, 1),
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": counters_traffic(name, "dw1d_ntc.hip" if kind == "data" else "dw1d_wgrad.hip")
+                         if name else None}}
 
 
 def roofline(wl, route, kernel_ms, traffic):
@@ -385,7 +387,9 @@ def main():
 
     if args.backward:
         print(json.dumps({"backward": args.backward, "workload": "c3_dw1d_btc_f32",
-                          **bwd_entry(WORKLOADS["c3_dw1d_btc_f32"], args.backward, args.steps)}))
+                          **bwd_entry(WORKLOADS["c3_dw1d_btc_f32"], args.backward, args.steps,
+                                      f"n5_dw1d_bwd_data_f32" if args.backward == "data"
+                                      else "n6_dw1d_bwd_filter_f32")}))
         return
 
     name = args.workload or HEADLINE
@@ -427,8 +431,8 @@ def main():
                        for oname, owl in NEXT_WORKLOADS.items() if oname != name}
         # Backward of the Conformer depthwise conv1d (same shapes as its forward).
         conf = WORKLOADS["c3_dw1d_btc_f32"]
-        out["next"]["n5_dw1d_bwd_data_f32"] = bwd_entry(conf, "data", args.steps)
-        out["next"]["n6_dw1d_bwd_filter_f32"] = bwd_entry(conf, "filter", args.steps)
+        out["next"]["n5_dw1d_bwd_data_f32"] = bwd_entry(conf, "data", args.steps, "n5_dw1d_bwd_data_f32")
+        out["next"]["n6_dw1d_bwd_filter_f32"] = bwd_entry(conf, "filter", args.steps, "n6_dw1d_bwd_filter_f32")
     print(json.dumps(out))
 
 
