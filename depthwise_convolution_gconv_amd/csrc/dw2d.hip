@@ -15,9 +15,10 @@
 //    i.e. in the memory order of y, and workgroup b takes runs_per_wg consecutive
 //    ones, so a workgroup's stores cover one contiguous stretch of y.
 //  * Staging: the zero-padded input rows those runs read (virtual rows of the
-//    padded planes, so a workgroup may span plane boundaries) go to LDS as fp32,
-//    one row every WP floats, with 16-byte buffer loads along W (out-of-range
-//    offsets read as zero, which supplies the padding rows).  The filters of the
+//    padded planes, so a workgroup may span plane boundaries) go to LDS (fp32,
+//    or the raw 16 bits of 16-bit tensors), one row every WP elements, with
+//    16-byte buffer loads along W (out-of-range offsets read as zero, which
+//    supplies the padding rows).  The filters of the
 //    planes the workgroup touches go next to them.
 //  * Compute: each thread slides its run's window ((R-1)*S + K input columns,
 //    16-byte LDS reads) down the K filter rows, R fp32 accumulators, bias added
@@ -25,6 +26,7 @@
 //  * Workgroups are dealt to the XCDs in contiguous runs (workgroup b runs on XCD
 //    b % 8), so the halo rows that neighbouring workgroups share come from one L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "fastdiv.hpp"
@@ -72,19 +74,19 @@ template <> struct Load<2> {
     }
 };
 
-// Element e of a staged vector of T held in dwords.
-template <typename T> __device__ __forceinline__ float elem(const uint32_t *d, int e);
-template <> __device__ __forceinline__ float elem<float>(const uint32_t *d, int e)
+// LDS element of the staged input: fp32 for fp32 tensors, the raw 16 bits for
+// 16-bit ones (widened when read, which halves the LDS a workgroup's rows take).
+template <typename T> using LdsT = std::conditional_t<sizeof(T) == 4, float, uint16_t>;
+template <typename T> __device__ __forceinline__ LdsT<T> lds_elem(const uint32_t *d, int e)
 {
-    return __builtin_bit_cast(float, d[e]);
+    if constexpr (sizeof(T) == 4) return __builtin_bit_cast(float, d[e]);
+    else return (uint16_t)(d[e >> 1] >> (16 * (e & 1)));
 }
-template <> __device__ __forceinline__ float elem<_Float16>(const uint32_t *d, int e)
+template <typename T> __device__ __forceinline__ float widen(LdsT<T> v)
 {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)(d[e >> 1] >> (16 * (e & 1))));
-}
-template <> __device__ __forceinline__ float elem<__bf16>(const uint32_t *d, int e)
-{
-    return __builtin_bit_cast(float, (d[e >> 1] >> (16 * (e & 1))) << 16);
+    if constexpr (sizeof(T) == 4) return v;
+    else if constexpr (std::is_same_v<T, _Float16>) return (float)__builtin_bit_cast(_Float16, v);
+    else return __builtin_bit_cast(float, (uint32_t)v << 16);
 }
 
 // Bits of one rounded T value (round to nearest even), in the low bits of a dword.
@@ -119,13 +121,15 @@ __global__ void __launch_bounds__(kThreads)
 dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
           T *__restrict__ y, Dw2dGeom g)
 {
+    using LT = LdsT<T>;
     constexpr int KK = K * K;
-    constexpr bool kVecRead = (R * S) % 4 == 0;           // window starts are 16-byte aligned
+    constexpr int G = 16 / (int)sizeof(LT);               // LDS elements per 16-byte read
+    constexpr bool kVecRead = (R * S) % G == 0;           // window starts are 16-byte aligned
     constexpr int NWIN = (R - 1) * S + K;                 // input columns of one run
-    constexpr int NWR = kVecRead ? (NWIN + 3) / 4 * 4 : NWIN;
+    constexpr int NWR = kVecRead ? (NWIN + G - 1) / G * G : NWIN;
     constexpr int DW = (VI * (int)sizeof(T) + 3) / 4;     // dwords per staging load
     constexpr int NB = 8;                                 // staging loads in flight per thread
-    extern __shared__ float lds[];
+    extern __shared__ uint4 lds[];
 
     const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
     const int wg = xcd * g.wgs_per_xcd + rank;
@@ -140,8 +144,8 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     const int pa = fdiv(vr_a, g.fd_oh), pb = fdiv(vr_b, g.fd_oh);
     const int R_lo = pa * g.Hp + (vr_a - pa * g.OH) * S;
     const int NR = pb * g.Hp + (vr_b - pb * g.OH) * S + K - R_lo;
-    float *xs = lds;                          // [NR][WP]
-    float *ws = lds + g.NRmax * g.WP;         // [pb - pa + 1][K*K]
+    LT *xs = reinterpret_cast<LT *>(lds);                 // [NR][WP]
+    float *ws = reinterpret_cast<float *>(xs + g.NRmax * g.WP);   // [pb - pa + 1][K*K] (16-byte aligned)
 
     // Input plane read by output plane p: image n = p / Cout, channel (p % Cout) / M.
     auto in_plane = [&](int p) {
@@ -176,13 +180,13 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         for (int j = 0; j < NB; ++j)
             if (dst[j] >= 0) {
 #pragma unroll
-                for (int q = 0; q < VI; ++q) xs[dst[j] + q] = elem<T>(d[j], q);
+                for (int q = 0; q < VI; ++q) xs[dst[j] + q] = lds_elem<T>(d[j], q);
             }
     }
     // Columns outside the image: zero.
     for (int i = tid; i < NR * g.npad; i += kThreads) {
         const int r = fdiv(i, g.fd_npad), c = i - r * g.npad;
-        xs[r * g.WP + (c < g.pw ? c : c + g.W)] = 0.0f;
+        xs[r * g.WP + (c < g.pw ? c : c + g.W)] = LT(0);   // +0.0 in every storage type
     }
     // Filters of output planes pa .. pb.
     for (int i = tid; i < (pb - pa + 1) * KK; i += kThreads) {
@@ -200,19 +204,21 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = b0;
         const float *wt = ws + (p - pa) * KK;
-        const float *xrow = xs + (p * g.Hp + oh * S - R_lo) * g.WP + rc * (R * S);
+        const LT *xrow = xs + (p * g.Hp + oh * S - R_lo) * g.WP + rc * (R * S);
 #pragma unroll
         for (int kh = 0; kh < K; ++kh) {
             float win[NWR];
             if constexpr (kVecRead) {
 #pragma unroll
-                for (int v = 0; v < NWR / 4; ++v) {
-                    const float4 q = *reinterpret_cast<const float4 *>(xrow + kh * g.WP + 4 * v);
-                    win[4 * v] = q.x; win[4 * v + 1] = q.y; win[4 * v + 2] = q.z; win[4 * v + 3] = q.w;
+                for (int v = 0; v < NWR / G; ++v) {
+                    LT q[G];
+                    *reinterpret_cast<uint4 *>(q) = *reinterpret_cast<const uint4 *>(xrow + kh * g.WP + G * v);
+#pragma unroll
+                    for (int e = 0; e < G; ++e) win[G * v + e] = widen<T>(q[e]);
                 }
             } else {
 #pragma unroll
-                for (int v = 0; v < NWR; ++v) win[v] = xrow[kh * g.WP + v];
+                for (int v = 0; v < NWR; ++v) win[v] = widen<T>(xrow[kh * g.WP + v]);
             }
 #pragma unroll
             for (int kw = 0; kw < K; ++kw) {
@@ -261,8 +267,10 @@ Plan make_plan(const Conv2dArgs &a)
     if (planes * Hp + 2 * K >= (int64_t(1) << 31) || total_runs >= (int64_t(1) << 31)) return pl;
     const int R = pl.R;
     const int NWIN = (R - 1) * S + K;
-    const int NWR = (R * S) % 4 == 0 ? (NWIN + 3) / 4 * 4 : NWIN;
-    const int64_t WP = (std::max<int64_t>(a.W + 2 * a.pw, (RPR - 1) * R * S + NWR) + 3) / 4 * 4;
+    const int les = es;                                   // LDS bytes per staged element
+    const int G = 16 / les;
+    const int NWR = (R * S) % G == 0 ? (NWIN + G - 1) / G * G : NWIN;
+    const int64_t WP = (std::max<int64_t>(a.W + 2 * a.pw, (RPR - 1) * R * S + NWR) + G - 1) / G * G;
     // Runs per workgroup: as many as keep the workgroup's LDS within kLdsTarget, so
     // that 8 workgroups stay resident per CU with the most input bytes in flight
     // (measured on the 8 x 256 x 512 x 40 layers: stride 1 took 114 us with 256 runs
@@ -276,7 +284,7 @@ Plan make_plan(const Conv2dArgs &a)
         NR = std::min<int64_t>(NR, planes * Hp);
         const int64_t NP = std::min<int64_t>(crossings + 1, planes);
         *nr_out = NR;
-        return (NR * WP + NP * K * K) * (int64_t)sizeof(float);
+        return NR * WP * les + NP * K * K * (int64_t)sizeof(float);
     };
     int64_t passes = 8, nr = 0;
     while (passes > 1 && lds_for(passes * kThreads, &nr) > kLdsTarget) --passes;
