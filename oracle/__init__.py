@@ -17,7 +17,9 @@ Sources followed (cited by page title and the reply or code block on it):
   ibmua's reply on output ordering: the usual order is group-contiguous.
 * discuss.pytorch.org "F.conv2d runs x15 slower in mixed-precision/half-precision
   mode", the test script: ``F.conv2d(input, weight, padding=3 // 2, groups=4)``
-  -- cross-correlation with symmetric zero padding.
+  -- cross-correlation with symmetric zero padding; its later replies turn to the
+  NHWC (channels_last) memory format (``conv2d_nhwc``: the same sum over
+  x [N,H,W,C], w [Cout,KH,KW,C/g], y [N,OH,OW,Cout]).
 * speechbrain issue #2733 "Investigate custom Triton kernels for
   depthwise-separable convolutions in Conformer": depthwise conv with groups equal
   to the channel count, over a (batch, steps, channels) tensor; in its follow-up
@@ -74,6 +76,10 @@ def _load():
         lib.gconv_oracle_dwconv1d_btc.argtypes = dw_args + [_dp]
         lib.gconv_oracle_dwconv1d_btc_at.restype = ctypes.c_int
         lib.gconv_oracle_dwconv1d_btc_at.argtypes = dw_args + [_ip, _i64, _dp]
+        lib.gconv_oracle_conv2d_nhwc.restype = ctypes.c_int
+        lib.gconv_oracle_conv2d_nhwc.argtypes = conv_args + [_dp]
+        lib.gconv_oracle_conv2d_nhwc_at.restype = ctypes.c_int
+        lib.gconv_oracle_conv2d_nhwc_at.argtypes = conv_args + [_ip, _i64, _dp]
         bwd_args = [_dp, _i64, _i64, _i64, _dp, _i64, _i64, _i64, _i64]
         lib.gconv_oracle_dwconv1d_btc_bwd_data.restype = ctypes.c_int
         lib.gconv_oracle_dwconv1d_btc_bwd_data.argtypes = bwd_args + [_dp]
@@ -239,3 +245,46 @@ def dwconv1d_btc_bwd_filter(x, dy, K: int, stride=1, padding=0, dilation=1):
     _rc(lib.gconv_oracle_dwconv1d_btc_bwd_filter(xp, dyp, B, T, C, int(K), int(stride), int(padding),
                                                  int(dilation), dw.ctypes.data_as(_dp), db.ctypes.data_as(_dp)))
     return dw, db
+
+
+def conv2d_nhwc(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1) -> np.ndarray:
+    """Grouped conv2d forward in fp64 over channels-last tensors: x [N,H,W,C],
+    w [Cout,KH,KW,C/groups], bias [Cout] or None; returns y [N,OH,OW,Cout]."""
+    lib = _load()
+    x, xp = _f64(x)
+    w, wp = _f64(w)
+    N, H, W, C = x.shape
+    Cout, KH, KW, Cg_w = w.shape
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    dh, dw = _pair(dilation)
+    bp = None
+    if bias is not None:
+        bias, bp = _f64(bias)
+    OH = out_len(H, KH, sh, ph, dh)
+    OW = out_len(W, KW, sw, pw, dw)
+    y = np.zeros((N, max(OH, 0), max(OW, 0), Cout), dtype=np.float64)
+    _rc(lib.gconv_oracle_conv2d_nhwc(xp, N, C, H, W, wp, Cout, Cg_w, KH, KW, bp, groups,
+                                     sh, sw, ph, pw, dh, dw, y.ctypes.data_as(_dp)))
+    return y
+
+
+def conv2d_nhwc_at(x, w, flat_idx, bias=None, stride=1, padding=0, dilation=1, groups=1) -> np.ndarray:
+    """The elements y.flat[flat_idx] of conv2d_nhwc(...), evaluated one by one."""
+    lib = _load()
+    x, xp = _f64(x)
+    w, wp = _f64(w)
+    N, H, W, C = x.shape
+    Cout, KH, KW, Cg_w = w.shape
+    sh, sw = _pair(stride)
+    ph, pw = _pair(padding)
+    dh, dw = _pair(dilation)
+    bp = None
+    if bias is not None:
+        bias, bp = _f64(bias)
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    out = np.zeros(idx.shape, dtype=np.float64)
+    _rc(lib.gconv_oracle_conv2d_nhwc_at(xp, N, C, H, W, wp, Cout, Cg_w, KH, KW, bp, groups,
+                                        sh, sw, ph, pw, dh, dw, idx.ctypes.data_as(_ip), idx.size,
+                                        out.ctypes.data_as(_dp)))
+    return out

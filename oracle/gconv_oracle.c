@@ -325,3 +325,79 @@ int gconv_oracle_dwconv1d_btc_bwd_filter(const double *x, const double *dy, int6
     }
     return 0;
 }
+
+/* ---- grouped conv2d over channels-last (NHWC) tensors -----------------------
+ *
+ * The discuss.pytorch.org thread "F.conv2d runs x15 slower in mixed-precision/
+ * half-precision mode" (replies 7-11) turns to the NHWC (channels_last) memory
+ * format for the fp16 grouped conv.  The sum is the one above, only the element
+ * addresses change: x[n][ih][iw][c], w[o][kh][kw][ci] (PyTorch's channels_last
+ * weight order), y[n][oh][ow][o].
+ */
+static double conv2d_nhwc_one(const conv2d_geom *g, const double *x, const double *w,
+                              const double *bias, int64_t n, int64_t o, int64_t oh, int64_t ow)
+{
+    const int64_t Cg = g->C / g->groups;
+    const int64_t Ng = g->Cout / g->groups;
+    const int64_t k = o / Ng;
+    double acc = bias ? bias[o] : 0.0;
+    for (int64_t kh = 0; kh < g->KH; ++kh) {
+        const int64_t ih = oh * g->sh - g->ph + kh * g->dh;
+        if (ih < 0 || ih >= g->H) continue;
+        for (int64_t kw = 0; kw < g->KW; ++kw) {
+            const int64_t iw = ow * g->sw - g->pw + kw * g->dw;
+            if (iw < 0 || iw >= g->W) continue;
+            for (int64_t ci = 0; ci < Cg; ++ci) {
+                const double xv = x[((n * g->H + ih) * g->W + iw) * g->C + k * Cg + ci];
+                const double wv = w[((o * g->KH + kh) * g->KW + kw) * Cg + ci];
+                acc += xv * wv;
+            }
+        }
+    }
+    return acc;
+}
+
+/* x: [N][H][W][C]; w: [Cout][KH][KW][Cg_w] with Cg_w == C/groups; bias [Cout] or
+ * NULL; y: [N][OH][OW][Cout]. */
+int gconv_oracle_conv2d_nhwc(const double *x, int64_t N, int64_t C, int64_t H, int64_t W,
+                             const double *w, int64_t Cout, int64_t Cg_w, int64_t KH, int64_t KW,
+                             const double *bias, int64_t groups,
+                             int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                             double *y)
+{
+    conv2d_geom g;
+    int rc = conv2d_geom_make(&g, N, C, H, W, Cout, Cg_w, KH, KW, groups, sh, sw, ph, pw, dh, dw);
+    if (rc) return rc;
+#pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < N * g.OH * g.OW; ++q) {
+        const int64_t n = q / (g.OH * g.OW), oh = (q / g.OW) % g.OH, ow = q % g.OW;
+        for (int64_t o = 0; o < Cout; ++o)
+            y[q * Cout + o] = conv2d_nhwc_one(&g, x, w, bias, n, o, oh, ow);
+    }
+    return 0;
+}
+
+/* Selected outputs; idx[i] is a flat index into y[N][OH][OW][Cout]. */
+int gconv_oracle_conv2d_nhwc_at(const double *x, int64_t N, int64_t C, int64_t H, int64_t W,
+                                const double *w, int64_t Cout, int64_t Cg_w, int64_t KH, int64_t KW,
+                                const double *bias, int64_t groups,
+                                int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                                const int64_t *idx, int64_t n_idx, double *out)
+{
+    conv2d_geom g;
+    int rc = conv2d_geom_make(&g, N, C, H, W, Cout, Cg_w, KH, KW, groups, sh, sw, ph, pw, dh, dw);
+    if (rc) return rc;
+    const int64_t total = N * g.OH * g.OW * Cout;
+    for (int64_t i = 0; i < n_idx; ++i)
+        if (idx[i] < 0 || idx[i] >= total) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n_idx; ++i) {
+        int64_t r = idx[i];
+        const int64_t o = r % Cout; r /= Cout;
+        const int64_t ow = r % g.OW; r /= g.OW;
+        const int64_t oh = r % g.OH;
+        const int64_t n = r / g.OH;
+        out[i] = conv2d_nhwc_one(&g, x, w, bias, n, o, oh, ow);
+    }
+    return 0;
+}
