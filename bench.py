@@ -47,15 +47,21 @@ PAGE_FP16_MS = 60.74
 def flops(wl, exact=False):
     from depthwise_convolution_gconv_amd import gconv_out_shape
     ys = gconv_out_shape(wl.x_shape, wl.w_shape, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout)
-    if wl.layout == "nchw":
-        N, Co, OH, OW = ys
-        _, Cg, KH, KW = wl.w_shape
+    if wl.layout in ("nchw", "nhwc"):
+        if wl.layout == "nchw":
+            N, Co, OH, OW = ys
+            _, Cg, KH, KW = wl.w_shape
+            H, W = wl.x_shape[2], wl.x_shape[3]
+        else:
+            N, OH, OW, Co = ys
+            _, KH, KW, Cg = wl.w_shape
+            H, W = wl.x_shape[1], wl.x_shape[2]
         if not exact:
             return 2 * N * Co * OH * OW * Cg * KH * KW
         rows = sum(1 for o in range(OH) for k in range(KH)
-                   if 0 <= o * wl.stride - wl.pad + k * wl.dilation < wl.x_shape[2])
+                   if 0 <= o * wl.stride - wl.pad + k * wl.dilation < H)
         cols = sum(1 for o in range(OW) for k in range(KW)
-                   if 0 <= o * wl.stride - wl.pad + k * wl.dilation < wl.x_shape[3])
+                   if 0 <= o * wl.stride - wl.pad + k * wl.dilation < W)
         return 2 * N * Co * Cg * rows * cols
     B, To, C = ys
     K = wl.w_shape[2]
@@ -94,7 +100,8 @@ KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_fwd_f32_mfma32x32x
                 "direct2d_g4": "direct2d.hip", "direct2d_tiled": "direct2d.hip",
                 "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip",
                 "dw1d_btc_tile": "dw1d_ntc.hip", "dw1d_btc_window": "dw1d_ntc.hip",
-                "dw1d_btc_generic": "dw1d_ntc.hip"}
+                "dw1d_btc_generic": "dw1d_ntc.hip", "dw2d_nhwc_tile": "nhwc.hip",
+                "conv2d_nhwc_generic": "nhwc.hip"}
 
 
 def counters_traffic(wl_name, kernel_file):

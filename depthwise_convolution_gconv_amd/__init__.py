@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     GconvLaunchError,
     PreparedCall,
     conv2d,
+    conv2d_nhwc,
     dwconv1d_btc,
     dwconv1d_btc_backward,
     gconv_dw1d_bwd_data,

@@ -17,7 +17,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgconv.so")
 
 OK, ERR_INVALID_ARG, ERR_SHAPE, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3, 4
-LAYOUTS = {"nchw": 0, "ntc": 1}
+LAYOUTS = {"nchw": 0, "ntc": 1, "nhwc": 2}
 DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 DTYPE_NAMES = {"f32": 0, "f16": 1, "bf16": 2}
 ROUTES = {"auto": 0, "direct": 1, "igemm": 2}
@@ -105,7 +105,7 @@ def _arr(ctype, vals):
 
 
 def _geom(layout: str, stride, pad, dilation):
-    n = 2 if layout == "nchw" else 1
+    n = 1 if layout == "ntc" else 2
 
     def norm(v):
         if isinstance(v, (tuple, list)):
@@ -130,7 +130,7 @@ def gconv_out_shape(x_shape: Sequence[int], w_shape: Sequence[int], stride=1, pa
     lay = _layout(layout)
     out = (_i64 * 4)()
     _check(L.gconv_out_shape(_arr(_i64, x_shape), _arr(_i64, w_shape), s, p, d, int(groups), lay, out))
-    return tuple(int(v) for v in out[: (4 if layout == "nchw" else 3)])
+    return tuple(int(v) for v in out[: (3 if layout == "ntc" else 4)])
 
 
 def gconv_select_route(x_shape, w_shape, stride=1, pad=0, dilation=1, groups: int = 1,
@@ -162,7 +162,7 @@ def _call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], y: Opt
             raise GconvError(ERR_INVALID_ARG, f"{name} is on {t.device}, x on {x.device}")
     if x.dtype not in DTYPES:
         raise GconvError(ERR_INVALID_ARG, f"unsupported dtype {x.dtype}")
-    expect_dims = 4 if layout == "nchw" else 3
+    expect_dims = 3 if layout == "ntc" else 4
     if x.dim() != expect_dims or w.dim() != expect_dims:
         raise GconvError(ERR_INVALID_ARG, f"{layout} expects {expect_dims}-D x and w")
     if bias is not None and (bias.dim() != 1 or bias.shape[0] != w.shape[0]):
@@ -217,6 +217,12 @@ def conv2d(x, weight, bias=None, stride=1, padding=0, dilation=1, groups: int = 
     """F.conv2d-style call: x [N,C,H,W], weight [Cout,C/groups,KH,KW]."""
     return _call(x, weight, bias, None, stride, padding, dilation, groups, "nchw",
                  None if route == "auto" else route, None)
+
+
+def conv2d_nhwc(x, weight, bias=None, stride=1, padding=0, dilation=1, groups: int = 1):
+    """Grouped conv2d over channels-last tensors: x [N,H,W,C], weight [Cout,KH,KW,C/groups];
+    returns y [N,OH,OW,Cout]."""
+    return _call(x, weight, bias, None, stride, padding, dilation, groups, "nhwc", None, None)
 
 
 def dwconv1d_btc(x, weight, bias=None, stride=1, padding=0, dilation=1):

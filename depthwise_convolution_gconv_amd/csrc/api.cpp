@@ -55,14 +55,19 @@ gconv_status_t validate(const int64_t *x_shape, const int64_t *w_shape, const in
 {
     if (!x_shape || !w_shape || !stride || !pad || !dilation)
         return fail(GCONV_ERR_INVALID_ARG, "NULL shape, stride, pad or dilation array");
-    if (layout != GCONV_LAYOUT_NCHW && layout != GCONV_LAYOUT_NTC)
+    if (layout != GCONV_LAYOUT_NCHW && layout != GCONV_LAYOUT_NTC && layout != GCONV_LAYOUT_NHWC)
         return fail(GCONV_ERR_INVALID_ARG, "unknown layout %lld", (long long)layout);
     if (groups < 1) return fail(GCONV_ERR_INVALID_ARG, "groups must be >= 1 (got %lld)", groups);
     g->layout = layout;
     g->groups = groups;
-    if (layout == GCONV_LAYOUT_NCHW) {
-        g->N = x_shape[0]; g->C = x_shape[1]; g->H = x_shape[2]; g->W = x_shape[3];
-        g->Cout = w_shape[0]; g->Cg_w = w_shape[1]; g->KH = w_shape[2]; g->KW = w_shape[3];
+    if (layout == GCONV_LAYOUT_NCHW || layout == GCONV_LAYOUT_NHWC) {
+        if (layout == GCONV_LAYOUT_NCHW) {
+            g->N = x_shape[0]; g->C = x_shape[1]; g->H = x_shape[2]; g->W = x_shape[3];
+            g->Cout = w_shape[0]; g->Cg_w = w_shape[1]; g->KH = w_shape[2]; g->KW = w_shape[3];
+        } else {   // x {N,H,W,C}, w {Cout,KH,KW,C/g}
+            g->N = x_shape[0]; g->H = x_shape[1]; g->W = x_shape[2]; g->C = x_shape[3];
+            g->Cout = w_shape[0]; g->KH = w_shape[1]; g->KW = w_shape[2]; g->Cg_w = w_shape[3];
+        }
         g->sh = stride[0]; g->sw = stride[1]; g->ph = pad[0]; g->pw = pad[1];
         g->dh = dilation[0]; g->dw = dilation[1];
         if (g->N < 0 || g->C < 1 || g->H < 1 || g->W < 1)
@@ -141,7 +146,7 @@ gconv::Conv2dArgs conv2d_args(const Geometry &g, const void *x, const void *w, c
 // the direct route, which is bound by memory traffic rather than arithmetic.
 gconv_route_t auto_route(const Geometry &g, gconv_dtype_t dtype, bool igemm_ok)
 {
-    if (g.layout == GCONV_LAYOUT_NTC) return GCONV_ROUTE_DIRECT;
+    if (g.layout != GCONV_LAYOUT_NCHW) return GCONV_ROUTE_DIRECT;
     const int64_t Kg = g.Cg_w * g.KH * g.KW;
     const int64_t Ng = g.Cout / g.groups;
     if (igemm_ok && Kg >= 64 && Ng >= 16) return GCONV_ROUTE_IGEMM;
@@ -168,7 +173,7 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
     Geometry g;
     gconv_status_t st = validate(x_shape, w_shape, stride, pad, dilation, groups, layout, &g);
     if (st != GCONV_OK) return st;
-    const bool nchw = layout == GCONV_LAYOUT_NCHW;
+    const bool nchw = layout != GCONV_LAYOUT_NTC;   // NCHW or NHWC: the 2-D geometry
     if ((nchw && g.N == 0) || (!nchw && g.B == 0)) {
         // An empty batch has no elements: x and y may be NULL and nothing is enqueued.
         if (!w) return fail(GCONV_ERR_INVALID_ARG, "NULL w pointer");
@@ -185,7 +190,11 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
         return fail(GCONV_ERR_INVALID_ARG, "y overlaps x, w or bias");
     hipError_t err;
     const char *kname = "";
-    if (nchw) {
+    if (layout == GCONV_LAYOUT_NHWC) {
+        if (route == GCONV_ROUTE_IGEMM)
+            return fail(GCONV_ERR_UNSUPPORTED, "the implicit-GEMM route does not run the NHWC layout");
+        err = gconv::launch_conv2d_nhwc(conv2d_args(g, x, w, bias, y, dtype, stream), &kname);
+    } else if (nchw) {
         const gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
         const bool igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
         if (route == GCONV_ROUTE_AUTO) route = auto_route(g, dtype, igemm_ok);
@@ -257,6 +266,8 @@ gconv_status_t gconv_out_shape(const int64_t *x_shape, const int64_t *w_shape, c
     if (st != GCONV_OK) return st;
     if (layout == GCONV_LAYOUT_NCHW) {
         y_shape[0] = g.N; y_shape[1] = g.Cout; y_shape[2] = g.OH; y_shape[3] = g.OW;
+    } else if (layout == GCONV_LAYOUT_NHWC) {
+        y_shape[0] = g.N; y_shape[1] = g.OH; y_shape[2] = g.OW; y_shape[3] = g.Cout;
     } else {
         y_shape[0] = g.B; y_shape[1] = g.To; y_shape[2] = g.C;
     }

@@ -48,7 +48,8 @@ template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return
 
 // Launchers (each returns the launch status and the kernel name it picked).
 hipError_t launch_direct2d(const Conv2dArgs &a, const char **kname);
-bool dw2d_supported(const Conv2dArgs &a);             // depthwise K x K, stride 1 or 2
+bool dw2d_supported(const Conv2dArgs &a);
+hipError_t launch_conv2d_nhwc(const Conv2dArgs &a, const char **kname);   // x, w, y channels-last             // depthwise K x K, stride 1 or 2
 hipError_t launch_dw2d(const Conv2dArgs &a, const char **kname);
 bool igemm_supported(const Conv2dArgs &a);            // fp16 / bf16
 hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);

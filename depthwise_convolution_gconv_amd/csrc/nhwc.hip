@@ -1,0 +1,236 @@
+// nhwc.hip -- grouped conv2d over channels-last (NHWC) tensors.
+//
+// The discuss.pytorch.org thread "F.conv2d runs x15 slower in mixed-precision/
+// half-precision mode" turns, in its later replies, to the NHWC (channels_last)
+// memory format for the fp16 grouped conv.  Tensors: x [N][H][W][C],
+// w [Cout][KH][KW][C/g] (the channels_last order of PyTorch's weights),
+// y [N][OH][OW][Cout]; the sum is the one of the NCHW route.
+//
+// dw2d_nhwc_tile<T, K, S, VE>: depthwise layers (C/g = 1, Cout = C), K x K filters,
+//   stride S (1 or 2), dilation 1.  Channels are the contiguous axis, so lanes map
+//   to channels (as in the (batch, steps, channels) 1-D kernel): one workgroup =
+//   64 channels x 4 output rows x TW output columns.  It stages the input patch
+//   ((4-1)*S + K rows x (TW-1)*S + K columns x 64 channels, zero outside the
+//   image) and the 64 filters in LDS as fp32, with loads of VE channels along C;
+//   each thread (one channel, one output row) slides a window of (TW-1)*S + K
+//   input columns down the K filter rows and stores TW outputs, each store of a
+//   wave covering 64 consecutive channels.
+// conv2d_nhwc_generic<T>: any groups, stride, padding and dilation; one thread per
+//   output, output channels fastest (coalesced stores, and the group's input
+//   channels are contiguous reads).
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace gconv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCT = 64;                  // channels per tile (lanes)
+constexpr int kRows = kThreads / kCT;    // output rows per tile (one per wave)
+
+template <typename T> __device__ __forceinline__ float elem(const uint32_t *v, int e);
+template <> __device__ __forceinline__ float elem<float>(const uint32_t *v, int e)
+{
+    return __builtin_bit_cast(float, v[e]);
+}
+template <> __device__ __forceinline__ float elem<_Float16>(const uint32_t *v, int e)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+}
+template <> __device__ __forceinline__ float elem<__bf16>(const uint32_t *v, int e)
+{
+    return __builtin_bit_cast(float, (v[e >> 1] >> (16 * (e & 1))) << 16);
+}
+
+template <int S> struct TileW { static constexpr int value = 8 / S; };   // output columns per thread
+
+template <typename T, int K, int S, int VE>
+__global__ void __launch_bounds__(kThreads)
+dw2d_nhwc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+               T *__restrict__ y, int H, int W, int C, int OH, int OW, int ph, int pw,
+               int tiles_w, int tiles_h, int cblocks)
+{
+    constexpr int TW = TileW<S>::value;
+    constexpr int IRH = (kRows - 1) * S + K;          // staged input rows
+    constexpr int IRW = (TW - 1) * S + K;             // staged input columns
+    constexpr int KK = K * K;
+    constexpr int DW = (VE * (int)sizeof(T) + 3) / 4;
+    constexpr int CPP = kCT / VE;                     // staging loads per pixel
+    constexpr int NCH = IRH * IRW * CPP;              // staging loads per tile
+    constexpr int NB = 8;
+    __shared__ float xs[IRH][IRW][kCT];
+    __shared__ float ws[KK][kCT];
+
+    int rest = blockIdx.x;
+    const int cb = rest % cblocks; rest /= cblocks;
+    const int tw = rest % tiles_w; rest /= tiles_w;
+    const int th = rest % tiles_h;
+    const int n = rest / tiles_h;
+    const int tid = threadIdx.x, lane = tid % kCT, rg = tid / kCT;
+    const int c0 = cb * kCT, c = c0 + lane;
+    const int oh0 = th * kRows, ow0 = tw * TW;
+    const int ih0 = oh0 * S - ph, iw0 = ow0 * S - pw;
+
+    // Filters [tap][channel] (zero past C).
+    for (int i = tid; i < KK * kCT; i += kThreads) {
+        const int t = i / kCT, cc = c0 + i % kCT;
+        ws[t][i % kCT] = cc < C ? to_f32(w[(int64_t)cc * KK + t]) : 0.0f;
+    }
+    // Input patch, NB loads in flight per thread, zero outside the image and past C.
+    const T *xn = x + (int64_t)n * H * W * C;
+    for (int base = 0; base < NCH; base += NB * kThreads) {
+        uint32_t v[NB][DW];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            const int pix = i / CPP, cv = (i - pix * CPP) * VE;
+            const int r = pix / IRW, q = pix - r * IRW;
+            const int ih = ih0 + r, iw = iw0 + q, cc = c0 + cv;
+#pragma unroll
+            for (int e = 0; e < DW; ++e) v[j][e] = 0;
+            if (i < NCH && ih >= 0 && ih < H && iw >= 0 && iw < W && cc < C) {
+                const T *src = xn + ((int64_t)ih * W + iw) * C + cc;
+                if constexpr (DW == 4) {
+                    const uint4 u = *reinterpret_cast<const uint4 *>(src);
+                    v[j][0] = u.x; v[j][1] = u.y; v[j][2] = u.z; v[j][3] = u.w;
+                } else if constexpr (sizeof(T) == 4) {
+                    v[j][0] = __builtin_bit_cast(uint32_t, *src);
+                } else {
+                    v[j][0] = __builtin_bit_cast(uint16_t, *src);
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            if (i < NCH) {
+                const int pix = i / CPP, cv = (i - pix * CPP) * VE;
+                const int r = pix / IRW, q = pix - r * IRW;
+#pragma unroll
+                for (int e = 0; e < VE; ++e) xs[r][q][cv + e] = elem<T>(v[j], e);
+            }
+        }
+    }
+    __syncthreads();
+
+    const int oh = oh0 + rg;
+    if (c >= C || oh >= OH) return;
+    const float b0 = bias ? to_f32(bias[c]) : 0.0f;
+    float acc[TW];
+#pragma unroll
+    for (int r = 0; r < TW; ++r) acc[r] = b0;
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh) {
+        float win[IRW];
+#pragma unroll
+        for (int q = 0; q < IRW; ++q) win[q] = xs[rg * S + kh][q][lane];
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw) {
+            const float wv = ws[kh * K + kw][lane];
+#pragma unroll
+            for (int r = 0; r < TW; ++r) acc[r] = fmaf(win[r * S + kw], wv, acc[r]);
+        }
+    }
+    T *yp = y + (((int64_t)n * OH + oh) * OW + ow0) * C + c;
+#pragma unroll
+    for (int r = 0; r < TW; ++r)
+        if (ow0 + r < OW) yp[(int64_t)r * C] = from_f32<T>(acc[r]);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+conv2d_nhwc_generic(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+                    T *__restrict__ y, int64_t total, int C, int H, int W, int Cout, int KH, int KW,
+                    int Cg, int Ng, int OH, int OW, int sh, int sw, int ph, int pw, int dh, int dw)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * kThreads) {
+        int64_t r = i;
+        const int o = (int)(r % Cout); r /= Cout;
+        const int ow = (int)(r % OW); r /= OW;
+        const int oh = (int)(r % OH);
+        const int64_t n = r / OH;
+        const int k = o / Ng;
+        float acc = bias ? to_f32(bias[o]) : 0.0f;
+        for (int kh = 0; kh < KH; ++kh) {
+            const int ih = oh * sh - ph + kh * dh;
+            if (ih < 0 || ih >= H) continue;
+            for (int kw = 0; kw < KW; ++kw) {
+                const int iw = ow * sw - pw + kw * dw;
+                if (iw < 0 || iw >= W) continue;
+                const T *xp = x + ((n * H + ih) * W + iw) * C + (int64_t)k * Cg;
+                const T *wp = w + (((int64_t)o * KH + kh) * KW + kw) * Cg;
+                for (int ci = 0; ci < Cg; ++ci) acc = fmaf(to_f32(xp[ci]), to_f32(wp[ci]), acc);
+            }
+        }
+        y[i] = from_f32<T>(acc);
+    }
+}
+
+template <typename T, int K, int S, int VE>
+hipError_t run_tile(const Conv2dArgs &a)
+{
+    constexpr int TW = TileW<S>::value;
+    const int tiles_w = (int)ceil_div(a.OW, TW), tiles_h = (int)ceil_div(a.OH, kRows);
+    const int cblocks = (int)ceil_div(a.C, kCT);
+    const int64_t blocks = a.N * tiles_h * tiles_w * cblocks;
+    hipLaunchKernelGGL((dw2d_nhwc_tile<T, K, S, VE>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)a.H, (int)a.W,
+                       (int)a.C, (int)a.OH, (int)a.OW, a.ph, a.pw, tiles_w, tiles_h, cblocks);
+    return hipGetLastError();
+}
+
+template <typename T, int K, int S>
+hipError_t run_tile_ve(const Conv2dArgs &a)
+{
+    constexpr int VE = 16 / sizeof(T);
+    if (a.C % VE == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0) return run_tile<T, K, S, VE>(a);
+    return run_tile<T, K, S, 1>(a);
+}
+
+template <typename T, int K>
+hipError_t run_tile_s(const Conv2dArgs &a)
+{
+    return a.sh == 2 ? run_tile_ve<T, K, 2>(a) : run_tile_ve<T, K, 1>(a);
+}
+
+template <typename T>
+hipError_t run_typed(const Conv2dArgs &a, const char **kname)
+{
+    // Depthwise tile kernel: C/g = 1 and one filter per channel, square K in {3, 5, 7},
+    // square stride 1 or 2, dilation 1, tile indices and one image's offsets in int.
+    const bool dw = a.groups == a.C && a.Cout == a.C && a.KH == a.KW &&
+                    (a.KH == 3 || a.KH == 5 || a.KH == 7) && a.sh == a.sw && (a.sh == 1 || a.sh == 2) &&
+                    a.dh == 1 && a.dw == 1 && a.H * a.W * a.C < (int64_t(1) << 31) &&
+                    a.N * ceil_div(a.OH, kRows) * ceil_div(a.OW, 8 / a.sh) * ceil_div(a.C, kCT) < (int64_t(1) << 31);
+    if (dw) {
+        *kname = "dw2d_nhwc_tile";
+        switch (a.KH) {
+        case 3: return run_tile_s<T, 3>(a);
+        case 5: return run_tile_s<T, 5>(a);
+        default: return run_tile_s<T, 7>(a);
+        }
+    }
+    *kname = "conv2d_nhwc_generic";
+    const int64_t total = a.N * a.OH * a.OW * a.Cout;
+    const int64_t blocks = std::min<int64_t>(ceil_div(total, kThreads), 1 << 20);
+    hipLaunchKernelGGL((conv2d_nhwc_generic<T>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total, (int)a.C, (int)a.H,
+                       (int)a.W, (int)a.Cout, (int)a.KH, (int)a.KW, (int)(a.C / a.groups),
+                       (int)(a.Cout / a.groups), (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv2d_nhwc(const Conv2dArgs &a, const char **kname)
+{
+    switch (a.dtype) {
+    case DT_F32: return run_typed<float>(a, kname);
+    case DT_F16: return run_typed<_Float16>(a, kname);
+    default: return run_typed<__bf16>(a, kname);
+    }
+}
+
+}  // namespace gconv

@@ -38,7 +38,7 @@ DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 class Workload:
     name: str
     index: int                    # seed offset
-    layout: str                   # "nchw" or "ntc"
+    layout: str                   # "nchw", "nhwc" or "ntc"
     x_shape: Tuple[int, ...]
     w_shape: Tuple[int, ...]
     groups: int
@@ -99,6 +99,14 @@ NEXT_WORKLOADS = {
     "n3_dw2d_s1_f32": Workload(
         "n3_dw2d_s1_f32", 13, "nchw", (8, 256, 512, 40), (256, 1, 3, 3), 256, 1, 1, 1, "f32",
         1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d, stride 1"),
+    # The same stage in the channels-last (NHWC) layout: x [8, 512, 40, 256],
+    # w [256, 3, 3, 1].
+    "n7_dw2d_nhwc_s2_f32": Workload(
+        "n7_dw2d_nhwc_s2_f32", 17, "nhwc", (8, 512, 40, 256), (256, 3, 3, 1), 256, 2, 1, 1, "f32",
+        1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d over channels-last tensors, stride 2"),
+    "n8_dw2d_nhwc_s1_bf16": Workload(
+        "n8_dw2d_nhwc_s1_bf16", 18, "nhwc", (8, 512, 40, 256), (256, 3, 3, 1), 256, 1, 1, 1, "bf16",
+        1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d over channels-last tensors, stride 1, bf16"),
     "n4_dw1d_s2_f32": Workload(
         "n4_dw1d_s2_f32", 14, "ntc", (8, 1024, 512), (512, 1, 31), 512, 2, 15, 1, "f32",
         1.0, 1 / 31, 0.01, "depthwise conv1d, (batch, steps, channels), stride 2"),

@@ -35,6 +35,11 @@
  *            stride/pad/dilation = {h, w} (2 ints each), y = {N,Cout,OH,OW}.
  *      NTC : x_shape = {B,T,C}, w_shape = {C,1,K}, groups must equal C,
  *            stride/pad/dilation = 1 int each, y = {B,To,C}.
+ *      NHWC: the NCHW convolution over channels-last tensors (the NHWC memory
+ *            format the discuss.pytorch.org thread turns to for the fp16 grouped
+ *            conv): x_shape = {N,H,W,C}, w_shape = {Cout, KH, KW, C/groups}
+ *            (channels_last weight order), stride/pad/dilation = {h, w},
+ *            y = {N,OH,OW,Cout}.  Direct route only.
  *    Output length per axis: floor((L + 2p - d*(K-1) - 1)/s) + 1.
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
@@ -68,7 +73,8 @@ typedef enum {
 
 typedef enum {
     GCONV_LAYOUT_NCHW = 0,      /* conv2d, x [N,C,H,W]                                      */
-    GCONV_LAYOUT_NTC = 1        /* depthwise conv1d, x [B,T,C] = (batch, steps, channels)   */
+    GCONV_LAYOUT_NTC = 1,       /* depthwise conv1d, x [B,T,C] = (batch, steps, channels)   */
+    GCONV_LAYOUT_NHWC = 2       /* conv2d over channels-last tensors, x [N,H,W,C]          */
 } gconv_layout_t;
 
 typedef enum { GCONV_F32 = 0, GCONV_F16 = 1, GCONV_BF16 = 2 } gconv_dtype_t;
@@ -83,9 +89,11 @@ typedef enum {
                                    (batch, steps, channels) sliding-window kernel (NTC)     */
     GCONV_ROUTE_IGEMM = 2       /* implicit GEMM per group on the matrix cores: im2col
                                    tiles built in LDS, never materialised (NCHW only)      */
+    /* NHWC runs on the direct route: a channels-on-lanes tile kernel for depthwise
+       layers, a coalesced one-thread-per-output kernel otherwise. */
 } gconv_route_t;
 
-/* Output shape of a convolution.  y_shape receives 4 (NCHW) or 3 (NTC) values.
+/* Output shape of a convolution.  y_shape receives 4 (NCHW, NHWC) or 3 (NTC) values.
  * Returns GCONV_OK, GCONV_ERR_INVALID_ARG or GCONV_ERR_SHAPE; no device work. */
 gconv_status_t gconv_out_shape(const int64_t *x_shape, const int64_t *w_shape,
                                const int32_t *stride, const int32_t *pad,

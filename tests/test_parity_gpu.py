@@ -182,6 +182,46 @@ def test_dw2d_sweep_vs_oracle(ci, dt):
     assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
 
 
+# Channels-last (NHWC) conv2d: the depthwise tile kernel where it applies, the
+# generic kernel for every other geometry.
+NHWC_SWEEP = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
+    (2, 64, 64, 9, 8, 3, 3, 64, 1, 1, 1, True),        # depthwise, one channel block
+    (1, 100, 100, 13, 11, 3, 3, 100, 2, 1, 1, True),   # depthwise, ragged channel block, stride 2
+    (2, 72, 72, 10, 9, 5, 5, 72, 1, 2, 1, False),      # 5x5
+    (1, 128, 128, 15, 17, 7, 7, 128, 2, 3, 1, True),   # 7x7, stride 2, two channel blocks
+    (3, 12, 12, 6, 7, 3, 3, 12, 1, 0, 1, True),        # C not a multiple of 16 bytes (scalar loads)
+    (1, 16, 16, 2, 2, 3, 3, 16, 1, 1, 1, True),        # image smaller than the filter
+    (2, 32, 64, 8, 8, 3, 3, 32, 1, 1, 1, True),        # two filters per channel (generic)
+    (2, 32, 48, 9, 7, 3, 3, 4, 1, 1, 1, True),         # grouped (generic)
+    (1, 24, 24, 11, 10, 3, 2, 3, (2, 1), (1, 0), (1, 2), True),   # anisotropic (generic)
+    (2, 16, 16, 7, 7, 3, 3, 16, 1, 2, 2, True),        # depthwise with dilation 2 (generic)
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(NHWC_SWEEP)))
+def test_nhwc_sweep_vs_oracle(ci, dt):
+    N, C, Co, H, W, KH, KW, g, s, p, d, has_b = NHWC_SWEEP[ci]
+    seed = 80 * ci + {"f32": 0, "f16": 1, "bf16": 2}[dt]
+    x = draw((N, H, W, C), 1.0, 7900 + seed, dt)
+    w = draw((Co, KH, KW, C // g), 1.0 / (C // g * KH * KW), 8900 + seed, dt)
+    b = draw((Co,), 0.01, 9900 + seed, dt) if has_b else None
+    r = oracle.conv2d_nhwc(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=p, dilation=d, groups=g)
+    y = gc.conv2d_nhwc(gpu(x), gpu(w), gpu(b), stride=s, padding=p, dilation=d, groups=g)
+    torch.cuda.synchronize()
+    dw = g == C and Co == C and KH == KW and KH in (3, 5, 7) and s in (1, 2) and d == 1
+    assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else "conv2d_nhwc_generic")
+    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+
+
+def test_nhwc_rejects_the_implicit_gemm_route():
+    x = torch.randn(1, 8, 8, 32, device="cuda", dtype=torch.float16)
+    w = torch.randn(32, 3, 3, 16, device="cuda", dtype=torch.float16)
+    with pytest.raises(gc.GconvError) as e:
+        gc.gconv_fwd_route(x, w, None, 1, 1, 1, 2, "nhwc", route="igemm")
+    assert e.value.status == 3
+
+
 def test_dw2d_unaligned_output_and_input():
     # y and x that start 4 bytes past a 16-byte boundary: single-element runs and loads.
     N, C, H, W, K = 2, 6, 24, 24, 3
@@ -337,6 +377,9 @@ def test_next_workload_full_size(name):
     if wl.layout == "ntc":
         r = oracle.dwconv1d_btc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation)
         assert gc.gconv_last_kernel() == "dw1d_btc_tile"
+    elif wl.layout == "nhwc":
+        r = oracle.conv2d_nhwc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
+        assert gc.gconv_last_kernel() == "dw2d_nhwc_tile"
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         assert gc.gconv_last_kernel() == "dw2d_rows"
