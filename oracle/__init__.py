@@ -76,6 +76,8 @@ def _load():
         lib.gconv_oracle_dwconv1d_btc.argtypes = dw_args + [_dp]
         lib.gconv_oracle_dwconv1d_btc_at.restype = ctypes.c_int
         lib.gconv_oracle_dwconv1d_btc_at.argtypes = dw_args + [_ip, _i64, _dp]
+        lib.gconv_oracle_conv2d_interleaved.restype = ctypes.c_int
+        lib.gconv_oracle_conv2d_interleaved.argtypes = conv_args + [_dp]
         lib.gconv_oracle_conv2d_nhwc.restype = ctypes.c_int
         lib.gconv_oracle_conv2d_nhwc.argtypes = conv_args + [_dp]
         lib.gconv_oracle_conv2d_nhwc_at.restype = ctypes.c_int
@@ -120,8 +122,11 @@ def _rc(rc: int):
         raise ValueError("oracle: output would be empty")
 
 
-def conv2d(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1) -> np.ndarray:
-    """Grouped conv2d forward in fp64.  x [N,C,H,W], w [Cout,C/groups,KH,KW]."""
+def conv2d(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1,
+           out_order: str = "grouped") -> np.ndarray:
+    """Grouped conv2d forward in fp64.  x [N,C,H,W], w [Cout,C/groups,KH,KW].
+    out_order "interleaved": filter j of group k goes to output channel j*groups + k
+    (the neon issue's 1234... order) instead of k*Cout/groups + j."""
     lib = _load()
     x, xp = _f64(x)
     w, wp = _f64(w)
@@ -137,8 +142,11 @@ def conv2d(x, w, bias=None, stride=1, padding=0, dilation=1, groups=1) -> np.nda
     OH = out_len(H, KH, sh, ph, dh)
     OW = out_len(W, KW, sw, pw, dw)
     y = np.zeros((N, Cout, max(OH, 0), max(OW, 0)), dtype=np.float64)
-    _rc(lib.gconv_oracle_conv2d(xp, N, C, H, W, wp, Cout, Cg_w, KH, KW, bp, groups,
-                                sh, sw, ph, pw, dh, dw, y.ctypes.data_as(_dp)))
+    if out_order not in ("grouped", "interleaved"):
+        raise ValueError("oracle: out_order must be 'grouped' or 'interleaved'")
+    fn = lib.gconv_oracle_conv2d if out_order == "grouped" else lib.gconv_oracle_conv2d_interleaved
+    _rc(fn(xp, N, C, H, W, wp, Cout, Cg_w, KH, KW, bp, groups, sh, sw, ph, pw, dh, dw,
+           y.ctypes.data_as(_dp)))
     return y
 
 

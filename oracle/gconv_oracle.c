@@ -166,6 +166,34 @@ int gconv_oracle_conv2d_at(const double *x, int64_t N, int64_t C, int64_t H, int
     return 0;
 }
 
+/*
+ * The interleaved output order of the neon issue "Grouped convolutions" (ibmua's
+ * reply on output ordering: 1234123412341234 instead of the usual 111122223333):
+ * filter j of group k (filter index o = k*Ng + j, the same weights and sum as
+ * above) is stored at output channel j*groups + k.  y: [N][Cout][OH][OW].
+ */
+int gconv_oracle_conv2d_interleaved(const double *x, int64_t N, int64_t C, int64_t H, int64_t W,
+                                    const double *w, int64_t Cout, int64_t Cg_w, int64_t KH, int64_t KW,
+                                    const double *bias, int64_t groups,
+                                    int64_t sh, int64_t sw, int64_t ph, int64_t pw, int64_t dh, int64_t dw,
+                                    double *y)
+{
+    conv2d_geom g;
+    int rc = conv2d_geom_make(&g, N, C, H, W, Cout, Cg_w, KH, KW, groups, sh, sw, ph, pw, dh, dw);
+    if (rc) return rc;
+    const int64_t Ng = Cout / groups;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t p = 0; p < N * Cout; ++p) {
+        const int64_t n = p / Cout, o = p % Cout;       /* o: filter index */
+        const int64_t k = o / Ng, j = o % Ng;
+        const int64_t oc = j * groups + k;              /* its output channel */
+        for (int64_t oh = 0; oh < g.OH; ++oh)
+            for (int64_t ow = 0; ow < g.OW; ++ow)
+                y[((n * Cout + oc) * g.OH + oh) * g.OW + ow] = conv2d_one(&g, x, w, bias, n, o, oh, ow);
+    }
+    return 0;
+}
+
 /* ---- depthwise 1-D convolution over (batch, steps, channels) ---------------- */
 
 static double dw1d_one(const double *x, int64_t T, int64_t C, const double *w, int64_t K,

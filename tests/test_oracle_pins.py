@@ -336,3 +336,26 @@ def test_invalid_arguments_raise():
     with pytest.raises(ValueError):
         oracle.conv2d(x, np.zeros((6, 2, 7, 7)), groups=3)      # empty output
     assert oracle.conv2d(np.zeros((0, 6, 5, 5)), np.zeros((6, 2, 3, 3)), groups=3).shape == (0, 6, 3, 3)
+
+
+# ---------------------------------------------------------------- interleaved output order
+
+@pytest.mark.parametrize("N,C,Co,H,W,K,g", [(2, 8, 12, 6, 7, 3, 4), (1, 6, 6, 5, 5, 3, 3), (2, 4, 8, 4, 4, 1, 2)])
+def test_interleaved_order_is_the_channel_permutation(N, C, Co, H, W, K, g):
+    """Output channel j*g + k holds filter j of group k: the grouped result with its
+    channel axis viewed as [g, Cout/g] and transposed to [Cout/g, g]."""
+    rng = np.random.default_rng(N * 100 + C)
+    x, w, b = rnd(rng, N, C, H, W), rnd(rng, Co, C // g, K, K), rnd(rng, Co)
+    yg = oracle.conv2d(x, w, b, 1, K // 2, 1, g)
+    yi = oracle.conv2d(x, w, b, 1, K // 2, 1, g, out_order="interleaved")
+    OH, OW = yg.shape[2:]
+    perm = yg.reshape(N, g, Co // g, OH, OW).transpose(0, 2, 1, 3, 4).reshape(N, Co, OH, OW)
+    np.testing.assert_array_equal(yi, perm)
+
+
+def test_interleaved_order_is_the_identity_for_one_group_or_one_filter_per_group():
+    rng = np.random.default_rng(5)
+    x = rnd(rng, 2, 6, 5, 5)
+    for w, g in ((rnd(rng, 4, 6, 3, 3), 1), (rnd(rng, 6, 1, 3, 3), 6), (rnd(rng, 3, 2, 3, 3), 3)):
+        np.testing.assert_array_equal(oracle.conv2d(x, w, None, 1, 1, 1, g, out_order="interleaved"),
+                                      oracle.conv2d(x, w, None, 1, 1, 1, g))
