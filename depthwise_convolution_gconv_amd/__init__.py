@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     gconv_dw1d_bwd_filter,
     gconv_dw1d_bwd_filter_workspace,
     gconv_fwd,
+    gconv_fwd_ex,
     gconv_fwd_route,
     gconv_last_error,
     gconv_last_kernel,

@@ -22,9 +22,10 @@ DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 DTYPE_NAMES = {"f32": 0, "f16": 1, "bf16": 2}
 ROUTES = {"auto": 0, "direct": 1, "igemm": 2}
 ROUTE_NAMES = {v: k for k, v in ROUTES.items()}
+ORDERS = {"grouped": 0, "interleaved": 1}
 
 # Every symbol include/gconv.h declares.
-EXPORTS = ("gconv_out_shape", "gconv_select_route", "gconv_fwd", "gconv_fwd_route",
+EXPORTS = ("gconv_out_shape", "gconv_select_route", "gconv_fwd", "gconv_fwd_route", "gconv_fwd_ex",
            "gconv_dw1d_bwd_data", "gconv_dw1d_bwd_filter_workspace", "gconv_dw1d_bwd_filter",
            "gconv_last_kernel", "gconv_status_string", "gconv_last_error")
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.gconv_fwd.restype = _i32
         L.gconv_fwd_route.argtypes = conv + [_i32, _vp]
         L.gconv_fwd_route.restype = _i32
+        L.gconv_fwd_ex.argtypes = conv + [_i32, _i32, _vp]
+        L.gconv_fwd_ex.restype = _i32
         L.gconv_out_shape.argtypes = [_i64p, _i64p, _i32p, _i32p, _i32p, _i32, _i32, _i64p]
         L.gconv_out_shape.restype = _i32
         L.gconv_select_route.argtypes = [_i64p, _i64p, _i32p, _i32p, _i32p, _i32, _i32, _i32, _i32p]
@@ -147,7 +150,7 @@ def gconv_select_route(x_shape, w_shape, stride=1, pad=0, dilation=1, groups: in
 
 def _call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], y: Optional[torch.Tensor],
           stride, pad, dilation, groups: int, layout: str, route: Optional[str],
-          stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+          stream: Optional[torch.cuda.Stream], out_order: Optional[str] = None) -> torch.Tensor:
     L = lib()
     for name, t in (("x", x), ("w", w), ("bias", bias), ("y", y)):
         if t is None:
@@ -178,7 +181,11 @@ def _call(x: torch.Tensor, w: torch.Tensor, bias: Optional[torch.Tensor], y: Opt
         args = [_vp(x.data_ptr()), _arr(_i64, x.shape), _vp(w.data_ptr()), _arr(_i64, w.shape),
                 _vp(bias.data_ptr() if bias is not None else 0), _vp(y.data_ptr()), s, p, d, int(groups),
                 _layout(layout), DTYPES[x.dtype]]
-        if route is None:
+        if out_order is not None:
+            if out_order not in ORDERS or (route or "auto") not in ROUTES:
+                raise GconvError(ERR_INVALID_ARG, f"unknown output order {out_order!r} or route {route!r}")
+            _check(L.gconv_fwd_ex(*args, ROUTES[route or "auto"], ORDERS[out_order], _vp(st.cuda_stream)))
+        elif route is None:
             _check(L.gconv_fwd(*args, _vp(st.cuda_stream)))
         else:
             if route not in ROUTES:
@@ -197,6 +204,13 @@ def gconv_fwd_route(x, w, bias=None, stride=1, pad=0, dilation=1, groups: int = 
                     route: str = "auto", y=None, stream=None) -> torch.Tensor:
     """gconv_fwd with the route ("auto", "direct", "igemm") forced."""
     return _call(x, w, bias, y, stride, pad, dilation, groups, layout, route, stream)
+
+
+def gconv_fwd_ex(x, w, bias=None, stride=1, pad=0, dilation=1, groups: int = 1, layout: str = "nchw",
+                 route: str = "auto", out_order: str = "grouped", y=None, stream=None) -> torch.Tensor:
+    """gconv_fwd with the route and the output-channel order ("grouped": filter j of
+    group k at channel k*Cout/g + j; "interleaved": at channel j*g + k) chosen."""
+    return _call(x, w, bias, y, stride, pad, dilation, groups, layout, route, stream, out_order)
 
 
 def gconv_last_kernel() -> str:

@@ -136,6 +136,7 @@ gconv::Conv2dArgs conv2d_args(const Geometry &g, const void *x, const void *w, c
     a.groups = g.groups; a.OH = g.OH; a.OW = g.OW;
     a.sh = g.sh; a.sw = g.sw; a.ph = g.ph; a.pw = g.pw; a.dh = g.dh; a.dw = g.dw;
     a.dtype = (int)dtype;
+    a.interleaved = 0;
     a.stream = (hipStream_t)stream;
     return a;
 }
@@ -163,9 +164,11 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const int64_t *w_shape,
                    const void *bias, void *y, const int32_t *stride, const int32_t *pad,
                    const int32_t *dilation, int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
-                   gconv_route_t route, void *stream)
+                   gconv_route_t route, gconv_out_order_t order, void *stream)
 {
     g_last_error[0] = '\0';
+    if (order != GCONV_ORDER_GROUPED && order != GCONV_ORDER_INTERLEAVED)
+        return fail(GCONV_ERR_INVALID_ARG, "unknown output order %lld", (long long)order);
     if (dtype != GCONV_F32 && dtype != GCONV_F16 && dtype != GCONV_BF16)
         return fail(GCONV_ERR_INVALID_ARG, "unknown dtype %lld", (long long)dtype);
     if (route != GCONV_ROUTE_AUTO && route != GCONV_ROUTE_DIRECT && route != GCONV_ROUTE_IGEMM)
@@ -193,9 +196,12 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
     if (layout == GCONV_LAYOUT_NHWC) {
         if (route == GCONV_ROUTE_IGEMM)
             return fail(GCONV_ERR_UNSUPPORTED, "the implicit-GEMM route does not run the NHWC layout");
-        err = gconv::launch_conv2d_nhwc(conv2d_args(g, x, w, bias, y, dtype, stream), &kname);
+        gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
+        a.interleaved = order == GCONV_ORDER_INTERLEAVED;
+        err = gconv::launch_conv2d_nhwc(a, &kname);
     } else if (nchw) {
-        const gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
+        gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
+        a.interleaved = order == GCONV_ORDER_INTERLEAVED;
         const bool igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
         if (route == GCONV_ROUTE_AUTO) route = auto_route(g, dtype, igemm_ok);
         if (route == GCONV_ROUTE_IGEMM) {
@@ -302,7 +308,7 @@ gconv_status_t gconv_fwd(const void *x, const int64_t *x_shape, const void *w, c
                          void *hip_stream)
 {
     return run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype,
-               GCONV_ROUTE_AUTO, hip_stream);
+               GCONV_ROUTE_AUTO, GCONV_ORDER_GROUPED, hip_stream);
 }
 
 gconv_status_t gconv_fwd_route(const void *x, const int64_t *x_shape, const void *w, const int64_t *w_shape,
@@ -311,6 +317,16 @@ gconv_status_t gconv_fwd_route(const void *x, const int64_t *x_shape, const void
                                gconv_dtype_t dtype, gconv_route_t route, void *hip_stream)
 {
     return run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype, route,
+               GCONV_ORDER_GROUPED, hip_stream);
+}
+
+gconv_status_t gconv_fwd_ex(const void *x, const int64_t *x_shape, const void *w, const int64_t *w_shape,
+                            const void *bias, void *y, const int32_t *stride, const int32_t *pad,
+                            const int32_t *dilation, int32_t groups, gconv_layout_t layout,
+                            gconv_dtype_t dtype, gconv_route_t route, gconv_out_order_t order,
+                            void *hip_stream)
+{
+    return run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype, route, order,
                hip_stream);
 }
 

@@ -18,6 +18,7 @@ struct Conv2dArgs {
     int64_t OH, OW;
     int32_t sh, sw, ph, pw, dh, dw;
     int dtype;  // gconv_dtype_t
+    int interleaved;  // 1: filter j of group k is stored at output channel j*groups + k
     hipStream_t stream;
 };
 

@@ -36,15 +36,18 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 direct2d_naive(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                T *__restrict__ y, int64_t total, int C, int H, int W, int Cout, int KH, int KW,
-               int Cg, int Ng, int OH, int OW, int sh, int sw, int ph, int pw, int dh, int dw)
+               int Cg, int Ng, int OH, int OW, int sh, int sw, int ph, int pw, int dh, int dw,
+               int interleaved)
 {
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * kThreads) {
         int64_t r = i;
         const int ow = (int)(r % OW); r /= OW;
         const int oh = (int)(r % OH); r /= OH;
-        const int o = (int)(r % Cout);
+        const int oc = (int)(r % Cout);   // output channel; o is its filter
         const int64_t n = r / Cout;
+        const int G = Cout / Ng;
+        const int o = interleaved ? (oc % G) * Ng + oc / G : oc;
         const int k = o / Ng;
         float acc = bias ? to_f32(bias[o]) : 0.0f;
         const T *xg = x + (n * C + (int64_t)k * Cg) * H * W;
@@ -72,6 +75,7 @@ struct TiledGeom {
     int IHt, IWt;        // input halo tile
     int CC;              // input channels staged per chunk
     int tiles_w, tiles_h, ochunks, groups;
+    int ocs, okg;        // output channel of filter j of group k: j*ocs + k*okg
 };
 
 // NB: output channels per workgroup (accumulators per thread).
@@ -143,10 +147,10 @@ direct2d_tiled(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         __syncthreads();
     }
     if (oh < g.OH && ow < g.OW) {
-        T *yp = y + (((int64_t)n * g.Cout + o0) * g.OH + oh) * g.OW + ow;
+        T *yp = y + (((int64_t)n * g.Cout + oc_i * NB * g.ocs + k * g.okg) * g.OH + oh) * g.OW + ow;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-            if (j < nb) yp[(int64_t)j * g.OH * g.OW] = from_f32<T>(acc[j]);
+            if (j < nb) yp[(int64_t)j * g.ocs * g.OH * g.OW] = from_f32<T>(acc[j]);
     }
 }
 
@@ -199,7 +203,7 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
             T *__restrict__ y, int G, int H, int W, int OH, int OW, int ph, int pw, int slabs,
-            uint32_t mw, uint32_t mow)
+            uint32_t mw, uint32_t mow, int ocs, int okg)
 {
     extern __shared__ uint2 g4s[];
     const int HP = H + 2 * ph, WP = W + 2 * pw;
@@ -277,7 +281,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
     for (int t = 0; t < 9; ++t) fa[t] = fs[t * 4 + (lane & 3)];
 
-    T *yg = y + ((int64_t)n * C + 4 * k) * OH * OW;
+    T *yg = y + ((int64_t)n * C + k * okg) * OH * OW;   // filter o of the group: channel o*ocs + k*okg
     for (int p0 = 0; p0 < OH * OW; p0 += 64) {
         const int p = min(p0 + lane, OH * OW - 1);
         const int oh = g4_div(p, mow), ow = p - oh * OW;
@@ -289,7 +293,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
             for (int kw = 0; kw < 3; ++kw) acc = Mfma4<T>::run(fa[kh * 3 + kw], xp[kh * WP + kw], acc);
         if (p0 + lane < OH * OW) {
 #pragma unroll
-            for (int o = 0; o < 4; ++o) yg[(int64_t)o * OH * OW + p] = from_f32<T>(acc[o]);
+            for (int o = 0; o < 4; ++o) yg[(int64_t)o * ocs * OH * OW + p] = from_f32<T>(acc[o]);
         }
     }
 }
@@ -320,7 +324,8 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
         hipLaunchKernelGGL((direct2d_g4<T>), dim3((unsigned)ceil_div(slabs, kG4Waves)), dim3(kThreads), lds,
                            a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
                            (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, slabs,
-                           (uint32_t)(((1u << 20) + a.W - 1) / a.W), (uint32_t)(((1u << 20) + a.OW - 1) / a.OW));
+                           (uint32_t)(((1u << 20) + a.W - 1) / a.W), (uint32_t)(((1u << 20) + a.OW - 1) / a.OW),
+                           a.interleaved ? (int)a.groups : 1, a.interleaved ? 1 : 4);
         return hipGetLastError();
     }
 tiled:
@@ -347,7 +352,7 @@ tiled:
         hipLaunchKernelGGL((direct2d_naive<T>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                            (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total,
                            (int)a.C, (int)a.H, (int)a.W, (int)a.Cout, (int)a.KH, (int)a.KW, Cg, Ng,
-                           (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw);
+                           (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw, a.interleaved);
         return hipGetLastError();
     }
     g.CC = (int)std::min<int64_t>(cc, Cg);
@@ -355,6 +360,8 @@ tiled:
     g.tiles_h = (int)ceil_div(a.OH, g.TH);
     g.ochunks = (int)ceil_div(Ng, NB);
     g.groups = (int)a.groups;
+    g.ocs = a.interleaved ? (int)a.groups : 1;
+    g.okg = a.interleaved ? 1 : Ng;
     const size_t lds = (size_t)g.CC * per_chunk * sizeof(float);
     const int64_t blocks = a.N * a.groups * g.ochunks * g.tiles_h * g.tiles_w;
     *kname = "direct2d_tiled";

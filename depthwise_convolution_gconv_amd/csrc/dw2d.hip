@@ -246,6 +246,7 @@ Plan make_plan(const Conv2dArgs &a)
     if (a.groups != a.C || a.KH != a.KW || (a.KH != 3 && a.KH != 5 && a.KH != 7)) return pl;
     if (a.sh != a.sw || (a.sh != 1 && a.sh != 2) || a.dh != 1 || a.dw != 1) return pl;
     if (a.ph > a.KH || a.pw > a.KW) return pl;
+    if (a.interleaved && a.Cout != a.C) return pl;   // the order differs only with several filters per channel
     const int K = (int)a.KH, S = a.sh;
     Dw2dGeom &g = pl.g;
     // Run length: 16 or 8 bytes of y when the output rows split into such runs and y

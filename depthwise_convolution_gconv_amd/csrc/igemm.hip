@@ -123,6 +123,8 @@ struct IgemmGeom {
     int tiles, tiles_per_xcd;   // m_tiles*n_tiles*groups; ceil(tiles/8)
     int y_vec;           // 1: 8 consecutive positions of a channel are one aligned 16-byte run of y
     int defer;           // 1: outputs staged in their own LDS area, stored during the next tile
+    int ocs, okg;        // output channel of filter j of group k: j*ocs + k*okg (grouped: 1, Ng;
+                         // interleaved: groups, 1)
     uint32_t w_bytes, b_bytes;
     FastDiv fd_ohw, fd_ow, fd_hp, fd_nseg, fd_nr, fd_mt, fd_nt;
 };
@@ -463,7 +465,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     auto put_deferred = [&](int u, uint4 v) {
         const int row = drow0 + 4 * (dnext + u);
         if (dnext + u < kDefItems && row < dlimit)
-            *reinterpret_cast<uint4 *>(y + dy + (int64_t)row * OHW) = v;
+            *reinterpret_cast<uint4 *>(y + dy + (int64_t)row * g.ocs * OHW) = v;
     };
 
     for (int i = tid; i < XU; i += kIgThreads) {
@@ -636,7 +638,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             dlimit = p < g.P ? min(BN, g.Ng - ts.nt * BN) : 0;
             const int n = fdiv(min(p, g.P - 1), g.fd_ohw);
             const int q = fmod_q(min(p, g.P - 1), n, g.fd_ohw);
-            dy = ((int64_t)n * g.Cout + ts.k * g.Ng + ts.nt * BN) * OHW + q;
+            dy = ((int64_t)n * g.Cout + ts.k * g.okg + ts.nt * BN * g.ocs) * OHW + q;
             stage ^= 1;
             tile = next_tile;
             ts = nts;
@@ -655,11 +657,12 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             const int nrow = p < g.P ? min(BN, g.Ng - ts.nt * BN) : 0;
             const int n = fdiv(min(p, g.P - 1), g.fd_ohw);
             const int q = fmod_q(min(p, g.P - 1), n, g.fd_ohw);
-            T *yp = y + ((int64_t)n * g.Cout + ts.k * g.Ng + ts.nt * BN) * OHW + q;
+            T *yp = y + ((int64_t)n * g.Cout + ts.k * g.okg + ts.nt * BN * g.ocs) * OHW + q;
+            const int64_t ystep = (int64_t)g.ocs * OHW;   // between consecutive filters
             const T *cp = ct + (tid % (kBM / 8)) * 8;
 #pragma unroll 4
             for (int row = tid / (kBM / 8); row < nrow; row += kRowStep)
-                *reinterpret_cast<uint4 *>(yp + (int64_t)row * OHW) =
+                *reinterpret_cast<uint4 *>(yp + row * ystep) =
                     *reinterpret_cast<const uint4 *>(cp + row * kCStride);
         } else {
             for (int c = tid; c < BN * (kBM / 8); c += kIgThreads) {
@@ -667,7 +670,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
                 const int on = ts.nt * BN + row;
                 const int p = ts.p0 + p8 * 8;
                 if (on >= g.Ng || p >= g.P) continue;
-                const int co = ts.k * g.Ng + on;
+                const int co = on * g.ocs + ts.k * g.okg;
                 const T *srcp = ct + row * kCStride + p8 * 8;
                 for (int e = 0; e < 8 && p + e < g.P; ++e) {
                     const int n = fdiv(p + e, g.fd_ohw);
@@ -759,6 +762,8 @@ Plan make_plan(const Conv2dArgs &a)
     const size_t stage_bytes = (size_t)((int64_t)halo_units(g.xslots) + KT * (2 * (BN + 4) + 1)) * sizeof(uint4);
     pl.lds = 2 * stage_bytes + sizeof(uint4);
     if (pl.lds > (size_t)kLdsBudget) return pl;
+    g.ocs = a.interleaved ? g.groups : 1;
+    g.okg = a.interleaved ? 1 : g.Ng;
     g.y_vec = ((int64_t)g.OH * g.OW) % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
     const size_t ct_bytes = (size_t)BN * kCStride * 2;      // staged outputs of one tile
     g.defer = pl.WN == 2 && g.y_vec && pl.lds + ct_bytes <= (size_t)kLdsBudget;

@@ -51,6 +51,8 @@ struct GeomF32 {
     int m_tiles, n_tiles, groups, nchunks;
     int tiles, tiles_per_xcd;
     int y_vec;           // 1: 4 consecutive positions of a channel are one aligned 16-byte run of y
+    int ocs, okg;        // output channel of filter j of group k: j*ocs + k*okg (grouped: 1, Ng;
+                         // interleaved: groups, 1)
     uint32_t w_bytes, b_bytes;
     FastDiv fd_ohw, fd_ow, fd_hp, fd_nseg, fd_mt, fd_nt;
 };
@@ -422,7 +424,7 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
                 const int on = ts.nt * BN + pass * kERows + row;
                 const int p = ts.p0 + p4 * 4;
                 if (on >= g.Ng || p >= g.P) continue;
-                const int co = ts.k * g.Ng + on;
+                const int co = on * g.ocs + ts.k * g.okg;
                 const float *srcp = ct + row * kCStride + p4 * 4;
                 if (g.y_vec) {
                     const int n = fdiv(p, g.fd_ohw);
@@ -512,6 +514,8 @@ PlanF32 make_plan_f32(const Conv2dArgs &a)
     pl.lds = std::max(2 * stage_bytes + sizeof(uint4), (size_t)kERows * kCStride * sizeof(float));
     if (pl.lds > (size_t)kLdsBudget) return pl;
     g.y_vec = ((int64_t)g.OH * g.OW) % 4 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
+    g.ocs = a.interleaved ? (int)a.groups : 1;
+    g.okg = a.interleaved ? 1 : g.Ng;
     g.m_tiles = (int)ceil_div(g.P, kBM);
     g.n_tiles = (int)ceil_div(g.Ng, BN);
     g.nchunks = (int)ceil_div(g.Cg, kCK);

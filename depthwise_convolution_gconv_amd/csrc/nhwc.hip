@@ -142,15 +142,18 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 conv2d_nhwc_generic(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                     T *__restrict__ y, int64_t total, int C, int H, int W, int Cout, int KH, int KW,
-                    int Cg, int Ng, int OH, int OW, int sh, int sw, int ph, int pw, int dh, int dw)
+                    int Cg, int Ng, int OH, int OW, int sh, int sw, int ph, int pw, int dh, int dw,
+                    int interleaved)
 {
     for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * kThreads) {
         int64_t r = i;
-        const int o = (int)(r % Cout); r /= Cout;
+        const int oc = (int)(r % Cout); r /= Cout;   // output channel; o is its filter
         const int ow = (int)(r % OW); r /= OW;
         const int oh = (int)(r % OH);
         const int64_t n = r / OH;
+        const int G = Cout / Ng;
+        const int o = interleaved ? (oc % G) * Ng + oc / G : oc;
         const int k = o / Ng;
         float acc = bias ? to_f32(bias[o]) : 0.0f;
         for (int kh = 0; kh < KH; ++kh) {
@@ -218,7 +221,8 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
     hipLaunchKernelGGL((conv2d_nhwc_generic<T>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                        (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total, (int)a.C, (int)a.H,
                        (int)a.W, (int)a.Cout, (int)a.KH, (int)a.KW, (int)(a.C / a.groups),
-                       (int)(a.Cout / a.groups), (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw);
+                       (int)(a.Cout / a.groups), (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw, a.dh, a.dw,
+                       a.interleaved);
     return hipGetLastError();
 }
 

@@ -173,7 +173,29 @@ gconv_status_t gconv_dw1d_bwd_filter(const void *x, const int64_t *x_shape, cons
                                      const int32_t *dilation, gconv_dtype_t dtype,
                                      void *workspace, size_t workspace_bytes, void *hip_stream);
 
-/* Name of the kernel the last successful gconv_fwd / gconv_fwd_route /
+/* Order of the output channels.  The neon issue "Grouped convolutions" (ibmua's
+ * reply on output ordering) names two: the usual group-contiguous order
+ * 111122223333 (filter j of group k at channel k*Cout/g + j) and the interleaved
+ * order 123412341234 (filter j of group k at channel j*g + k).  Only the output
+ * channel index changes; w and bias stay indexed by filter o = k*Cout/g + j. */
+typedef enum {
+    GCONV_ORDER_GROUPED = 0,
+    GCONV_ORDER_INTERLEAVED = 1
+} gconv_out_order_t;
+
+/* gconv_fwd with the route and the output-channel order chosen by the caller
+ * (GCONV_ROUTE_AUTO and GCONV_ORDER_GROUPED give gconv_fwd).  The orders coincide
+ * when there is one group or one filter per group (NTC always).  Same arguments,
+ * conventions and errors as gconv_fwd_route; an unknown order is
+ * GCONV_ERR_INVALID_ARG. */
+gconv_status_t gconv_fwd_ex(const void *x, const int64_t *x_shape,
+                            const void *w, const int64_t *w_shape,
+                            const void *bias, void *y,
+                            const int32_t *stride, const int32_t *pad, const int32_t *dilation,
+                            int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
+                            gconv_route_t route, gconv_out_order_t order, void *hip_stream);
+
+/* Name of the kernel the last successful gconv_fwd / gconv_fwd_route / gconv_fwd_ex /
  * gconv_dw1d_bwd_data / gconv_dw1d_bwd_filter call on this host thread launched
  * (the first of two for the filter gradient; "" before the first call or after
  * an empty batch).  The string has static storage. */

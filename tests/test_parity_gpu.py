@@ -222,6 +222,54 @@ def test_nhwc_rejects_the_implicit_gemm_route():
     assert e.value.status == 3
 
 
+# The interleaved output-channel order (filter j of group k at channel j*g + k),
+# through every kernel family that stores grouped outputs.
+ORDER_CASES = [  # N, C, Cout, H, W, K, groups, route, dtypes, kernel prefix
+    (2, 32, 64, 12, 13, 3, 2, "igemm", ("f16", "bf16", "f32"), "igemm"),
+    (4, 64, 256, 12, 12, 3, 4, "igemm", ("f16",), "igemm"),        # 64 filters per group: deferred stores
+    (2, 16, 24, 9, 10, 3, 4, "direct", ("f32", "bf16"), "direct2d_tiled"),
+    (3, 16, 16, 7, 10, 3, 4, "direct", ("f16", "bf16"), "direct2d_g4"),
+    (2, 8, 16, 9, 9, 3, 8, "direct", ("f32",), "direct2d_tiled"),  # depthwise, 2 filters per channel
+]
+
+
+@pytest.mark.parametrize("ci", range(len(ORDER_CASES)))
+def test_interleaved_output_order_vs_oracle(ci):
+    N, C, Co, H, W, K, g, route, dts, kern = ORDER_CASES[ci]
+    for di, dt in enumerate(dts):
+        seed = 90 * ci + di
+        x = draw((N, C, H, W), 1.0, 7950 + seed, dt)
+        w = draw((Co, C // g, K, K), 1.0 / (C // g * K * K), 8950 + seed, dt)
+        b = draw((Co,), 0.01, 9950 + seed, dt)
+        r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), 1, K // 2, 1, g, out_order="interleaved")
+        y = gc.gconv_fwd_ex(gpu(x), gpu(w), gpu(b), 1, K // 2, 1, g, "nchw", route=route, out_order="interleaved")
+        torch.cuda.synchronize()
+        assert gc.gconv_last_kernel().startswith(kern), gc.gconv_last_kernel()
+        assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+
+
+def test_interleaved_output_order_nhwc_and_naive():
+    # NHWC generic kernel: against the NCHW interleaved oracle on permuted tensors.
+    N, C, Co, H, W, g = 2, 12, 18, 7, 8, 3
+    x = draw((N, H, W, C), 1.0, 7990, "f32")
+    w = draw((Co, 3, 3, C // g), 1.0 / (C // g * 9), 8990, "f32")
+    b = draw((Co,), 0.01, 9990, "f32")
+    r = oracle.conv2d(as_f64(x).transpose(0, 3, 1, 2), as_f64(w).transpose(0, 3, 1, 2), as_f64(b), 1, 1, 1, g,
+                      out_order="interleaved").transpose(0, 2, 3, 1)
+    y = gc.gconv_fwd_ex(gpu(x), gpu(w), gpu(b), 1, 1, 1, g, "nhwc", out_order="interleaved")
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "conv2d_nhwc_generic"
+    assert normwise(as_f64(y.cpu()), r) <= TOL["f32"]
+    # NCHW naive kernel (a dilation whose halo tile does not fit the tiled kernel's LDS).
+    x2 = draw((1, 4, 112, 112), 1.0, 7991, "f32")
+    w2 = draw((6, 2, 3, 3), 1.0 / 18, 8991, "f32")
+    r2 = oracle.conv2d(as_f64(x2), as_f64(w2), None, 1, 0, 55, 2, out_order="interleaved")
+    y2 = gc.gconv_fwd_ex(gpu(x2), gpu(w2), None, 1, 0, 55, 2, "nchw", route="direct", out_order="interleaved")
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "direct2d_naive"
+    assert normwise(as_f64(y2.cpu()), r2) <= TOL["f32"]
+
+
 def test_dw2d_unaligned_output_and_input():
     # y and x that start 4 bytes past a 16-byte boundary: single-element runs and loads.
     N, C, H, W, K = 2, 6, 24, 24, 3
