@@ -116,7 +116,7 @@ def counters_traffic(wl_name, kernel_file):
     return rec.get("hbm_bytes_per_launch")
 
 
-def measure(wl, steps, warmup, rotate_bytes=512 << 20):
+def measure(wl, steps, warmup, rotate_bytes=512 << 20, route=None):
     """Time `steps` gconv_fwd calls on rotating buffer sets.  Returns a dict.
 
     step_ms: `steps` back-to-back calls from Python (host validation, route
@@ -145,7 +145,8 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20):
         yi = torch.empty(ys, dtype=x.dtype, device=dev)
         outs.append(yi)
         sets.append((xi, wi, bi, yi))
-        calls.append(gc.PreparedCall(xi, wi, bi, yi, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout))
+        calls.append(gc.PreparedCall(xi, wi, bi, yi, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout,
+                                     route=route))
     stream = torch.cuda.current_stream(dev)
     for i in range(warmup):
         calls[i % nsets]()
@@ -168,8 +169,8 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20):
 
     # graph replay: one launch per buffer set, no host work in between
     gstream = torch.cuda.Stream(dev)
-    gcalls = [gc.PreparedCall(*t, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout, stream=gstream)
-              for t in sets]
+    gcalls = [gc.PreparedCall(*t, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout, route=route,
+                              stream=gstream) for t in sets]
     graph = torch.cuda.CUDAGraph()
     outs[0].zero_()
     torch.cuda.synchronize()
@@ -281,6 +282,28 @@ def bwd_entry(wl, kind, steps, name=None):
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
                          "traffic": counters_traffic(name, "dw1d_ntc.hip" if kind == "data" else "dw1d_wgrad.hip")
                          if name else None}}
+
+
+def autotune_entries(workloads, steps):
+    import torch
+    import depthwise_convolution_gconv_amd as gc
+    from depthwise_convolution_gconv_amd.workloads import make_inputs
+    out = {}
+    for name, wl in workloads.items():
+        ms = {}
+        for r in ("direct", "igemm"):
+            try:
+                ms[r] = round(measure(wl, max(10, steps // 10), 2, route=r)["kernel_ms_avg"], 5)
+            except gc.GconvError:
+                pass
+        x, w, b = (None if t is None else t.cuda() for t in make_inputs(wl))
+        gc.gconv_autotune_clear()
+        tuned = gc.gconv_autotune(x, w, b, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout, reps=5)
+        gc.gconv_autotune_clear()
+        del x, w, b
+        torch.cuda.empty_cache()
+        out[name] = {"static": route_of(wl), "tuned": tuned, "kernel_ms_by_route": ms}
+    return out
 
 
 def roofline(wl, route, kernel_ms, traffic):
@@ -436,6 +459,9 @@ def main():
         # Strided depthwise layers (beyond the five workloads above).
         out["next"] = {oname: measure_entry(owl, args.steps)
                        for oname, owl in NEXT_WORKLOADS.items() if oname != name}
+        # Per-shape route tuning: each route that runs the workload, timed as above,
+        # beside the static choice and the route gconv_autotune records.
+        out["autotune"] = autotune_entries(WORKLOADS, args.steps)
         # Backward of the Conformer depthwise conv1d (same shapes as its forward).
         conf = WORKLOADS["c3_dw1d_btc_f32"]
         out["next"]["n5_dw1d_bwd_data_f32"] = bwd_entry(conf, "data", args.steps, "n5_dw1d_bwd_data_f32")

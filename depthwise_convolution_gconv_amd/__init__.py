@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     conv2d_nhwc,
     dwconv1d_btc,
     dwconv1d_btc_backward,
+    gconv_autotune,
+    gconv_autotune_clear,
     gconv_dw1d_bwd_data,
     gconv_dw1d_bwd_filter,
     gconv_dw1d_bwd_filter_workspace,

@@ -27,6 +27,7 @@ ORDERS = {"grouped": 0, "interleaved": 1}
 # Every symbol include/gconv.h declares.
 EXPORTS = ("gconv_out_shape", "gconv_select_route", "gconv_fwd", "gconv_fwd_route", "gconv_fwd_ex",
            "gconv_dw1d_bwd_data", "gconv_dw1d_bwd_filter_workspace", "gconv_dw1d_bwd_filter",
+           "gconv_autotune", "gconv_autotune_clear",
            "gconv_last_kernel", "gconv_status_string", "gconv_last_error")
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.gconv_dw1d_bwd_filter.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _vp, _i32p, _i32p, _i32p, _i32,
                                             _vp, ctypes.c_size_t, _vp]
         L.gconv_dw1d_bwd_filter.restype = _i32
+        L.gconv_autotune.argtypes = conv + [_i32, _vp, _i32p]
+        L.gconv_autotune.restype = _i32
+        L.gconv_autotune_clear.argtypes = []
+        L.gconv_autotune_clear.restype = None
         L.gconv_last_kernel.argtypes = []
         L.gconv_last_kernel.restype = ctypes.c_char_p
         L.gconv_status_string.argtypes = [_i32]
@@ -211,6 +216,32 @@ def gconv_fwd_ex(x, w, bias=None, stride=1, pad=0, dilation=1, groups: int = 1, 
     """gconv_fwd with the route and the output-channel order ("grouped": filter j of
     group k at channel k*Cout/g + j; "interleaved": at channel j*g + k) chosen."""
     return _call(x, w, bias, y, stride, pad, dilation, groups, layout, route, stream, out_order)
+
+
+def gconv_autotune(x, w, bias=None, stride=1, pad=0, dilation=1, groups: int = 1, layout: str = "nchw",
+                   reps: int = 3, y=None, stream=None) -> str:
+    """Times every route that can run this call on these tensors (synchronising the
+    stream) and records the fastest for the geometry; returns its name.  y (allocated
+    when None) is overwritten with the chosen route's result."""
+    _check_tensors(x, w=w, bias=bias, y=y)
+    yshape = gconv_out_shape(tuple(x.shape), tuple(w.shape), stride, pad, dilation, groups, layout)
+    if y is None:
+        y = torch.empty(yshape, dtype=x.dtype, device=x.device)
+    elif tuple(y.shape) != yshape:
+        raise GconvError(ERR_SHAPE, f"y has shape {tuple(y.shape)}, expected {yshape}")
+    s, p, d = _geom(layout, stride, pad, dilation)
+    best = _i32(-1)
+    with torch.cuda.device(x.device):
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        _check(lib().gconv_autotune(_vp(x.data_ptr()), _arr(_i64, x.shape), _vp(w.data_ptr()), _arr(_i64, w.shape),
+                                    _vp(bias.data_ptr() if bias is not None else 0), _vp(y.data_ptr()), s, p, d,
+                                    int(groups), _layout(layout), DTYPES[x.dtype], int(reps),
+                                    _vp(st.cuda_stream), ctypes.byref(best)))
+    return ROUTE_NAMES[best.value]
+
+
+def gconv_autotune_clear() -> None:
+    lib().gconv_autotune_clear()
 
 
 def gconv_last_kernel() -> str:

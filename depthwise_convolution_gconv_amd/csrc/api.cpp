@@ -6,6 +6,9 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <map>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 #include "gconv.h"
@@ -141,6 +144,32 @@ gconv::Conv2dArgs conv2d_args(const Geometry &g, const void *x, const void *w, c
     return a;
 }
 
+// Per-shape route cache filled by gconv_autotune (the "time the candidates once,
+// keep the fastest" idea: cudnn.benchmark in the discuss.pytorch.org thread, and
+// neon compiling kernel variants and keeping the fastest in the grouped-conv
+// issue).  Keyed by everything that decides which routes can run a call and how
+// fast: layout, dtype, shapes, stride, padding, dilation and groups.
+using TuneKey = std::vector<int64_t>;
+std::mutex g_tune_mu;
+std::map<TuneKey, gconv_route_t> g_tune;
+
+TuneKey tune_key(const Geometry &g, gconv_dtype_t dtype)
+{
+    if (g.layout == GCONV_LAYOUT_NTC)
+        return {g.layout, dtype, g.B, g.T, g.C, g.Cout, g.K, g.s, g.p, g.d, g.groups};
+    return {g.layout, dtype, g.N, g.C, g.H, g.W, g.Cout, g.KH, g.KW, g.sh, g.sw, g.ph, g.pw, g.dh, g.dw, g.groups};
+}
+
+bool tuned_route(const Geometry &g, gconv_dtype_t dtype, gconv_route_t *r)
+{
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    if (g_tune.empty()) return false;
+    const auto it = g_tune.find(tune_key(g, dtype));
+    if (it == g_tune.end()) return false;
+    *r = it->second;
+    return true;
+}
+
 // Route heuristic: the implicit GEMM pays off once the per-group contraction
 // (C/g * KH * KW) and the per-group output width (Cout/g) are wide enough to
 // fill matrix-core tiles; narrow groups (depthwise, 4-channel groups) stay on
@@ -203,7 +232,11 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
         gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
         a.interleaved = order == GCONV_ORDER_INTERLEAVED;
         const bool igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
-        if (route == GCONV_ROUTE_AUTO) route = auto_route(g, dtype, igemm_ok);
+        if (route == GCONV_ROUTE_AUTO) {
+            gconv_route_t t;
+            route = (tuned_route(g, dtype, &t) && (t != GCONV_ROUTE_IGEMM || igemm_ok)) ? t
+                                                                                        : auto_route(g, dtype, igemm_ok);
+        }
         if (route == GCONV_ROUTE_IGEMM) {
             if (!igemm_ok)
                 return fail(GCONV_ERR_UNSUPPORTED, "the implicit-GEMM route does not cover this geometry "
@@ -298,8 +331,69 @@ gconv_status_t gconv_select_route(const int64_t *x_shape, const int64_t *w_shape
         const gconv::Conv2dArgs a = conv2d_args(g, dummy, dummy, nullptr, nullptr, dtype, nullptr);
         igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
     }
-    *route = auto_route(g, dtype, igemm_ok);
+    gconv_route_t t;
+    *route = (tuned_route(g, dtype, &t) && (t != GCONV_ROUTE_IGEMM || igemm_ok)) ? t : auto_route(g, dtype, igemm_ok);
     return GCONV_OK;
+}
+
+gconv_status_t gconv_autotune(const void *x, const int64_t *x_shape, const void *w, const int64_t *w_shape,
+                              const void *bias, void *y, const int32_t *stride, const int32_t *pad,
+                              const int32_t *dilation, int32_t groups, gconv_layout_t layout,
+                              gconv_dtype_t dtype, int32_t reps, void *hip_stream, gconv_route_t *best)
+{
+    g_last_error[0] = '\0';
+    if (!best) return fail(GCONV_ERR_INVALID_ARG, "NULL best");
+    if (reps < 1) return fail(GCONV_ERR_INVALID_ARG, "reps must be >= 1 (got %lld)", reps);
+    Geometry g;
+    gconv_status_t st = validate(x_shape, w_shape, stride, pad, dilation, groups, layout, &g);
+    if (st != GCONV_OK) return st;
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return fail(GCONV_ERR_LAUNCH, "hipEventCreate failed");
+    }
+    gconv_route_t win = GCONV_ROUTE_AUTO;
+    float win_ms = 0.0f;
+    gconv_status_t first_err = GCONV_OK;
+    for (gconv_route_t r : {GCONV_ROUTE_DIRECT, GCONV_ROUTE_IGEMM}) {
+        // One untimed call (which also tells whether the route runs this call),
+        // then `reps` calls between two events on the caller's stream.
+        st = run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype, r,
+                 GCONV_ORDER_GROUPED, hip_stream);
+        if (st == GCONV_ERR_UNSUPPORTED) continue;
+        if (st != GCONV_OK) { first_err = st; break; }
+        float ms = 0.0f;
+        bool ok = hipEventRecord(e0, stream) == hipSuccess;
+        for (int i = 0; ok && i < reps; ++i)
+            ok = run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype, r,
+                     GCONV_ORDER_GROUPED, hip_stream) == GCONV_OK;
+        ok = ok && hipEventRecord(e1, stream) == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+             hipEventElapsedTime(&ms, e0, e1) == hipSuccess;
+        if (!ok) { first_err = GCONV_ERR_LAUNCH; break; }
+        if (win == GCONV_ROUTE_AUTO || ms < win_ms) { win = r; win_ms = ms; }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (first_err != GCONV_OK) return first_err == GCONV_ERR_LAUNCH && !g_last_error[0]
+                                          ? fail(GCONV_ERR_LAUNCH, "timing a route failed") : first_err;
+    if (win == GCONV_ROUTE_AUTO) return fail(GCONV_ERR_UNSUPPORTED, "no route runs this convolution");
+    // y ends up holding the chosen route's result.
+    st = run(x, x_shape, w, w_shape, bias, y, stride, pad, dilation, groups, layout, dtype, win,
+             GCONV_ORDER_GROUPED, hip_stream);
+    if (st != GCONV_OK) return st;
+    {
+        std::lock_guard<std::mutex> lk(g_tune_mu);
+        g_tune[tune_key(g, dtype)] = win;
+    }
+    *best = win;
+    return GCONV_OK;
+}
+
+void gconv_autotune_clear(void)
+{
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    g_tune.clear();
 }
 
 gconv_status_t gconv_fwd(const void *x, const int64_t *x_shape, const void *w, const int64_t *w_shape,

@@ -44,8 +44,9 @@
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
  *  - The library keeps no state between calls apart from a thread-local error
- *    string, allocates no device memory and is safe to call from several host
- *    threads at once.
+ *    string and the route cache of gconv_autotune (empty unless it is called),
+ *    allocates no device memory and is safe to call from several host threads
+ *    at once.
  *  - Errors: argument and shape errors are detected on the host before anything
  *    is enqueued, and leave y untouched.  A zero-sized batch (N == 0 or B == 0)
  *    is valid and enqueues nothing; x and y may then be NULL.  No C++ exception
@@ -83,7 +84,8 @@ typedef enum { GCONV_F32 = 0, GCONV_F16 = 1, GCONV_BF16 = 2 } gconv_dtype_t;
  * functorch issue #365 "Optimize convolution batching rule performance", where
  * the maintainers agree on a user option selecting the group-convolution route. */
 typedef enum {
-    GCONV_ROUTE_AUTO = 0,       /* chosen per shape by gconv_select_route                  */
+    GCONV_ROUTE_AUTO = 0,       /* chosen per shape by gconv_select_route (a route recorded
+                                   by gconv_autotune, else the static heuristic)            */
     GCONV_ROUTE_DIRECT = 1,     /* direct convolution on the vector ALUs: LDS halo tiles,
                                    group index folded into the grid (NCHW), or the
                                    (batch, steps, channels) sliding-window kernel (NTC)     */
@@ -194,6 +196,35 @@ gconv_status_t gconv_fwd_ex(const void *x, const int64_t *x_shape,
                             const int32_t *stride, const int32_t *pad, const int32_t *dilation,
                             int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
                             gconv_route_t route, gconv_out_order_t order, void *hip_stream);
+
+/* Per-shape route tuning.  The discuss.pytorch.org thread "F.conv2d runs x15
+ * slower in mixed-precision/half-precision mode" suggests
+ * torch.backends.cudnn.benchmark (time the candidate algorithms once per shape,
+ * keep the fastest), and the neon issue "Grouped convolutions" describes neon
+ * compiling kernel variants, timing them and keeping the fastest.
+ *
+ * gconv_autotune runs the call once per route that can run it (GCONV_ROUTE_DIRECT,
+ * GCONV_ROUTE_IGEMM) untimed, then `reps` (>= 1) times between two HIP events on
+ * hip_stream, and records the route with the shortest time for this geometry
+ * (layout, dtype, shapes, stride, padding, dilation, groups) in a process-wide
+ * cache.  Later GCONV_ROUTE_AUTO calls and gconv_select_route of the same
+ * geometry take the recorded route (when it can run the call: the implicit-GEMM
+ * route also depends on pointer alignment).  The arguments are those of
+ * gconv_fwd; y is overwritten and holds the chosen route's result on return.
+ * Unlike every other entry point this one SYNCHRONISES hip_stream (to read the
+ * events).  *best receives the chosen route.  Errors as gconv_fwd;
+ * GCONV_ERR_UNSUPPORTED if no route runs the call.  The cache is guarded by a
+ * mutex; it holds host memory only and lives until gconv_autotune_clear or the
+ * end of the process. */
+gconv_status_t gconv_autotune(const void *x, const int64_t *x_shape,
+                              const void *w, const int64_t *w_shape,
+                              const void *bias, void *y,
+                              const int32_t *stride, const int32_t *pad, const int32_t *dilation,
+                              int32_t groups, gconv_layout_t layout, gconv_dtype_t dtype,
+                              int32_t reps, void *hip_stream, gconv_route_t *best);
+
+/* Forgets every route gconv_autotune recorded. */
+void gconv_autotune_clear(void);
 
 /* Name of the kernel the last successful gconv_fwd / gconv_fwd_route / gconv_fwd_ex /
  * gconv_dw1d_bwd_data / gconv_dw1d_bwd_filter call on this host thread launched

@@ -270,6 +270,36 @@ def test_interleaved_output_order_nhwc_and_naive():
     assert normwise(as_f64(y2.cpu()), r2) <= TOL["f32"]
 
 
+def test_autotune_records_a_route_and_auto_calls_follow_it():
+    gc.gconv_autotune_clear()
+    x = draw((2, 64, 28, 28), 1.0, 7970, "f16")
+    w = draw((64, 32, 3, 3), 1.0 / 288, 8970, "f16")
+    b = draw((64,), 0.01, 9970, "f16")
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), 1, 1, 1, 2)
+    heur = gc.gconv_select_route(x.shape, w.shape, 1, 1, 1, 2, "nchw", "f16")
+    assert heur == "igemm"
+    xg, wg, bg = gpu(x), gpu(w), gpu(b)
+    y = torch.full((2, 64, 28, 28), float("nan"), dtype=torch.float16, device="cuda")
+    best = gc.gconv_autotune(xg, wg, bg, 1, 1, 1, 2, "nchw", reps=3, y=y)
+    assert best in ("direct", "igemm")
+    assert normwise(as_f64(y.cpu()), r) <= TOL["f16"]            # y holds the chosen route's result
+    assert gc.gconv_select_route(x.shape, w.shape, 1, 1, 1, 2, "nchw", "f16") == best
+    y2 = gc.gconv_fwd(xg, wg, bg, 1, 1, 1, 2, "nchw")
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel().startswith("igemm") == (best == "igemm")
+    assert normwise(as_f64(y2.cpu()), r) <= TOL["f16"]
+    gc.gconv_autotune_clear()
+    assert gc.gconv_select_route(x.shape, w.shape, 1, 1, 1, 2, "nchw", "f16") == heur
+
+
+def test_autotune_skips_routes_that_cannot_run_the_call():
+    gc.gconv_autotune_clear()
+    wl = WORKLOADS["c3_dw1d_btc_f32"]
+    x, w, b = (gpu(t) for t in make_inputs(wl))
+    assert gc.gconv_autotune(x, w, b, wl.stride, wl.pad, wl.dilation, wl.groups, "ntc", reps=2) == "direct"
+    gc.gconv_autotune_clear()
+
+
 def test_dw2d_unaligned_output_and_input():
     # y and x that start 4 bytes past a 16-byte boundary: single-element runs and loads.
     N, C, H, W, K = 2, 6, 24, 24, 3
