@@ -15,9 +15,9 @@
 //    the taps (wave g takes taps g, g+4, ...; wave 0 also sums dy for the bias),
 //    lane = channel.  The tile's fp32 sums go to part[tile][k][c] (k = K holds
 //    the bias sums).
-//  * dw1d_btc_wgrad_reduce: one workgroup per (tap, 64 channels); 4 slices of
-//    the tiles are summed in order, then combined in a fixed order and rounded
-//    once to the tensor dtype.
+//  * dw1d_btc_wgrad_reduce: one workgroup per (tap, 64 channels); 16 slices of
+//    the tiles are summed in order (16-byte loads of 4 channels), then combined
+//    in a fixed order and rounded once to the tensor dtype.
 #include <algorithm>
 
 #include "common.hpp"
@@ -59,7 +59,7 @@ dw1d_btc_wgrad_partial(const T *__restrict__ x, const T *__restrict__ dy, float 
 {
     constexpr int DW = (VE * (int)sizeof(T) + 3) / 4;   // dwords per staging load
     constexpr int CPR = kCT / VE;                       // staging loads per row of 64 channels
-    constexpr int NB = 8;                               // staging loads in flight per thread
+    constexpr int NB = 16;                              // staging loads in flight per thread
     extern __shared__ float sm[];
     float *dys = sm;                  // [TT][kCT]
     float *xs = sm + TT * kCT;        // [NRW][kCT], directly after the dy rows
@@ -176,31 +176,51 @@ __global__ void __launch_bounds__(kThreads)
 dw1d_btc_wgrad_reduce(const float *__restrict__ part, T *__restrict__ dw, T *__restrict__ db,
                       int C, int K, int ntiles, int cblocks)
 {
-    __shared__ float red[kGroups][kCT];
-    const int tid = threadIdx.x, lane = tid % kCT, q = tid / kCT;
+    // 16 slices of 16 lanes; lane l of a slice takes channels 4l .. 4l+3 of the block
+    // (one 16-byte load per tile when C allows), slice q sums tiles q, q + 16, ...
+    // in order, then slice 0 adds the 16 slice sums in order.
+    constexpr int kSlices = kThreads / (kCT / 4);
+    __shared__ float red[kSlices][kCT];
+    const int tid = threadIdx.x, l16 = tid % (kCT / 4), q = tid / (kCT / 4);
     const int kk = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;   // kk == K: the bias row
-    const int c = cb * kCT + lane;
-    // Tiles q, q + 4, q + 8, ... in order, 8 loads in flight at a time.
+    const int c4 = cb * kCT + 4 * l16;
+    const bool vec = (C & 3) == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0;   // 16-byte loads
     constexpr int NB = 8;
-    float acc = 0.0f;
-    if (c < C) {
-        const float *src = part + (int64_t)kk * C + c;
-        const int64_t step = (int64_t)(K + 1) * C;
-        for (int i0 = q; i0 < ntiles; i0 += NB * kGroups) {
-            float v[NB];
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float *src = part + (int64_t)kk * C + c4;
+    const int64_t step = (int64_t)(K + 1) * C;
+    for (int i0 = q; i0 < ntiles; i0 += NB * kSlices) {
+        float4 v[NB];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int i = i0 + j * kGroups;
-                v[j] = i < ntiles ? src[i * step] : 0.0f;
+        for (int j = 0; j < NB; ++j) {
+            const int i = i0 + j * kSlices;
+            v[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (i < ntiles) {
+                const float *p = src + i * step;
+                if (vec && c4 < C) {
+                    v[j] = *reinterpret_cast<const float4 *>(p);
+                } else {
+                    if (c4 < C) v[j].x = p[0];
+                    if (c4 + 1 < C) v[j].y = p[1];
+                    if (c4 + 2 < C) v[j].z = p[2];
+                    if (c4 + 3 < C) v[j].w = p[3];
+                }
             }
+        }
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc += v[j];
+        for (int j = 0; j < NB; ++j) {
+            acc[0] += v[j].x; acc[1] += v[j].y; acc[2] += v[j].z; acc[3] += v[j].w;
         }
     }
-    red[q][lane] = acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[q][4 * l16 + e] = acc[e];
     __syncthreads();
-    if (q != 0 || c >= C) return;
-    const float v = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+    if (tid >= kCT) return;
+    const int lane = tid, c = cb * kCT + lane;
+    if (c >= C) return;
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) v += red[i][lane];
     if (kk < K) dw[(int64_t)c * K + kk] = from_f32<T>(v);
     else if (db) db[c] = from_f32<T>(v);
 }

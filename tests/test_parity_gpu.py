@@ -397,6 +397,22 @@ def test_dw1d_backward_kernels_and_determinism():
     assert normwise(as_f64(dx1.cpu()).ravel()[idx], rdx) <= 1e-4
 
 
+def test_dw1d_bwd_filter_with_a_workspace_4_bytes_off_alignment():
+    # The workspace need only be 4-byte aligned; the reduction then reads it 4 bytes at a time.
+    B_, T, C, K = 2, 90, 40, 9
+    x = draw((B_, T, C), 1.0, 7980, "f32")
+    dy = draw((B_, T, C), 1.0, 8980, "f32")
+    need = gc.gconv_dw1d_bwd_filter_workspace((B_, T, C), (C, 1, K), 1, 4, 1, "f32")
+    buf = torch.empty(need + 16, dtype=torch.uint8, device="cuda")
+    ws = buf[4:4 + need]
+    assert ws.data_ptr() % 16 == 4
+    dw, db = gc.gconv_dw1d_bwd_filter(gpu(x), gpu(dy), K, 1, 4, 1, workspace=ws)
+    torch.cuda.synchronize()
+    rdw, rdb = oracle.dwconv1d_btc_bwd_filter(as_f64(x), as_f64(dy), K, 1, 4, 1)
+    assert normwise(as_f64(dw.cpu()), rdw) <= 1e-4
+    assert normwise(as_f64(db.cpu()), rdb) <= 1e-4
+
+
 def test_dw1d_backward_empty_batch():
     x = torch.empty(0, 16, 8, device="cuda")
     w = torch.randn(8, 1, 3, device="cuda")
