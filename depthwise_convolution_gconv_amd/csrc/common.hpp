@@ -47,6 +47,31 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float v) { return (_Float16)v; }
 template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float v) { return (__bf16)v; }
 
+// Output stores that do not keep the written lines in L2 (non-temporal): outputs are
+// written once and not read again by the kernel, while the inputs a tile shares with
+// its neighbours (halo rows, filters) are.  Measured on the Conformer depthwise
+// conv1d: 12.1 -> 9.3 us.
+typedef uint32_t gconv_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gconv_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt(uint4 *p, uint4 v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(gconv_u32x4, v), reinterpret_cast<gconv_u32x4 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint2 *p, uint2 v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(gconv_u32x2, v), reinterpret_cast<gconv_u32x2 *>(p));
+}
+__device__ __forceinline__ void store_nt(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(float *p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_nt(_Float16 *p, _Float16 v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, v), reinterpret_cast<uint16_t *>(p));
+}
+__device__ __forceinline__ void store_nt(__bf16 *p, __bf16 v)
+{
+    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, v), reinterpret_cast<uint16_t *>(p));
+}
+
 // Launchers (each returns the launch status and the kernel name it picked).
 hipError_t launch_direct2d(const Conv2dArgs &a, const char **kname);
 bool dw2d_supported(const Conv2dArgs &a);

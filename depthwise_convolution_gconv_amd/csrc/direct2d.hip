@@ -293,7 +293,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
             for (int kw = 0; kw < 3; ++kw) acc = Mfma4<T>::run(fa[kh * 3 + kw], xp[kh * WP + kw], acc);
         if (p0 + lane < OH * OW) {
 #pragma unroll
-            for (int o = 0; o < 4; ++o) yg[(int64_t)o * ocs * OH * OW + p] = from_f32<T>(acc[o]);
+            for (int o = 0; o < 4; ++o) store_nt(yg + (int64_t)o * ocs * OH * OW + p, from_f32<T>(acc[o]));
         }
     }
 }

@@ -230,7 +230,7 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
     const int rmax = min(kRT, To - (t0 + rg * kRT));
 #pragma unroll
     for (int r = 0; r < kRT; ++r)
-        if (cok && r < rmax) yb[(int64_t)r * C] = from_f32<T>(acc[r]);
+        if (cok && r < rmax) store_nt(yb + (int64_t)r * C, from_f32<T>(acc[r]));
 }
 
 template <typename T>

@@ -102,7 +102,7 @@ __device__ __forceinline__ void store_run(T *p, const float *v)
 {
     constexpr int NDW = (R * (int)sizeof(T) + 3) / 4;
     if constexpr (R * sizeof(T) < 4) {
-        *p = from_f32<T>(v[0]);
+        store_nt(p, from_f32<T>(v[0]));
     } else {
         uint32_t d[NDW];
 #pragma unroll
@@ -110,9 +110,9 @@ __device__ __forceinline__ void store_run(T *p, const float *v)
             if constexpr (sizeof(T) == 4) d[i] = bits_of<T>(v[i]);
             else d[i] = bits_of<T>(v[2 * i]) | (bits_of<T>(v[2 * i + 1]) << 16);
         }
-        if constexpr (NDW == 4) *reinterpret_cast<uint4 *>(p) = make_uint4(d[0], d[1], d[2], d[3]);
-        else if constexpr (NDW == 2) *reinterpret_cast<uint2 *>(p) = make_uint2(d[0], d[1]);
-        else *reinterpret_cast<uint32_t *>(p) = d[0];
+        if constexpr (NDW == 4) store_nt(reinterpret_cast<uint4 *>(p), make_uint4(d[0], d[1], d[2], d[3]));
+        else if constexpr (NDW == 2) store_nt(reinterpret_cast<uint2 *>(p), make_uint2(d[0], d[1]));
+        else store_nt(reinterpret_cast<uint32_t *>(p), d[0]);
     }
 }
 

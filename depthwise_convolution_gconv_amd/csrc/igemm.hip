@@ -465,7 +465,7 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     auto put_deferred = [&](int u, uint4 v) {
         const int row = drow0 + 4 * (dnext + u);
         if (dnext + u < kDefItems && row < dlimit)
-            *reinterpret_cast<uint4 *>(y + dy + (int64_t)row * g.ocs * OHW) = v;
+            store_nt(reinterpret_cast<uint4 *>(y + dy + (int64_t)row * g.ocs * OHW), v);
     };
 
     for (int i = tid; i < XU; i += kIgThreads) {
@@ -662,8 +662,8 @@ igemm_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             const T *cp = ct + (tid % (kBM / 8)) * 8;
 #pragma unroll 4
             for (int row = tid / (kBM / 8); row < nrow; row += kRowStep)
-                *reinterpret_cast<uint4 *>(yp + row * ystep) =
-                    *reinterpret_cast<const uint4 *>(cp + row * kCStride);
+                store_nt(reinterpret_cast<uint4 *>(yp + row * ystep),
+                         *reinterpret_cast<const uint4 *>(cp + row * kCStride));
         } else {
             for (int c = tid; c < BN * (kBM / 8); c += kIgThreads) {
                 const int row = c / (kBM / 8), p8 = c % (kBM / 8);

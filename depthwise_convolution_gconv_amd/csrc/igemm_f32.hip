@@ -429,8 +429,8 @@ igemm_fwd_f32(const float *__restrict__ x, const float *__restrict__ w, const fl
                 if (g.y_vec) {
                     const int n = fdiv(p, g.fd_ohw);
                     const int q = fmod_q(p, n, g.fd_ohw);
-                    *reinterpret_cast<f32x4 *>(y + ((int64_t)n * g.Cout + co) * OHW + q) =
-                        *reinterpret_cast<const f32x4 *>(srcp);
+                    store_nt(reinterpret_cast<uint4 *>(y + ((int64_t)n * g.Cout + co) * OHW + q),
+                             *reinterpret_cast<const uint4 *>(srcp));
                 } else {
                     for (int e = 0; e < 4 && p + e < g.P; ++e) {
                         const int n = fdiv(p + e, g.fd_ohw);

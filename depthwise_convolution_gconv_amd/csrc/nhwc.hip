@@ -152,7 +152,7 @@ dw2d_nhwc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         T *yp = y + (((int64_t)n * OH + oh) * OW + ow0) * C + c;
 #pragma unroll
         for (int r = 0; r < TW; ++r)
-            if (ow0 + r < OW) yp[(int64_t)r * C] = from_f32<T>(acc[r]);
+            if (ow0 + r < OW) store_nt(yp + (int64_t)r * C, from_f32<T>(acc[r]));
     }
 }
 
