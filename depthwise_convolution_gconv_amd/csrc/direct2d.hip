@@ -203,7 +203,7 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
             T *__restrict__ y, int G, int H, int W, int OH, int OW, int ph, int pw, int slabs,
-            uint32_t mw, uint32_t mow, int ocs, int okg)
+            uint32_t mw, uint32_t mow, int ocs, int okg, int ystage)
 {
     extern __shared__ uint2 g4s[];
     const int HP = H + 2 * ph, WP = W + 2 * pw;
@@ -211,8 +211,9 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
     const int lane = threadIdx.x & 63;
     const int slab = blockIdx.x * kG4Waves + wave;
     if (slab >= slabs) return;   // whole wave; this kernel has no workgroup barrier
-    uint2 *xs = g4s + wave * (HP * WP + kG4Filters);
+    uint2 *xs = g4s + wave * (HP * WP + kG4Filters + OH * OW);
     uint2 *fs = xs + HP * WP;
+    uint16_t *ys = reinterpret_cast<uint16_t *>(fs + kG4Filters);   // [4][OH*OW] staged outputs
     const int HW = H * W, C = 4 * G;
     const int n = slab / G, k = slab - n * G;
     auto wave_sync = [&]() {
@@ -292,9 +293,22 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
             for (int kw = 0; kw < 3; ++kw) acc = Mfma4<T>::run(fa[kh * 3 + kw], xp[kh * WP + kw], acc);
         if (p0 + lane < OH * OW) {
+            if (ystage) {
 #pragma unroll
-            for (int o = 0; o < 4; ++o) store_nt(yg + (int64_t)o * ocs * OH * OW + p, from_f32<T>(acc[o]));
+                for (int o = 0; o < 4; ++o) ys[o * OH * OW + p] = bits16(from_f32<T>(acc[o]));
+            } else {
+#pragma unroll
+                for (int o = 0; o < 4; ++o) store_nt(yg + (int64_t)o * ocs * OH * OW + p, from_f32<T>(acc[o]));
+            }
         }
+    }
+    if (ystage) {
+        // The group's 4 output planes are one contiguous, 8-byte aligned run of y:
+        // written as whole 8-byte pieces (the 2-byte stores above would reach HBM as
+        // partial lines, the stores being non-temporal).
+        wave_sync();
+        const uint2 *ys2 = reinterpret_cast<const uint2 *>(ys);
+        for (int i = lane; i < OH * OW; i += 64) store_nt(reinterpret_cast<uint2 *>(yg) + i, ys2[i]);
     }
 }
 
@@ -307,6 +321,8 @@ bool g4_applies(const Conv2dArgs &a)
         const int64_t Cg = a.C / a.groups, Ng = a.Cout / a.groups;
         return Cg == 4 && Ng == 4 && a.KH == 3 && a.KW == 3 && a.sh == 1 && a.sw == 1 && a.dh == 1 &&
                a.dw == 1 && a.ph <= 1 && a.pw <= 1 && (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= kG4MaxPos &&
+               // image, filters and staged outputs of 4 waves within 64 KB of LDS
+               kG4Waves * ((a.H + 2 * a.ph) * (a.W + 2 * a.pw) + kG4Filters + a.OH * a.OW) * 8 <= 64 * 1024 &&
                a.W <= 339 && a.OW <= 339 &&
                (a.H * a.W) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 3) == 0 &&
                a.N * a.groups < (int64_t(1) << 30);
@@ -319,13 +335,15 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
     if constexpr (sizeof(T) == 2) {
         if (!g4_applies<T>(a)) goto tiled;
         const int slabs = (int)(a.N * a.groups);
-        const size_t lds = (size_t)kG4Waves * ((a.H + 2 * a.ph) * (a.W + 2 * a.pw) + kG4Filters) * sizeof(uint2);
+        const size_t lds = (size_t)kG4Waves * ((a.H + 2 * a.ph) * (a.W + 2 * a.pw) + kG4Filters + a.OH * a.OW) *
+                           sizeof(uint2);
         *kname = "direct2d_g4";
         hipLaunchKernelGGL((direct2d_g4<T>), dim3((unsigned)ceil_div(slabs, kG4Waves)), dim3(kThreads), lds,
                            a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
                            (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, slabs,
                            (uint32_t)(((1u << 20) + a.W - 1) / a.W), (uint32_t)(((1u << 20) + a.OW - 1) / a.OW),
-                           a.interleaved ? (int)a.groups : 1, a.interleaved ? 1 : 4);
+                           a.interleaved ? (int)a.groups : 1, a.interleaved ? 1 : 4,
+                           (!a.interleaved && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0) ? 1 : 0);
         return hipGetLastError();
     }
 tiled:
