@@ -306,6 +306,35 @@ def autotune_entries(workloads, steps):
     return out
 
 
+def copy_peak_gbs(nbytes=1 << 30, reps=10):
+    """HBM bandwidth a plain device copy reaches on this GPU (read + write bytes per
+    second), the measured counterpart of the published 8 TB/s."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
+def with_copy_frac(rf, copy_gbs):
+    """Adds the fraction of the measured copy bandwidth to an HBM-bound roofline."""
+    if rf.get("unit") == "GB/s" and copy_gbs:
+        rf = dict(rf)
+        rf["frac_of_measured_copy"] = round(rf["achieved"] / copy_gbs, 4)
+    return rf
+
+
 def roofline(wl, route, kernel_ms, traffic):
     f = flops(wl)
     byts = alg_bytes(wl)
@@ -454,6 +483,9 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     if not args.no_others:
+        copy_gbs = copy_peak_gbs()
+        out["measured_peaks"] = {"hbm_copy_GBs": copy_gbs,
+                                 "how": "torch device copy of 1 GiB, 10 repetitions; read + write bytes"}
         out["others"] = {oname: measure_entry(owl, args.steps)
                          for oname, owl in WORKLOADS.items() if oname != name}
         # Strided depthwise layers (beyond the five workloads above).
@@ -461,11 +493,16 @@ def main():
                        for oname, owl in NEXT_WORKLOADS.items() if oname != name}
         # Per-shape route tuning: each route that runs the workload, timed as above,
         # beside the static choice and the route gconv_autotune records.
+        for group in ("others", "next"):
+            for v in out[group].values():
+                v["roofline"] = with_copy_frac(v["roofline"], copy_gbs)
         out["autotune"] = autotune_entries(WORKLOADS, args.steps)
         # Backward of the Conformer depthwise conv1d (same shapes as its forward).
         conf = WORKLOADS["c3_dw1d_btc_f32"]
-        out["next"]["n5_dw1d_bwd_data_f32"] = bwd_entry(conf, "data", args.steps, "n5_dw1d_bwd_data_f32")
-        out["next"]["n6_dw1d_bwd_filter_f32"] = bwd_entry(conf, "filter", args.steps, "n6_dw1d_bwd_filter_f32")
+        for bname, kind in (("n5_dw1d_bwd_data_f32", "data"), ("n6_dw1d_bwd_filter_f32", "filter")):
+            e = bwd_entry(conf, kind, args.steps, bname)
+            e["roofline"] = with_copy_frac(e["roofline"], copy_gbs)
+            out["next"][bname] = e
     print(json.dumps(out))
 
 
