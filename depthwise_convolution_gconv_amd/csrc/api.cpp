@@ -176,7 +176,7 @@ bool tuned_route(const Geometry &g, gconv_dtype_t dtype, gconv_route_t *r)
 // the direct route, which is bound by memory traffic rather than arithmetic.
 gconv_route_t auto_route(const Geometry &g, gconv_dtype_t dtype, bool igemm_ok)
 {
-    if (g.layout != GCONV_LAYOUT_NCHW) return GCONV_ROUTE_DIRECT;
+    if (g.layout == GCONV_LAYOUT_NTC) return GCONV_ROUTE_DIRECT;
     const int64_t Kg = g.Cg_w * g.KH * g.KW;
     const int64_t Ng = g.Cout / g.groups;
     if (igemm_ok && Kg >= 64 && Ng >= 16) return GCONV_ROUTE_IGEMM;
@@ -223,11 +223,22 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
     hipError_t err;
     const char *kname = "";
     if (layout == GCONV_LAYOUT_NHWC) {
-        if (route == GCONV_ROUTE_IGEMM)
-            return fail(GCONV_ERR_UNSUPPORTED, "the implicit-GEMM route does not run the NHWC layout");
         gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
         a.interleaved = order == GCONV_ORDER_INTERLEAVED;
-        err = gconv::launch_conv2d_nhwc(a, &kname);
+        const bool igemm_ok = gconv::igemm_nhwc_supported(a);
+        if (route == GCONV_ROUTE_AUTO) {
+            gconv_route_t t;
+            route = (tuned_route(g, dtype, &t) && (t != GCONV_ROUTE_IGEMM || igemm_ok)) ? t
+                                                                                        : auto_route(g, dtype, igemm_ok);
+        }
+        if (route == GCONV_ROUTE_IGEMM) {
+            if (!igemm_ok)
+                return fail(GCONV_ERR_UNSUPPORTED, "the NHWC implicit-GEMM route needs fp16/bf16, C/g a multiple "
+                            "of 16, Cout/g a multiple of 4, the grouped output order, 16-byte aligned x and w");
+            err = gconv::launch_igemm_nhwc(a, &kname);
+        } else {
+            err = gconv::launch_conv2d_nhwc(a, &kname);
+        }
     } else if (nchw) {
         gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
         a.interleaved = order == GCONV_ORDER_INTERLEAVED;
@@ -325,11 +336,13 @@ gconv_status_t gconv_select_route(const int64_t *x_shape, const int64_t *w_shape
     const gconv_status_t st = validate(x_shape, w_shape, stride, pad, dilation, groups, layout, &g);
     if (st != GCONV_OK) return st;
     bool igemm_ok = false;
+    // A 16-byte aligned dummy pointer for x and w: the plans only inspect their alignment.
+    alignas(16) static const char dummy[16] = {0};
     if (layout == GCONV_LAYOUT_NCHW) {
-        // A 16-byte aligned dummy filter pointer: the plan only inspects its alignment.
-        alignas(16) static const char dummy[16] = {0};
         const gconv::Conv2dArgs a = conv2d_args(g, dummy, dummy, nullptr, nullptr, dtype, nullptr);
         igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
+    } else if (layout == GCONV_LAYOUT_NHWC) {
+        igemm_ok = gconv::igemm_nhwc_supported(conv2d_args(g, dummy, dummy, nullptr, nullptr, dtype, nullptr));
     }
     gconv_route_t t;
     *route = (tuned_route(g, dtype, &t) && (t != GCONV_ROUTE_IGEMM || igemm_ok)) ? t : auto_route(g, dtype, igemm_ok);

@@ -75,7 +75,9 @@ __device__ __forceinline__ void store_nt(__bf16 *p, __bf16 v)
 // Launchers (each returns the launch status and the kernel name it picked).
 hipError_t launch_direct2d(const Conv2dArgs &a, const char **kname);
 bool dw2d_supported(const Conv2dArgs &a);
-hipError_t launch_conv2d_nhwc(const Conv2dArgs &a, const char **kname);   // x, w, y channels-last             // depthwise K x K, stride 1 or 2
+hipError_t launch_conv2d_nhwc(const Conv2dArgs &a, const char **kname);   // x, w, y channels-last
+bool igemm_nhwc_supported(const Conv2dArgs &a);       // channels-last, fp16 / bf16
+hipError_t launch_igemm_nhwc(const Conv2dArgs &a, const char **kname);             // depthwise K x K, stride 1 or 2
 hipError_t launch_dw2d(const Conv2dArgs &a, const char **kname);
 bool igemm_supported(const Conv2dArgs &a);            // fp16 / bf16
 hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);

@@ -107,6 +107,11 @@ NEXT_WORKLOADS = {
     "n8_dw2d_nhwc_s1_bf16": Workload(
         "n8_dw2d_nhwc_s1_bf16", 18, "nhwc", (8, 512, 40, 256), (256, 3, 3, 1), 256, 1, 1, 1, "bf16",
         1.0, 1 / 9, 0.01, "depthwise 3x3 conv2d over channels-last tensors, stride 1, bf16"),
+    # The 32-model ensemble layer in the channels-last layout: x [64, 28, 28, 1024],
+    # w [2048, 3, 3, 32], groups 32.
+    "n9_ensemble_nhwc_f16": Workload(
+        "n9_ensemble_nhwc_f16", 19, "nhwc", (64, 28, 28, 1024), (2048, 3, 3, 32), 32, 1, 1, 1, "f16",
+        1.0, 1 / 288, 0.01, "32-model ensemble folded into groups, channels-last"),
     "n4_dw1d_s2_f32": Workload(
         "n4_dw1d_s2_f32", 14, "ntc", (8, 1024, 512), (512, 1, 31), 512, 2, 15, 1, "f32",
         1.0, 1 / 31, 0.01, "depthwise conv1d, (batch, steps, channels), stride 2"),

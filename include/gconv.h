@@ -39,7 +39,8 @@
  *            format the discuss.pytorch.org thread turns to for the fp16 grouped
  *            conv): x_shape = {N,H,W,C}, w_shape = {Cout, KH, KW, C/groups}
  *            (channels_last weight order), stride/pad/dilation = {h, w},
- *            y = {N,OH,OW,Cout}.  Direct route only.
+ *            y = {N,OH,OW,Cout}.  The implicit-GEMM route runs fp16/bf16 with C/g a
+ *            multiple of 16 (its MFMA fragments load straight from x and w).
  *    Output length per axis: floor((L + 2p - d*(K-1) - 1)/s) + 1.
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
@@ -89,10 +90,12 @@ typedef enum {
     GCONV_ROUTE_DIRECT = 1,     /* direct convolution on the vector ALUs: LDS halo tiles,
                                    group index folded into the grid (NCHW), or the
                                    (batch, steps, channels) sliding-window kernel (NTC)     */
-    GCONV_ROUTE_IGEMM = 2       /* implicit GEMM per group on the matrix cores: im2col
-                                   tiles built in LDS, never materialised (NCHW only)      */
-    /* NHWC runs on the direct route: a channels-on-lanes tile kernel for depthwise
-       layers, a coalesced one-thread-per-output kernel otherwise. */
+    GCONV_ROUTE_IGEMM = 2       /* implicit GEMM per group on the matrix cores, im2col
+                                   never materialised (NCHW: tiles built in LDS; NHWC:
+                                   fragments read straight from x and w)                  */
+    /* NHWC: the direct route is a channels-on-lanes tile kernel for depthwise layers
+       and a coalesced one-thread-per-output kernel otherwise; the implicit-GEMM route
+       loads its fragments straight from the channels-last tensors. */
 } gconv_route_t;
 
 /* Output shape of a convolution.  y_shape receives 4 (NCHW, NHWC) or 3 (NTC) values.

@@ -214,12 +214,41 @@ def test_nhwc_sweep_vs_oracle(ci, dt):
     assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
 
 
-def test_nhwc_rejects_the_implicit_gemm_route():
-    x = torch.randn(1, 8, 8, 32, device="cuda", dtype=torch.float16)
-    w = torch.randn(32, 3, 3, 16, device="cuda", dtype=torch.float16)
-    with pytest.raises(gc.GconvError) as e:
-        gc.gconv_fwd_route(x, w, None, 1, 1, 1, 2, "nhwc", route="igemm")
-    assert e.value.status == 3
+NHWC_IGEMM = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
+    (2, 64, 128, 12, 13, 3, 3, 2, 1, 1, 1, True),     # 32 in / 64 out per group
+    (1, 32, 96, 9, 9, 3, 3, 1, 2, 1, 1, False),       # dense, stride 2, 96 filters: a partial filter tile
+    (3, 128, 64, 7, 10, 1, 1, 4, 1, 0, 1, True),      # 1x1, ragged positions
+    (1, 64, 64, 11, 8, 5, 3, 4, (2, 1), (2, 1), (1, 2), True),   # anisotropic
+    (4, 256, 512, 14, 14, 3, 3, 8, 1, 1, 1, True),    # many workgroups
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(NHWC_IGEMM)))
+def test_nhwc_igemm_vs_oracle(ci, dt):
+    N, C, Co, H, W, KH, KW, g, s, p, d, has_b = NHWC_IGEMM[ci]
+    seed = 85 * ci + {"f16": 1, "bf16": 2}[dt]
+    x = draw((N, H, W, C), 1.0, 7920 + seed, dt)
+    w = draw((Co, KH, KW, C // g), 1.0 / (C // g * KH * KW), 8920 + seed, dt)
+    b = draw((Co,), 0.01, 9920 + seed, dt) if has_b else None
+    r = oracle.conv2d_nhwc(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=p, dilation=d, groups=g)
+    y = gc.gconv_fwd_route(gpu(x), gpu(w), gpu(b), s, p, d, g, "nhwc", route="igemm")
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "igemm_nhwc_mfma32x32x16"
+    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+    yd = gc.gconv_fwd_route(gpu(x), gpu(w), gpu(b), s, p, d, g, "nhwc", route="direct")
+    torch.cuda.synchronize()
+    assert normwise(as_f64(y.cpu()), as_f64(yd.cpu())) <= TOL[dt]   # the two routes agree
+
+
+def test_nhwc_implicit_gemm_route_limits():
+    # fp32, or 8 input channels per group: not the implicit GEMM; the route says so.
+    for dt, cg in ((torch.float32, 16), (torch.float16, 8)):
+        x = torch.randn(1, 8, 8, 2 * cg, device="cuda", dtype=dt)
+        w = torch.randn(32, 3, 3, cg, device="cuda", dtype=dt)
+        with pytest.raises(gc.GconvError) as e:
+            gc.gconv_fwd_route(x, w, None, 1, 1, 1, 2, "nhwc", route="igemm")
+        assert e.value.status == 3
 
 
 # The interleaved output-channel order (filter j of group k at channel j*g + k),
@@ -473,7 +502,7 @@ def test_next_workload_full_size(name):
         assert gc.gconv_last_kernel() == "dw1d_btc_tile"
     elif wl.layout == "nhwc":
         r = oracle.conv2d_nhwc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
-        assert gc.gconv_last_kernel() == "dw2d_nhwc_tile"
+        assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if wl.w_shape[3] == 1 else "igemm_nhwc_mfma32x32x16")
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         assert gc.gconv_last_kernel() == "dw2d_rows"
