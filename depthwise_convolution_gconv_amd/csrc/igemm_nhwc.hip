@@ -13,7 +13,7 @@
 // K steps of one tap x 16 channels; m = (n, oh, ow) output positions.
 // Tile: a workgroup = 4 waves = 256 consecutive positions x 64 filters of one
 // group; a wave = 64 positions x 64 filters (2 x 2 blocks of 32 x 32, 64 fp32
-// accumulators), fragments double-buffered across K steps.  Output: each lane holds
+// accumulators), fragments of 4 K steps in flight.  Output: each lane holds
 // 4 consecutive filters of one position per accumulator quad, stored as 8 bytes
 // (the two lane halves of a block write 16 contiguous bytes of y's channel run).
 #include <algorithm>
@@ -32,6 +32,7 @@ constexpr int kThreads = 256;
 constexpr int kPosWave = 64;                  // positions per wave (2 blocks of 32)
 constexpr int kPosTile = 4 * kPosWave;        // positions per workgroup
 constexpr int kFilTile = 64;                  // filters per workgroup (2 blocks of 32)
+constexpr int kDepth = 4;                     // K steps of fragments in flight
 
 template <typename T> struct MfmaN;
 template <> struct MfmaN<_Float16> {
@@ -133,26 +134,25 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
 
-    uint4 a0[2], b0[2], a1[2], b1[2];
-    load_step(0, a0, b0);
-    int s = 0;
-    for (; s + 2 <= g.ksteps; s += 2) {
-        load_step(s + 1, a1, b1);
+    // A ring of kDepth steps of fragments: step s computes from slot s % kDepth,
+    // whose next load (step s + kDepth) is issued right after, so each load has
+    // kDepth - 1 steps of MFMAs to arrive.
+    uint4 fa[kDepth][2], fb[kDepth][2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+    for (int d = 0; d < kDepth; ++d)
+        if (d < g.ksteps) load_step(d, fa[d], fb[d]);
+    for (int s0 = 0; s0 < g.ksteps; s0 += kDepth) {
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = MfmaN<T>::run(a0[nb], b0[mb], acc[nb][mb]);
-        if (s + 2 < g.ksteps) load_step(s + 2, a0, b0);
+        for (int d = 0; d < kDepth; ++d) {
+            const int s = s0 + d;
+            if (s < g.ksteps) {   // uniform
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = MfmaN<T>::run(a1[nb], b1[mb], acc[nb][mb]);
-    }
-    if (s < g.ksteps) {   // odd number of K steps: the last one is in a0/b0
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = MfmaN<T>::run(a0[nb], b0[mb], acc[nb][mb]);
+                    for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = MfmaN<T>::run(fa[d][nb], fb[d][mb], acc[nb][mb]);
+                if (s + kDepth < g.ksteps) load_step(s + kDepth, fa[d], fb[d]);
+            }
+        }
     }
 
     // Epilogue: accumulator r of block (nb, mb) is filter f0 + nb*32 + (r/4)*8 +
