@@ -61,6 +61,7 @@ struct NhwcGeom {
     int sh, sw, ph, pw, dh, dw;
     int P;                   // N*OH*OW
     int m_tiles, n_tiles;    // ceil(P / 256), ceil(Ng / 64)
+    int tiles, tiles_per_xcd;
     int ksteps;              // KH*KW*Cg/16
     FastDiv fd_ohw, fd_ow, fd_mt, fd_nt, fd_cs;   // fd_cs: Cg/16 (channel steps per tap)
 };
@@ -73,8 +74,14 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
     // Tile: (group k, filter tile nt, position tile mt), position tiles fastest.
-    const int bq = fdiv((int)blockIdx.x, g.fd_mt);
-    const int mt = (int)blockIdx.x - bq * g.m_tiles;
+    // Tiles are dealt to the XCDs in contiguous runs (workgroup b runs on XCD b % 8),
+    // so neighbouring position tiles, which read the same input rows, and the
+    // tiles of one group, which read the same filters, share one L2.
+    const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+    const int tile = xcd * g.tiles_per_xcd + rank;
+    if (tile >= min((xcd + 1) * g.tiles_per_xcd, g.tiles)) return;   // uniform over the workgroup
+    const int bq = fdiv(tile, g.fd_mt);
+    const int mt = tile - bq * g.m_tiles;
     const int k = fdiv(bq, g.fd_nt);
     const int nt = bq - k * g.n_tiles;
     const int f0 = nt * kFilTile;                       // first filter (within the group)
@@ -191,7 +198,7 @@ bool make_geom(const Conv2dArgs &a, NhwcGeom &g)
         return false;
     const int64_t P = a.N * a.OH * a.OW;
     const int64_t m_tiles = ceil_div(P, kPosTile), n_tiles = ceil_div(Ng, kFilTile);
-    if (P >= (int64_t(1) << 31) || m_tiles * n_tiles * a.groups >= (int64_t(1) << 31) ||
+    if (P >= (int64_t(1) << 31) || 8 * ceil_div(m_tiles * n_tiles * a.groups, 8) >= (int64_t(1) << 31) ||
         a.Cout * a.KH * a.KW * Cg >= (int64_t(1) << 31))
         return false;
     g.N = (int)a.N; g.C = (int)a.C; g.H = (int)a.H; g.W = (int)a.W; g.Cout = (int)a.Cout;
@@ -200,6 +207,8 @@ bool make_geom(const Conv2dArgs &a, NhwcGeom &g)
     g.P = (int)P;
     g.m_tiles = (int)m_tiles;
     g.n_tiles = (int)n_tiles;
+    g.tiles = (int)(m_tiles * n_tiles * a.groups);
+    g.tiles_per_xcd = (int)ceil_div(g.tiles, 8);
     g.ksteps = (int)(a.KH * a.KW * Cg / 16);
     g.fd_ohw = make_fastdiv((uint32_t)(a.OH * a.OW));
     g.fd_ow = make_fastdiv((uint32_t)a.OW);
@@ -222,7 +231,7 @@ hipError_t launch_igemm_nhwc(const Conv2dArgs &a, const char **kname)
     NhwcGeom g;
     if (!make_geom(a, g)) return hipErrorInvalidValue;
     *kname = "igemm_nhwc_mfma32x32x16";
-    const unsigned blocks = (unsigned)((int64_t)g.m_tiles * g.n_tiles * a.groups);
+    const unsigned blocks = (unsigned)(8 * (int64_t)g.tiles_per_xcd);
     if (a.dtype == DT_F16)
         hipLaunchKernelGGL((igemm_nhwc<_Float16>), dim3(blocks), dim3(kThreads), 0, a.stream,
                            (const _Float16 *)a.x, (const _Float16 *)a.w, (const _Float16 *)a.bias,
