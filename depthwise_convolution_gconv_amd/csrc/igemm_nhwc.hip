@@ -33,6 +33,7 @@ constexpr int kPosWave = 64;                  // positions per wave (2 blocks of
 constexpr int kPosTile = 4 * kPosWave;        // positions per workgroup
 constexpr int kFilTile = 64;                  // filters per workgroup (2 blocks of 32)
 constexpr int kDepth = 4;                     // K steps of fragments in flight
+constexpr int kRowE = kFilTile + 8;           // staged output row (elements): 144 bytes
 
 template <typename T> struct MfmaN;
 template <> struct MfmaN<_Float16> {
@@ -61,9 +62,9 @@ struct NhwcGeom {
     int sh, sw, ph, pw, dh, dw;
     int P;                   // N*OH*OW
     int m_tiles, n_tiles;    // ceil(P / 256), ceil(Ng / 64)
-    int tiles, tiles_per_xcd;
+    int tiles, tiles_per_xcd, groups;
     int ksteps;              // KH*KW*Cg/16
-    FastDiv fd_ohw, fd_ow, fd_mt, fd_nt, fd_cs;   // fd_cs: Cg/16 (channel steps per tap)
+    FastDiv fd_ohw, fd_ow, fd_g, fd_nt, fd_cs;   // fd_cs: Cg/16 (channel steps per tap)
 };
 
 template <typename T>
@@ -73,17 +74,18 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
-    // Tile: (group k, filter tile nt, position tile mt), position tiles fastest.
-    // Tiles are dealt to the XCDs in contiguous runs (workgroup b runs on XCD b % 8),
-    // so neighbouring position tiles, which read the same input rows, and the
-    // tiles of one group, which read the same filters, share one L2.
+    // Tile: (position tile mt, filter tile nt, group k), groups fastest: the tiles of
+    // all groups of one position range run together, so every 128-byte line of x
+    // (64 channels, several groups) is used whole while it is in L2.  Tiles are dealt
+    // to the XCDs in contiguous runs (workgroup b runs on XCD b % 8), so neighbouring
+    // position ranges, which read the same input rows, share one L2.
     const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
     const int tile = xcd * g.tiles_per_xcd + rank;
     if (tile >= min((xcd + 1) * g.tiles_per_xcd, g.tiles)) return;   // uniform over the workgroup
-    const int bq = fdiv(tile, g.fd_mt);
-    const int mt = tile - bq * g.m_tiles;
-    const int k = fdiv(bq, g.fd_nt);
-    const int nt = bq - k * g.n_tiles;
+    const int bq = fdiv(tile, g.fd_g);
+    const int k = tile - bq * g.groups;
+    const int mt = fdiv(bq, g.fd_nt);
+    const int nt = bq - mt * g.n_tiles;
     const int f0 = nt * kFilTile;                       // first filter (within the group)
     const int p0 = mt * kPosTile + wave * kPosWave;     // first position of this wave
 
@@ -163,27 +165,51 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     }
 
     // Epilogue: accumulator r of block (nb, mb) is filter f0 + nb*32 + (r/4)*8 +
-    // 4*half + r%4 at position p0 + mb*32 + l32; bias in fp32, one rounding, 8-byte
-    // stores of 4 consecutive filters.
+    // 4*half + r%4 at position p0 + mb*32 + l32; bias in fp32, one rounding.  When
+    // the tile's 64 filters are one 128-byte run of y per position (Cout/g a multiple
+    // of 8, y 16-byte aligned), the wave stages its 64 positions x 64 filters in its own LDS area (rows
+    // of kRowE elements, padded against bank conflicts) and stores whole 16-byte
+    // pieces, 8 lanes per position: the 8-byte pieces of the accumulator layout, from
+    // 8 different store instructions, would reach HBM as partial lines.
+    __shared__ uint4 ystage[4 * kPosWave * kRowE / 8];
+    T *st = reinterpret_cast<T *>(ystage) + wave * kPosWave * kRowE;
+    const bool staged = (g.Ng & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        if (!pok[mb]) continue;
         const int p = p0 + mb * 32 + l32;
         T *yp = y + (int64_t)p * g.Cout + k * g.Ng;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int f = f0 + nb * 32 + q * 8 + 4 * half;   // first of 4 filters
-                if (f >= g.Ng) continue;
+                const int fl = nb * 32 + q * 8 + 4 * half;   // first of 4 filters, within the tile
+                const int f = f0 + fl;
                 float v[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[nb][mb][q * 4 + e];
-                    if (bias) v[e] += to_f32(bias[k * g.Ng + f + e]);
+                    if (bias && f + e < g.Ng) v[e] += to_f32(bias[k * g.Ng + f + e]);
                 }
-                *reinterpret_cast<uint2 *>(yp + f) = make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]));
+                const uint2 pk = make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]));
+                if (staged)
+                    *reinterpret_cast<uint2 *>(st + (mb * 32 + l32) * kRowE + fl) = pk;
+                else if (pok[mb] && f < g.Ng)
+                    *reinterpret_cast<uint2 *>(yp + f) = pk;
             }
+    }
+    if (staged) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int nch = min(kFilTile, g.Ng - f0) / 8;   // 16-byte pieces per position
+#pragma unroll
+        for (int i = 0; i < kPosWave * 8 / 64; ++i) {
+            const int c = lane + 64 * i, pos = c >> 3, ch = c & 7;
+            const int p = p0 + pos;
+            if (p < g.P && ch < nch)
+                store_nt(reinterpret_cast<uint4 *>(y + (int64_t)p * g.Cout + k * g.Ng + f0 + ch * 8),
+                         *reinterpret_cast<const uint4 *>(st + pos * kRowE + ch * 8));
+        }
     }
 }
 
@@ -212,7 +238,8 @@ bool make_geom(const Conv2dArgs &a, NhwcGeom &g)
     g.ksteps = (int)(a.KH * a.KW * Cg / 16);
     g.fd_ohw = make_fastdiv((uint32_t)(a.OH * a.OW));
     g.fd_ow = make_fastdiv((uint32_t)a.OW);
-    g.fd_mt = make_fastdiv((uint32_t)m_tiles);
+    g.groups = (int)a.groups;
+    g.fd_g = make_fastdiv((uint32_t)a.groups);
     g.fd_nt = make_fastdiv((uint32_t)n_tiles);
     g.fd_cs = make_fastdiv((uint32_t)(Cg / 16));
     return true;
