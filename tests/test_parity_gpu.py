@@ -220,6 +220,7 @@ NHWC_IGEMM = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (3, 128, 64, 7, 10, 1, 1, 4, 1, 0, 1, True),      # 1x1, ragged positions
     (1, 64, 64, 11, 8, 5, 3, 4, (2, 1), (2, 1), (1, 2), True),   # anisotropic
     (4, 256, 512, 14, 14, 3, 3, 8, 1, 1, 1, True),    # many workgroups
+    (2, 32, 24, 8, 9, 3, 3, 2, 1, 1, 1, True),        # 12 filters per group: 8-byte stores, not staged
 ]
 
 
