@@ -186,3 +186,34 @@ def test_bwd_data_rejects_bad_shapes_before_launch():
     rc = L.gconv_dw1d_bwd_data(B._vp(1 << 20), B._arr(B._i64, (2, 10, 4)), B._vp(16), B._arr(B._i64, (4, 1, 3)),
                                B._vp((1 << 20) + 8), s, p, d, 0, B._vp(0))
     assert rc == B.ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- NHWC and output order (host logic)
+
+def test_nhwc_route_selection():
+    # The channels-last ensemble layer: the implicit GEMM in 16-bit, the direct route in fp32
+    # (no fp32 NHWC implicit GEMM) and for depthwise layers.
+    xs, ws = (64, 28, 28, 1024), (2048, 3, 3, 32)
+    assert gc.gconv_select_route(xs, ws, 1, 1, 1, 32, "nhwc", "f16") == "igemm"
+    assert gc.gconv_select_route(xs, ws, 1, 1, 1, 32, "nhwc", "bf16") == "igemm"
+    assert gc.gconv_select_route(xs, ws, 1, 1, 1, 32, "nhwc", "f32") == "direct"
+    assert gc.gconv_select_route((8, 512, 40, 256), (256, 3, 3, 1), 2, 1, 1, 256, "nhwc", "f16") == "direct"
+    # 8 input channels per group: not the implicit GEMM.
+    assert gc.gconv_select_route((2, 8, 8, 64), (64, 3, 3, 8), 1, 1, 1, 8, "nhwc", "f16") == "direct"
+
+
+def test_nhwc_output_shape_and_weight_check():
+    OH, OW = oracle.out_len(9, 3, 2, 1, 1), oracle.out_len(11, 2, 1, 0, 2)
+    assert gc.gconv_out_shape((2, 9, 11, 12), (18, 3, 2, 4), (2, 1), (1, 0), (1, 2), 3, "nhwc") == (2, OH, OW, 18)
+    with pytest.raises(gc.GconvError) as e:   # w's last axis must be C/groups
+        gc.gconv_out_shape((2, 9, 11, 12), (18, 3, 3, 6), 1, 1, 1, 3, "nhwc")
+    assert e.value.status == B.ERR_SHAPE
+
+
+def test_unknown_output_order_is_rejected_before_launch():
+    L = B.lib()
+    s, p, d = B._geom("nchw", 1, 1, 1)
+    rc = L.gconv_fwd_ex(B._vp(16), B._arr(B._i64, (1, 8, 5, 5)), B._vp(1 << 20), B._arr(B._i64, (8, 4, 3, 3)),
+                        B._vp(0), B._vp(1 << 24), s, p, d, 2, 0, 0, 0, 7, B._vp(0))
+    assert rc == B.ERR_INVALID_ARG
+    assert "order" in gc.gconv_last_error()
