@@ -101,7 +101,8 @@ KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_fwd_f32_mfma32x32x
                 "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip",
                 "dw1d_btc_tile": "dw1d_ntc.hip", "dw1d_btc_window": "dw1d_ntc.hip",
                 "dw1d_btc_generic": "dw1d_ntc.hip", "dw2d_nhwc_tile": "nhwc.hip",
-                "igemm_nhwc_mfma32x32x16": "igemm_nhwc.hip",
+                "igemm_nhwc_mfma32x32x16": "igemm_nhwc.hip", "conv2d_nhwc_g4": "nhwc.hip",
+                "conv2d_nhwc_g4k3": "nhwc.hip",
                 "conv2d_nhwc_generic": "nhwc.hip"}
 
 

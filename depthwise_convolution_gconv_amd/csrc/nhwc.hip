@@ -16,6 +16,7 @@
 //   each thread (one channel, each of its wave's rows) slides a window of (TW-1)*S + K
 //   input columns down the K filter rows and stores TW outputs, each store of a
 //   wave covering 64 consecutive channels.
+// conv2d_nhwc_g4<T>, conv2d_nhwc_g4k3<T>: 4 in / 4 out channels per group (below).
 // conv2d_nhwc_generic<T>: any groups, stride, padding and dilation; one thread per
 //   output, output channels fastest (coalesced stores, and the group's input
 //   channels are contiguous reads).
@@ -189,6 +190,142 @@ conv2d_nhwc_generic(const T *__restrict__ x, const T *__restrict__ w, const T *_
     }
 }
 
+// conv2d_nhwc_g4<T>: 4 input and 4 output channels per group (the ResNeXt-style
+// cardinality of the neon issue), any filter, stride, padding and dilation.  One
+// thread per (position, group): the group's 4 channels at each tap are one vector
+// load (8 bytes in 16-bit, 16 in fp32), its 4 filters' taps come from L1, and the 4
+// outputs are one vector store.  Lanes take consecutive groups of one position, so
+// a wave's loads and stores are contiguous runs of 64 groups x 4 channels.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> { typedef uint4 type; };
+template <> struct Vec4<_Float16> { typedef uint2 type; };
+template <> struct Vec4<__bf16> { typedef uint2 type; };
+
+template <typename T>
+__device__ __forceinline__ void unpack4(typename Vec4<T>::type v, float *f)
+{
+    const uint32_t *d = reinterpret_cast<const uint32_t *>(&v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = elem<T>(d, e);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+conv2d_nhwc_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+               T *__restrict__ y, int64_t total, int G, int H, int W, int OH, int OW, int KH, int KW,
+               int sh, int sw, int ph, int pw, int dh, int dw)
+{
+    typedef typename Vec4<T>::type V;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * kThreads) {
+        const int k = (int)(i % G);
+        int64_t r = i / G;
+        const int ow = (int)(r % OW); r /= OW;
+        const int oh = (int)(r % OH);
+        const int64_t n = r / OH;
+        float acc[4];
+#pragma unroll
+        for (int o = 0; o < 4; ++o) acc[o] = bias ? to_f32(bias[4 * k + o]) : 0.0f;
+        const T *wk = w + (int64_t)(4 * k) * KH * KW * 4;   // [o][kh][kw][ci] of the group's filters
+        for (int kh = 0; kh < KH; ++kh) {
+            const int ih = oh * sh - ph + kh * dh;
+            if (ih < 0 || ih >= H) continue;
+            for (int kw = 0; kw < KW; ++kw) {
+                const int iw = ow * sw - pw + kw * dw;
+                if (iw < 0 || iw >= W) continue;
+                float xv[4];
+                unpack4<T>(*reinterpret_cast<const V *>(x + ((n * H + ih) * W + iw) * 4 * G + 4 * k), xv);
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    float wv[4];
+                    unpack4<T>(*reinterpret_cast<const V *>(wk + (((int64_t)o * KH + kh) * KW + kw) * 4), wv);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[o] = fmaf(xv[c], wv[c], acc[o]);
+                }
+            }
+        }
+        V out;
+        uint32_t *od = reinterpret_cast<uint32_t *>(&out);
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int o = 0; o < 4; ++o) od[o] = __builtin_bit_cast(uint32_t, acc[o]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                od[q] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[2 * q])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[2 * q + 1])) << 16);
+        }
+        store_nt(reinterpret_cast<V *>(y + i * 4), out);
+    }
+}
+
+// The same layer with 3 x 3 filters: each thread keeps its group's 4 x 9 x 4 filter
+// values in registers (packed 16-bit, or fp32) and computes kG4Pos consecutive
+// positions, so the weights are loaded once per thread instead of once per output.
+constexpr int kG4Pos = 8;
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+conv2d_nhwc_g4k3(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+                 T *__restrict__ y, int npix, int G, int H, int W, int OH, int OW,
+                 int sh, int sw, int ph, int pw, int dh, int dw)
+{
+    typedef typename Vec4<T>::type V;
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int k = (int)(t % G);
+    const int64_t pb = t / G;                        // block of kG4Pos positions
+    if (pb * kG4Pos >= npix) return;
+    V wr[4][9];                                      // [output][tap]: the 4 input channels
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+        for (int tp = 0; tp < 9; ++tp)
+            wr[o][tp] = *reinterpret_cast<const V *>(w + ((int64_t)(4 * k + o) * 9 + tp) * 4);
+    float b[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) b[o] = bias ? to_f32(bias[4 * k + o]) : 0.0f;
+    for (int j = 0; j < kG4Pos; ++j) {
+        const int64_t pix = pb * kG4Pos + j;
+        if (pix >= npix) break;
+        const int ow = (int)(pix % OW);
+        const int64_t r = pix / OW;
+        const int oh = (int)(r % OH);
+        const int64_t n = r / OH;
+        float acc[4] = {b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh) {
+            const int ih = oh * sh - ph + kh * dh;
+            if (ih < 0 || ih >= H) continue;
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+                const int iw = ow * sw - pw + kw * dw;
+                if (iw < 0 || iw >= W) continue;
+                float xv[4];
+                unpack4<T>(*reinterpret_cast<const V *>(x + ((n * H + ih) * W + iw) * 4 * G + 4 * k), xv);
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    float wv[4];
+                    unpack4<T>(wr[o][kh * 3 + kw], wv);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[o] = fmaf(xv[c], wv[c], acc[o]);
+                }
+            }
+        }
+        V out;
+        uint32_t *od = reinterpret_cast<uint32_t *>(&out);
+        if constexpr (sizeof(T) == 4) {
+#pragma unroll
+            for (int o = 0; o < 4; ++o) od[o] = __builtin_bit_cast(uint32_t, acc[o]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                od[q] = (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[2 * q])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[2 * q + 1])) << 16);
+        }
+        store_nt(reinterpret_cast<V *>(y + (pix * G + k) * 4), out);
+    }
+}
+
 template <typename T, int K, int S, int VE>
 hipError_t run_tile(const Conv2dArgs &a)
 {
@@ -232,6 +369,30 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
         case 5: return run_tile_s<T, 5>(a);
         default: return run_tile_s<T, 7>(a);
         }
+    }
+    // 4 in / 4 out per group, grouped output order, vector-aligned tensors.
+    constexpr uintptr_t kVecAlign = 4 * sizeof(T) - 1;
+    if (a.C == 4 * a.groups && a.Cout == a.C && !a.interleaved &&
+        ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.w) |
+          reinterpret_cast<uintptr_t>(a.y)) & kVecAlign) == 0) {
+        const int64_t npix = a.N * a.OH * a.OW;
+        if (a.KH == 3 && a.KW == 3 && npix < (int64_t(1) << 31)) {
+            *kname = "conv2d_nhwc_g4k3";
+            const int64_t threads = ceil_div(npix, kG4Pos) * a.groups;
+            hipLaunchKernelGGL((conv2d_nhwc_g4k3<T>), dim3((unsigned)ceil_div(threads, kThreads)), dim3(kThreads), 0,
+                               a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)npix,
+                               (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw,
+                               a.dh, a.dw);
+            return hipGetLastError();
+        }
+        *kname = "conv2d_nhwc_g4";
+        const int64_t total = a.N * a.OH * a.OW * a.groups;
+        const int64_t blocks = std::min<int64_t>(ceil_div(total, kThreads), 1 << 20);
+        hipLaunchKernelGGL((conv2d_nhwc_g4<T>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                           (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, total, (int)a.groups,
+                           (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, (int)a.KH, (int)a.KW, a.sh, a.sw, a.ph, a.pw,
+                           a.dh, a.dw);
+        return hipGetLastError();
     }
     *kname = "conv2d_nhwc_generic";
     const int64_t total = a.N * a.OH * a.OW * a.Cout;

@@ -112,6 +112,10 @@ NEXT_WORKLOADS = {
     "n9_ensemble_nhwc_f16": Workload(
         "n9_ensemble_nhwc_f16", 19, "nhwc", (64, 28, 28, 1024), (2048, 3, 3, 32), 32, 1, 1, 1, "f16",
         1.0, 1 / 288, 0.01, "32-model ensemble folded into groups, channels-last"),
+    # The fully grouped layer (4 in / 4 out per group) in the channels-last layout.
+    "n10_fullgroup_nhwc_bf16": Workload(
+        "n10_fullgroup_nhwc_bf16", 20, "nhwc", (32, 14, 14, 1024), (1024, 3, 3, 4), 256, 1, 1, 1, "bf16",
+        1.0, 1 / 36, 0.01, "fully grouped conv2d, 4 in / 4 out per group, channels-last"),
     "n4_dw1d_s2_f32": Workload(
         "n4_dw1d_s2_f32", 14, "ntc", (8, 1024, 512), (512, 1, 31), 512, 2, 15, 1, "f32",
         1.0, 1 / 31, 0.01, "depthwise conv1d, (batch, steps, channels), stride 2"),

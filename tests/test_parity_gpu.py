@@ -195,6 +195,9 @@ NHWC_SWEEP = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (2, 32, 48, 9, 7, 3, 3, 4, 1, 1, 1, True),         # grouped (generic)
     (1, 24, 24, 11, 10, 3, 2, 3, (2, 1), (1, 0), (1, 2), True),   # anisotropic (generic)
     (2, 16, 16, 7, 7, 3, 3, 16, 1, 2, 2, True),        # depthwise with dilation 2 (generic)
+    (2, 64, 64, 9, 10, 3, 3, 16, 1, 1, 1, True),       # 4 in / 4 out per group (g4 kernel)
+    (1, 32, 32, 11, 9, 3, 3, 8, 2, 1, 2, False),       # 4 in / 4 out, stride 2, dilation 2
+    (1, 16, 16, 7, 8, 5, 3, 4, 1, (2, 1), 1, True),    # 4 in / 4 out with a 5 x 3 filter (g4 kernel)
 ]
 
 
@@ -210,7 +213,9 @@ def test_nhwc_sweep_vs_oracle(ci, dt):
     y = gc.conv2d_nhwc(gpu(x), gpu(w), gpu(b), stride=s, padding=p, dilation=d, groups=g)
     torch.cuda.synchronize()
     dw = g == C and Co == C and KH == KW and KH in (3, 5, 7) and s in (1, 2) and d == 1
-    assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else "conv2d_nhwc_generic")
+    g4 = C == 4 * g and Co == C
+    g4k = "conv2d_nhwc_g4k3" if (KH, KW) == (3, 3) else "conv2d_nhwc_g4"
+    assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else g4k if g4 else "conv2d_nhwc_generic")
     assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
 
 
@@ -503,7 +508,8 @@ def test_next_workload_full_size(name):
         assert gc.gconv_last_kernel() == "dw1d_btc_tile"
     elif wl.layout == "nhwc":
         r = oracle.conv2d_nhwc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
-        assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if wl.w_shape[3] == 1 else "igemm_nhwc_mfma32x32x16")
+        expect = {1: "dw2d_nhwc_tile", 4: "conv2d_nhwc_g4k3"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
+        assert gc.gconv_last_kernel() == expect
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         assert gc.gconv_last_kernel() == "dw2d_rows"
