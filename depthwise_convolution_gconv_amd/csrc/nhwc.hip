@@ -268,10 +268,16 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 conv2d_nhwc_g4k3(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                  T *__restrict__ y, int npix, int G, int H, int W, int OH, int OW,
-                 int sh, int sw, int ph, int pw, int dh, int dw)
+                 int sh, int sw, int ph, int pw, int dh, int dw, int wgs, int wgs_per_xcd)
 {
     typedef typename Vec4<T>::type V;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // Workgroups are dealt to the XCDs in contiguous runs (workgroup b runs on XCD
+    // b % 8), so the position blocks above and below, which read the same input
+    // rows, are read through one L2.
+    const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+    const int wg = xcd * wgs_per_xcd + rank;
+    if (wg >= min((xcd + 1) * wgs_per_xcd, wgs)) return;   // uniform over the workgroup
+    const int64_t t = (int64_t)wg * kThreads + threadIdx.x;
     const int k = (int)(t % G);
     const int64_t pb = t / G;                        // block of kG4Pos positions
     if (pb * kG4Pos >= npix) return;
@@ -376,13 +382,15 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
         ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.w) |
           reinterpret_cast<uintptr_t>(a.y)) & kVecAlign) == 0) {
         const int64_t npix = a.N * a.OH * a.OW;
-        if (a.KH == 3 && a.KW == 3 && npix < (int64_t(1) << 31)) {
+        if (a.KH == 3 && a.KW == 3 && npix < (int64_t(1) << 31) &&
+            8 * ceil_div(ceil_div(ceil_div(npix, kG4Pos) * a.groups, kThreads), 8) < (int64_t(1) << 31)) {
             *kname = "conv2d_nhwc_g4k3";
             const int64_t threads = ceil_div(npix, kG4Pos) * a.groups;
-            hipLaunchKernelGGL((conv2d_nhwc_g4k3<T>), dim3((unsigned)ceil_div(threads, kThreads)), dim3(kThreads), 0,
+            const int64_t wgs = ceil_div(threads, kThreads), per_xcd = ceil_div(wgs, 8);
+            hipLaunchKernelGGL((conv2d_nhwc_g4k3<T>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0,
                                a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)npix,
                                (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.sh, a.sw, a.ph, a.pw,
-                               a.dh, a.dw);
+                               a.dh, a.dw, (int)wgs, (int)per_xcd);
             return hipGetLastError();
         }
         *kname = "conv2d_nhwc_g4";
