@@ -7,8 +7,14 @@
 // register layout in memory: a fragment lane holds 8 consecutive K values (input
 // channels) of one row or column, and 8 consecutive channels of one position of x,
 // or of one filter tap of w [Cout][KH][KW][C/g], are one contiguous 16-byte run.
-// So this kernel loads its fragments straight from global memory (through L1/L2),
-// with no LDS staging and no transposes:
+// So this kernel needs no transposes.  Three modes, by what fits in LDS:
+//  * halo (the usual one): the tile's filter block (64 contiguous rows of w) and
+//    a zero-padded halo of the input rows its 256 positions read, the group's C/g
+//    channels per position, are copied into LDS once per workgroup with coalesced
+//    16-byte loads; every fragment is then an LDS read, and each input element is
+//    fetched from memory once per tile instead of once per tap;
+//  * filters only: the filter block in LDS, input fragments from global memory;
+//  * neither: both fragments from global memory (through L1/L2):
 //   Y_k[o][m] = sum over (tap, ci) of W_k[o][tap, ci] * X_k[tap, ci][m],
 // K steps of one tap x 16 channels; m = (n, oh, ow) output positions.
 // Tile: a workgroup = 4 waves = 256 consecutive positions x 64 filters of one
@@ -34,6 +40,12 @@ constexpr int kPosTile = 4 * kPosWave;        // positions per workgroup
 constexpr int kFilTile = 64;                  // filters per workgroup (2 blocks of 32)
 constexpr int kDepth = 4;                     // K steps of fragments in flight
 constexpr int kRowE = kFilTile + 8;           // staged output row (elements): 144 bytes
+constexpr int kMaxKtLds = 512;                // largest KH*KW*C/g whose filter block is staged in LDS
+constexpr int kFilPieces = kFilTile * kMaxKtLds / 8 / kThreads;   // 16-byte pieces per thread, at most
+constexpr int kYStageBytes = 4 * kPosWave * kRowE * 2;
+constexpr int kHaloPieces = 8;                // 16-byte halo pieces per thread, at most
+constexpr int kLdsMax = 96 * 1024;            // LDS of one workgroup in halo mode, at most
+enum { kModeGlobal = 0, kModeLdsA = 1, kModeHalo = 2 };
 
 template <typename T> struct MfmaN;
 template <> struct MfmaN<_Float16> {
@@ -64,14 +76,27 @@ struct NhwcGeom {
     int m_tiles, n_tiles;    // ceil(P / 256), ceil(Ng / 64)
     int tiles, tiles_per_xcd, groups;
     int ksteps;              // KH*KW*Cg/16
+    int ktot;                // KH*KW*Cg: elements of one filter
     FastDiv fd_ohw, fd_ow, fd_g, fd_nt, fd_cs;   // fd_cs: Cg/16 (channel steps per tap)
+    FastDiv fd_ppr;          // ktot/8: 16-byte pieces per filter
+    // Halo mode: virtual padded input rows R = n*Hp + ih + ph; the tile's halo holds
+    // rows R_lo .. R_lo + NR - 1 (R_lo: the first position's first row) and padded
+    // columns 0 .. WL - 1, C/g channels per slot plus one spare 16-byte unit.
+    int Hp, NR, WL, hpieces;     // hpieces = NR*WL*Cg/8
+    FastDiv fd_hp, fd_wl, fd_c8; // Hp, WL, Cg/8
 };
 
-template <typename T>
+// MODE: kModeGlobal, kModeLdsA (filters in LDS, ktot <= kMaxKtLds) or kModeHalo
+// (filters and the input halo in LDS).
+template <typename T, int MODE>
 __global__ void __launch_bounds__(kThreads)
 igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
            T *__restrict__ y, NhwcGeom g)
 {
+    // LDS: the filter block and the input halo during the K loop, then the output
+    // staging.
+    constexpr bool LDS_A = MODE != kModeGlobal, HALO = MODE == kModeHalo;
+    extern __shared__ uint4 smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, l32 = lane & 31;
     // Tile: (position tile mt, filter tile nt, group k), groups fastest: the tiles of
@@ -105,7 +130,8 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     for (int mb = 0; mb < 2; ++mb) {
         const int p = p0 + mb * 32 + l32;
         pok[mb] = p < g.P;
-        const int pc = pok[mb] ? p : 0;
+        // Positions past P compute on a valid one (P - 1 lies in the tile, so also in its halo).
+        const int pc = pok[mb] ? p : (HALO ? g.P - 1 : 0);
         pn[mb] = fdiv(pc, g.fd_ohw);
         const int q = pc - pn[mb] * g.OH * g.OW;
         poh[mb] = fdiv(q, g.fd_ow);
@@ -113,26 +139,132 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     }
     const int cbase = k * g.Cg + 8 * half;               // this lane's channel offset in x
 
+    // Filter block in LDS: row r (filter f0 + r, zeros past Ng) holds the filter's
+    // ktot elements, K order (tap, channel), and one spare unit.  The row stride,
+    // ktot/8 + 1 units of 16 bytes, is odd, so the 16-byte A reads of consecutive
+    // rows are free of bank conflicts.  All of a thread's loads are issued before
+    // the first LDS write.
+    const int rowu = g.ktot / 8 + 1;
+    if constexpr (LDS_A) {
+        const int ppr = g.ktot / 8, nrows = min(kFilTile, g.Ng - f0);
+        const uint4 *wsrc = reinterpret_cast<const uint4 *>(w + (int64_t)(k * g.Ng + f0) * g.ktot);
+        uint4 pv[kFilPieces];
+#pragma unroll
+        for (int j = 0; j < kFilPieces; ++j) {
+            const int i = tid + j * kThreads;
+            pv[j] = make_uint4(0, 0, 0, 0);
+            if (i < kFilTile * ppr && fdiv(i, g.fd_ppr) < nrows) pv[j] = wsrc[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kFilPieces; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < kFilTile * ppr) {
+                const int r = fdiv(i, g.fd_ppr);
+                smem[r * rowu + (i - r * ppr)] = pv[j];
+            }
+        }
+    }
+    // Input halo, after the filter block: slot (rr, col) at units (rr*WL + col)*SU ..,
+    // SU = Cg/8 + 1 (odd, so lanes on consecutive slots read distinct banks).  Piece i
+    // is 8 channels of one slot; consecutive threads take consecutive pieces, so a
+    // load instruction covers whole C/g-channel runs of consecutive input columns.
+    // Rows outside the image (padding, or past the last image) and columns in the
+    // padding are written as zeros.
+    const int SU = g.Cg / 8 + 1;
+    uint4 *halo = smem + kFilTile * rowu;
+    int R_lo = 0;
+    if constexpr (HALO) {
+        const int pt = mt * kPosTile;
+        const int n_first = fdiv(pt, g.fd_ohw);
+        R_lo = n_first * g.Hp + fdiv(pt - n_first * g.OH * g.OW, g.fd_ow) * g.sh;
+        const int c8n = g.Cg / 8;
+        uint4 hv[kHaloPieces];
+#pragma unroll
+        for (int j = 0; j < kHaloPieces; ++j) {
+            const int i = tid + j * kThreads;
+            hv[j] = make_uint4(0, 0, 0, 0);
+            if (i < g.hpieces) {
+                const int slot = fdiv(i, g.fd_c8), c8 = i - slot * c8n;
+                const int rr = fdiv(slot, g.fd_wl), col = slot - rr * g.WL;
+                const int R = R_lo + rr, n = fdiv(R, g.fd_hp);
+                const int ih = R - n * g.Hp - g.ph, iw = col - g.pw;
+                if (n < g.N && ih >= 0 && ih < g.H && iw >= 0 && iw < g.W)
+                    hv[j] = *reinterpret_cast<const uint4 *>(
+                        x + (((int64_t)n * g.H + ih) * g.W + iw) * g.C + k * g.Cg + 8 * c8);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kHaloPieces; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < g.hpieces) {
+                const int slot = fdiv(i, g.fd_c8);
+                halo[slot * SU + (i - slot * c8n)] = hv[j];
+            }
+        }
+    }
+    if constexpr (LDS_A) __syncthreads();
+    // Halo mode: halo slot of tap (0, 0) for this lane's positions, and per-tap slot offsets.
+    int hslot[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+        hslot[mb] = (pn[mb] * g.Hp + poh[mb] * g.sh - R_lo) * g.WL + pow_[mb] * g.sw;
+
     // Fragments of K step s = (tap, channel step): zero for filters past Ng, for
     // positions past P and for taps in the padding.
-    auto load_step = [&](int s, uint4 (&a)[2], uint4 (&b)[2]) {
-        const int t = fdiv(s, g.fd_cs);
-        const int cs = (s - t * (g.Cg / 16)) * 16;
-        const int kh = t / g.KW, kw = t - kh * g.KW;
+    // Steps are loaded in order, so the (tap, channel step) of the next load is kept
+    // as wave-uniform counters and advanced once per step, with no division.
+    struct StepPos {
+        int s, cc, kh, kw;   // step; channel step within the tap; tap row and column
+        int toff;            // halo mode: units from a position's tap (0,0) slot to its tap (kh,kw) slot
+    } ld = {0, 0, 0, 0, 0};
+    const int csteps = g.Cg / 16;
+    auto advance = [&]() {
+        ++ld.s;
+        if (++ld.cc == csteps) {
+            ld.cc = 0;
+            ld.toff += g.dw * SU;
+            if (++ld.kw == g.KW) {
+                ld.kw = 0;
+                ++ld.kh;
+                ld.toff += (g.dh * g.WL - g.KW * g.dw) * SU;
+            }
+        }
+    };
+    int arow[2], hbase[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) arow[nb] = (nb * 32 + l32) * rowu + half;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) hbase[mb] = hslot[mb] * SU + half;
+    // Fragments of the step at ld: zero for filters past Ng, for positions past P
+    // and for taps in the padding.
+    auto load_step = [&](uint4 (&a)[2], uint4 (&b)[2]) {
+        const int cs = ld.cc * 16;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            a[nb] = make_uint4(0, 0, 0, 0);
-            if (fok[nb]) a[nb] = *reinterpret_cast<const uint4 *>(wrow[nb] + t * g.Cg + cs);
+            if constexpr (LDS_A) {
+                // elements s*16 + 8*half .. +7 of row nb*32 + l32 (K order: tap, channel)
+                a[nb] = smem[arow[nb] + 2 * ld.s];
+            } else {
+                a[nb] = make_uint4(0, 0, 0, 0);
+                if (fok[nb])
+                    a[nb] = *reinterpret_cast<const uint4 *>(wrow[nb] + (ld.kh * g.KW + ld.kw) * g.Cg + cs);
+            }
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int ih = poh[mb] * g.sh - g.ph + kh * g.dh;
-            const int iw = pow_[mb] * g.sw - g.pw + kw * g.dw;
-            b[mb] = make_uint4(0, 0, 0, 0);
-            if (pok[mb] && ih >= 0 && ih < g.H && iw >= 0 && iw < g.W)
-                b[mb] = *reinterpret_cast<const uint4 *>(
-                    x + (((int64_t)pn[mb] * g.H + ih) * g.W + iw) * g.C + cbase + cs);
+            if constexpr (HALO) {
+                // channels cs + 8*half .. +7 at the tap's slot
+                b[mb] = halo[hbase[mb] + ld.toff + 2 * ld.cc];
+            } else {
+                const int ih = poh[mb] * g.sh - g.ph + ld.kh * g.dh;
+                const int iw = pow_[mb] * g.sw - g.pw + ld.kw * g.dw;
+                b[mb] = make_uint4(0, 0, 0, 0);
+                if (pok[mb] && ih >= 0 && ih < g.H && iw >= 0 && iw < g.W)
+                    b[mb] = *reinterpret_cast<const uint4 *>(
+                        x + (((int64_t)pn[mb] * g.H + ih) * g.W + iw) * g.C + cbase + cs);
+            }
         }
+        advance();
     };
 
     f32x16 acc[2][2];
@@ -146,10 +278,25 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     // A ring of kDepth steps of fragments: step s computes from slot s % kDepth,
     // whose next load (step s + kDepth) is issued right after, so each load has
     // kDepth - 1 steps of MFMAs to arrive.
+    // Bias of this lane's accumulator rows, loaded ahead of the K loop and kept as
+    // 16-bit values, two per register.
+    uint32_t bv[2][4][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+                uint32_t lo = 0, hi = 0;
+                const int f = f0 + nb * 32 + q * 8 + 4 * half + 2 * e2;
+                if (bias && f < g.Ng) lo = __builtin_bit_cast(uint16_t, bias[k * g.Ng + f]);
+                if (bias && f + 1 < g.Ng) hi = __builtin_bit_cast(uint16_t, bias[k * g.Ng + f + 1]);
+                bv[nb][q][e2] = lo | (hi << 16);
+            }
     uint4 fa[kDepth][2], fb[kDepth][2];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
-        if (d < g.ksteps) load_step(d, fa[d], fb[d]);
+        if (d < g.ksteps) load_step(fa[d], fb[d]);
     for (int s0 = 0; s0 < g.ksteps; s0 += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
@@ -159,7 +306,7 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
                 for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                     for (int mb = 0; mb < 2; ++mb) acc[nb][mb] = MfmaN<T>::run(fa[d][nb], fb[d][mb], acc[nb][mb]);
-                if (s + kDepth < g.ksteps) load_step(s + kDepth, fa[d], fb[d]);
+                if (s + kDepth < g.ksteps) load_step(fa[d], fb[d]);
             }
         }
     }
@@ -171,9 +318,9 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
     // of kRowE elements, padded against bank conflicts) and stores whole 16-byte
     // pieces, 8 lanes per position: the 8-byte pieces of the accumulator layout, from
     // 8 different store instructions, would reach HBM as partial lines.
-    __shared__ uint4 ystage[4 * kPosWave * kRowE / 8];
-    T *st = reinterpret_cast<T *>(ystage) + wave * kPosWave * kRowE;
+    T *st = reinterpret_cast<T *>(smem) + wave * kPosWave * kRowE;
     const bool staged = (g.Ng & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
+    if constexpr (LDS_A) __syncthreads();   // the other waves' last A reads are done
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         const int p = p0 + mb * 32 + l32;
@@ -188,7 +335,10 @@ igemm_nhwc(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     v[e] = acc[nb][mb][q * 4 + e];
-                    if (bias && f + e < g.Ng) v[e] += to_f32(bias[k * g.Ng + f + e]);
+                    if (bias) {
+                        const uint16_t h = (uint16_t)(bv[nb][q][e >> 1] >> (16 * (e & 1)));
+                        v[e] += to_f32(__builtin_bit_cast(T, h));
+                    }
                 }
                 const uint2 pk = make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]));
                 if (staged)
@@ -236,6 +386,28 @@ bool make_geom(const Conv2dArgs &a, NhwcGeom &g)
     g.tiles = (int)(m_tiles * n_tiles * a.groups);
     g.tiles_per_xcd = (int)ceil_div(g.tiles, 8);
     g.ksteps = (int)(a.KH * a.KW * Cg / 16);
+    g.ktot = (int)(a.KH * a.KW * Cg);
+    g.fd_ppr = make_fastdiv((uint32_t)(g.ktot / 8));
+    // Halo rows one tile can need: the virtual output rows its kPosTile positions
+    // touch (V), the image boundaries among them, each adding the rows between the
+    // images' output ranges, and the filter's reach; never more than all N*Hp rows.
+    const int64_t Hp = a.H + 2 * (int64_t)a.ph;
+    const bool aligned_rows = kPosTile % a.OW == 0;
+    const int64_t V = aligned_rows ? kPosTile / a.OW : (kPosTile - 1) / a.OW + 2;
+    const int64_t crossings =
+        (V <= 1) ? 0 : ((aligned_rows && a.OH % (kPosTile / a.OW) == 0) ? 0 : (V - 2) / a.OH + 1);
+    const int64_t gap = std::max<int64_t>(0, Hp - a.OH * (int64_t)a.sh);
+    const int64_t NR = std::min<int64_t>((V - 1) * a.sh + crossings * gap + (a.KH - 1) * (int64_t)a.dh + 1,
+                                         a.N * Hp);
+    const int64_t WL = (a.OW - 1) * (int64_t)a.sw + (a.KW - 1) * (int64_t)a.dw + 1;
+    const int64_t hpieces = NR * WL * (Cg / 8);
+    g.Hp = (int)std::min<int64_t>(Hp, INT32_MAX);
+    g.NR = (int)std::min<int64_t>(NR, INT32_MAX);
+    g.WL = (int)std::min<int64_t>(WL, INT32_MAX);
+    g.hpieces = (int)std::min<int64_t>(hpieces, INT32_MAX);
+    g.fd_hp = make_fastdiv((uint32_t)g.Hp);
+    g.fd_wl = make_fastdiv((uint32_t)g.WL);
+    g.fd_c8 = make_fastdiv((uint32_t)(Cg / 8));
     g.fd_ohw = make_fastdiv((uint32_t)(a.OH * a.OW));
     g.fd_ow = make_fastdiv((uint32_t)a.OW);
     g.groups = (int)a.groups;
@@ -243,6 +415,40 @@ bool make_geom(const Conv2dArgs &a, NhwcGeom &g)
     g.fd_nt = make_fastdiv((uint32_t)n_tiles);
     g.fd_cs = make_fastdiv((uint32_t)(Cg / 16));
     return true;
+}
+
+// LDS bytes of the filter block and of the input halo.
+size_t filter_lds(const NhwcGeom &g) { return (size_t)kFilTile * (g.ktot / 8 + 1) * 16; }
+size_t halo_lds(const NhwcGeom &g) { return (size_t)g.NR * g.WL * (g.Cg / 8 + 1) * 16; }
+
+int pick_mode(const NhwcGeom &g)
+{
+    if (g.ktot > kMaxKtLds) return kModeGlobal;
+    if (g.hpieces <= kHaloPieces * kThreads && (int64_t)g.N * g.Hp < (int64_t(1) << 30) &&
+        filter_lds(g) + halo_lds(g) <= (size_t)kLdsMax)
+        return kModeHalo;
+    return kModeLdsA;
+}
+
+template <typename T, int MODE>
+void launch_mode(const Conv2dArgs &a, const NhwcGeom &g, unsigned blocks, size_t lds)
+{
+    hipLaunchKernelGGL((igemm_nhwc<T, MODE>), dim3(blocks), dim3(kThreads), lds, a.stream, (const T *)a.x,
+                       (const T *)a.w, (const T *)a.bias, (T *)a.y, g);
+}
+
+template <typename T>
+void launch_typed(const Conv2dArgs &a, const NhwcGeom &g, unsigned blocks)
+{
+    const int mode = pick_mode(g);
+    const size_t lds = std::max<size_t>(
+        kYStageBytes, mode == kModeHalo ? filter_lds(g) + halo_lds(g) : mode == kModeLdsA ? filter_lds(g) : 0);
+    if (mode == kModeHalo)
+        launch_mode<T, kModeHalo>(a, g, blocks, lds);
+    else if (mode == kModeLdsA)
+        launch_mode<T, kModeLdsA>(a, g, blocks, lds);
+    else
+        launch_mode<T, kModeGlobal>(a, g, blocks, lds);
 }
 
 }  // namespace
@@ -260,12 +466,9 @@ hipError_t launch_igemm_nhwc(const Conv2dArgs &a, const char **kname)
     *kname = "igemm_nhwc_mfma32x32x16";
     const unsigned blocks = (unsigned)(8 * (int64_t)g.tiles_per_xcd);
     if (a.dtype == DT_F16)
-        hipLaunchKernelGGL((igemm_nhwc<_Float16>), dim3(blocks), dim3(kThreads), 0, a.stream,
-                           (const _Float16 *)a.x, (const _Float16 *)a.w, (const _Float16 *)a.bias,
-                           (_Float16 *)a.y, g);
+        launch_typed<_Float16>(a, g, blocks);
     else
-        hipLaunchKernelGGL((igemm_nhwc<__bf16>), dim3(blocks), dim3(kThreads), 0, a.stream,
-                           (const __bf16 *)a.x, (const __bf16 *)a.w, (const __bf16 *)a.bias, (__bf16 *)a.y, g);
+        launch_typed<__bf16>(a, g, blocks);
     return hipGetLastError();
 }
 

@@ -226,6 +226,10 @@ NHWC_IGEMM = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (1, 64, 64, 11, 8, 5, 3, 4, (2, 1), (2, 1), (1, 2), True),   # anisotropic
     (4, 256, 512, 14, 14, 3, 3, 8, 1, 1, 1, True),    # many workgroups
     (2, 32, 24, 8, 9, 3, 3, 2, 1, 1, 1, True),        # 12 filters per group: 8-byte stores, not staged
+    (1, 128, 32, 5, 6, 2, 2, 1, 1, 0, 1, False),      # 512 elements per filter: the largest LDS filter block
+    (1, 128, 64, 6, 7, 3, 3, 2, 1, 1, 1, True),       # 576 elements per filter: filters from global memory
+    (1, 64, 64, 4, 300, 3, 3, 2, 1, 1, 1, True),      # 300-wide rows: input halo too large, filters in LDS
+    (3, 64, 64, 5, 7, 3, 3, 2, 2, 1, 1, True),        # stride 2, tiles across several images
 ]
 
 
