@@ -332,6 +332,97 @@ conv2d_nhwc_g4k3(const T *__restrict__ x, const T *__restrict__ w, const T *__re
     }
 }
 
+// 16-bit 3 x 3 layers with column stride and dilation 1: each thread takes 8
+// consecutive outputs of one output row for its group.  It loads its group's
+// filters (4 outputs x 9 taps x 4 inputs, packed pairs) and the 3 x 10 input
+// vectors the 8 outputs read, all before the first product, and accumulates with
+// v_dot2_f32_{f16,bf16} (two products of 16-bit pairs added to an fp32 sum), so no
+// operand is converted.  Index math is 32-bit and done once per thread.
+template <typename T> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c);
+template <> __device__ __forceinline__ float dot2<_Float16>(uint32_t a, uint32_t b, float c)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+}
+template <> __device__ __forceinline__ float dot2<__bf16>(uint32_t a, uint32_t b, float c)
+{
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+}
+
+constexpr int kRowOut = 8;   // outputs per thread along a row
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+conv2d_nhwc_g4k3_row(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+                     T *__restrict__ y, int G, int H, int W, int OH, int OW, int sh, int ph, int pw, int dh,
+                     int nowb, int total, int wgs, int wgs_per_xcd)
+{
+    // Workgroups are dealt to the XCDs in contiguous runs (workgroup b runs on XCD
+    // b % 8), so neighbouring rows, which read the same input rows, share one L2.
+    const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+    const int wg = xcd * wgs_per_xcd + rank;
+    if (wg >= min((xcd + 1) * wgs_per_xcd, wgs)) return;   // uniform over the workgroup
+    const int t = wg * kThreads + (int)threadIdx.x;
+    if (t >= total) return;
+    // t = ((n*OH + oh)*nowb + owb)*G + k: groups fastest, so a wave's lanes read and
+    // write consecutive 8-byte runs of one position.
+    const int k = t % G;
+    int r = t / G;
+    const int owb = r % nowb;
+    r /= nowb;
+    const int oh = r % OH, n = r / OH;
+    const int ow0 = owb * kRowOut;
+    const int64_t rowstride = (int64_t)W * 4 * G;   // elements between input rows
+
+    uint2 wr[4][9];   // [output][tap]: the 4 input channels as two packed pairs
+#pragma unroll
+    for (int o = 0; o < 4; ++o)
+#pragma unroll
+        for (int tp = 0; tp < 9; ++tp)
+            wr[o][tp] = *reinterpret_cast<const uint2 *>(w + ((4 * k + o) * 9 + tp) * 4);
+    uint2 xr[3][kRowOut + 2];
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh) {
+        const int ih = oh * sh - ph + kh * dh;
+        const bool rok = ih >= 0 && ih < H;
+        const T *xrow = x + ((int64_t)n * H + (rok ? ih : 0)) * rowstride + 4 * k;
+#pragma unroll
+        for (int c = 0; c < kRowOut + 2; ++c) {
+            const int iw = ow0 - pw + c;
+            xr[kh][c] = make_uint2(0, 0);
+            if (rok && iw >= 0 && iw < W) xr[kh][c] = *reinterpret_cast<const uint2 *>(xrow + (int64_t)iw * 4 * G);
+        }
+    }
+    float b[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) b[o] = bias ? to_f32(bias[4 * k + o]) : 0.0f;
+    T *yrow = y + (((int64_t)n * OH + oh) * OW) * 4 * G + 4 * k;
+#pragma unroll
+    for (int j = 0; j < kRowOut; ++j) {
+        float acc[4] = {b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+                const uint2 xv = xr[kh][j + kw];
+#pragma unroll
+                for (int o = 0; o < 4; ++o) {
+                    acc[o] = dot2<T>(xv.x, wr[o][kh * 3 + kw].x, acc[o]);
+                    acc[o] = dot2<T>(xv.y, wr[o][kh * 3 + kw].y, acc[o]);
+                }
+            }
+        if (ow0 + j < OW) {
+            const uint2 out = make_uint2(
+                (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[0])) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[1])) << 16),
+                (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[2])) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(acc[3])) << 16));
+            store_nt(reinterpret_cast<uint2 *>(yrow + (int64_t)(ow0 + j) * 4 * G), out);
+        }
+    }
+}
+
 template <typename T, int K, int S, int VE>
 hipError_t run_tile(const Conv2dArgs &a)
 {
@@ -382,6 +473,21 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
         ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.w) |
           reinterpret_cast<uintptr_t>(a.y)) & kVecAlign) == 0) {
         const int64_t npix = a.N * a.OH * a.OW;
+        if constexpr (sizeof(T) == 2) {
+            const int64_t nowb = ceil_div(a.OW, kRowOut);
+            const int64_t total = a.N * a.OH * nowb * a.groups;
+            if (a.KH == 3 && a.KW == 3 && a.sw == 1 && a.dw == 1 &&
+                8 * ceil_div(ceil_div(total, kThreads), 8) * kThreads < (int64_t(1) << 31) &&
+                a.Cout * 9 * 4 < (int64_t(1) << 31)) {
+                *kname = "conv2d_nhwc_g4k3_row";
+                const int64_t wgs = ceil_div(total, kThreads), per_xcd = ceil_div(wgs, 8);
+                hipLaunchKernelGGL((conv2d_nhwc_g4k3_row<T>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0,
+                                   a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
+                                   (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.sh, a.ph, a.pw, a.dh,
+                                   (int)nowb, (int)total, (int)wgs, (int)per_xcd);
+                return hipGetLastError();
+            }
+        }
         if (a.KH == 3 && a.KW == 3 && npix < (int64_t(1) << 31) &&
             8 * ceil_div(ceil_div(ceil_div(npix, kG4Pos) * a.groups, kThreads), 8) < (int64_t(1) << 31)) {
             *kname = "conv2d_nhwc_g4k3";

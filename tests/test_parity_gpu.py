@@ -198,6 +198,9 @@ NHWC_SWEEP = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (2, 64, 64, 9, 10, 3, 3, 16, 1, 1, 1, True),       # 4 in / 4 out per group (g4 kernel)
     (1, 32, 32, 11, 9, 3, 3, 8, 2, 1, 2, False),       # 4 in / 4 out, stride 2, dilation 2
     (1, 16, 16, 7, 8, 5, 3, 4, 1, (2, 1), 1, True),    # 4 in / 4 out with a 5 x 3 filter (g4 kernel)
+    (3, 32, 32, 6, 13, 3, 3, 8, 1, 1, 1, True),        # 4 in / 4 out, rows of 13: a ragged 8-output block
+    (1, 64, 64, 10, 17, 3, 3, 16, (2, 1), (1, 0), (2, 1), False),   # 4 in / 4 out, row stride and dilation 2
+    (2, 16, 16, 5, 8, 3, 3, 4, 1, 0, 1, True),         # 4 in / 4 out, no padding
 ]
 
 
@@ -214,7 +217,10 @@ def test_nhwc_sweep_vs_oracle(ci, dt):
     torch.cuda.synchronize()
     dw = g == C and Co == C and KH == KW and KH in (3, 5, 7) and s in (1, 2) and d == 1
     g4 = C == 4 * g and Co == C
-    g4k = "conv2d_nhwc_g4k3" if (KH, KW) == (3, 3) else "conv2d_nhwc_g4"
+    sw = s[1] if isinstance(s, tuple) else s
+    dw_ = d[1] if isinstance(d, tuple) else d
+    row = dt != "f32" and sw == 1 and dw_ == 1
+    g4k = ("conv2d_nhwc_g4k3_row" if row else "conv2d_nhwc_g4k3") if (KH, KW) == (3, 3) else "conv2d_nhwc_g4"
     assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else g4k if g4 else "conv2d_nhwc_generic")
     assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
 
@@ -512,7 +518,8 @@ def test_next_workload_full_size(name):
         assert gc.gconv_last_kernel() == "dw1d_btc_tile"
     elif wl.layout == "nhwc":
         r = oracle.conv2d_nhwc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
-        expect = {1: "dw2d_nhwc_tile", 4: "conv2d_nhwc_g4k3"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
+        # the 4-in/4-out layers here are 16-bit, 3 x 3, unit column stride and dilation
+        expect = {1: "dw2d_nhwc_tile", 4: "conv2d_nhwc_g4k3_row"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
         assert gc.gconv_last_kernel() == expect
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
