@@ -356,21 +356,24 @@ template <typename T>
 __global__ void __launch_bounds__(kThreads)
 conv2d_nhwc_g4k3_row(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                      T *__restrict__ y, int G, int H, int W, int OH, int OW, int sh, int ph, int pw, int dh,
-                     int nowb, int total, int wgs, int wgs_per_xcd)
+                     int nowb, int nrb, int nkb, int wgs, int wgs_per_xcd)
 {
     // Workgroups are dealt to the XCDs in contiguous runs (workgroup b runs on XCD
     // b % 8), so neighbouring rows, which read the same input rows, share one L2.
     const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
     const int wg = xcd * wgs_per_xcd + rank;
     if (wg >= min((xcd + 1) * wgs_per_xcd, wgs)) return;   // uniform over the workgroup
+    // A wave takes 16 consecutive groups (lanes mod 16) x 4 consecutive row blocks
+    // (lanes / 16): each group's filters are read by 4 lanes at once, and each
+    // position's 16 groups are one 128-byte run of x or y.  Waves take the group
+    // blocks fastest.  Row block rbk = (n*OH + oh)*nowb + owb.
     const int t = wg * kThreads + (int)threadIdx.x;
-    if (t >= total) return;
-    // t = ((n*OH + oh)*nowb + owb)*G + k: groups fastest, so a wave's lanes read and
-    // write consecutive 8-byte runs of one position.
-    const int k = t % G;
-    int r = t / G;
-    const int owb = r % nowb;
-    r /= nowb;
+    const int q = t >> 6, kb = q % nkb;
+    const int k = kb * 16 + (t & 15);
+    const int rbk = (q / nkb) * 4 + ((t >> 4) & 3);
+    if (k >= G || rbk >= nrb) return;
+    const int owb = rbk % nowb;
+    const int r = rbk / nowb;
     const int oh = r % OH, n = r / OH;
     const int ow0 = owb * kRowOut;
     const int64_t rowstride = (int64_t)W * 4 * G;   // elements between input rows
@@ -475,7 +478,8 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
         const int64_t npix = a.N * a.OH * a.OW;
         if constexpr (sizeof(T) == 2) {
             const int64_t nowb = ceil_div(a.OW, kRowOut);
-            const int64_t total = a.N * a.OH * nowb * a.groups;
+            const int64_t nrb = a.N * a.OH * nowb, nkb = ceil_div(a.groups, 16);
+            const int64_t total = nkb * ceil_div(nrb, 4) * 64;   // threads, whole waves
             if (a.KH == 3 && a.KW == 3 && a.sw == 1 && a.dw == 1 &&
                 8 * ceil_div(ceil_div(total, kThreads), 8) * kThreads < (int64_t(1) << 31) &&
                 a.Cout * 9 * 4 < (int64_t(1) << 31)) {
@@ -484,7 +488,7 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
                 hipLaunchKernelGGL((conv2d_nhwc_g4k3_row<T>), dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0,
                                    a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
                                    (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.sh, a.ph, a.pw, a.dh,
-                                   (int)nowb, (int)total, (int)wgs, (int)per_xcd);
+                                   (int)nowb, (int)nrb, (int)nkb, (int)wgs, (int)per_xcd);
                 return hipGetLastError();
             }
         }
