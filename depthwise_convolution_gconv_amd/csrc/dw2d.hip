@@ -18,7 +18,7 @@
 //    padded planes, so a workgroup may span plane boundaries) go to LDS (fp32,
 //    or the raw 16 bits of 16-bit tensors), one row every WP elements, with
 //    16-byte buffer loads along W (out-of-range offsets read as zero, which
-//    supplies the padding rows).  The filters of the
+//    supplies the padding rows).  The filters and biases of the
 //    planes the workgroup touches go next to them.
 //  * Compute: each thread slides its run's window ((R-1)*S + K input columns,
 //    16-byte LDS reads) down the K filter rows, R fp32 accumulators, bias added
@@ -145,7 +145,7 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     const int R_lo = pa * g.Hp + (vr_a - pa * g.OH) * S;
     const int NR = pb * g.Hp + (vr_b - pb * g.OH) * S + K - R_lo;
     LT *xs = reinterpret_cast<LT *>(lds);                 // [NR][WP]
-    float *ws = reinterpret_cast<float *>(xs + g.NRmax * g.WP);   // [pb - pa + 1][K*K] (16-byte aligned)
+    float *ws = reinterpret_cast<float *>(xs + g.NRmax * g.WP);   // [pb - pa + 1][K*K + 1] (16-byte aligned)
 
     // Input plane read by output plane p: image n = p / Cout, channel (p % Cout) / M.
     auto in_plane = [&](int p) {
@@ -188,22 +188,24 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
         const int r = fdiv(i, g.fd_npad), c = i - r * g.npad;
         xs[r * g.WP + (c < g.pw ? c : c + g.W)] = LT(0);   // +0.0 in every storage type
     }
-    // Filters of output planes pa .. pb.
-    for (int i = tid; i < (pb - pa + 1) * KK; i += kThreads) {
-        const int p = pa + i / KK, t = i - (i / KK) * KK;
+    // Filters of output planes pa .. pb, each followed by the plane's bias (zero
+    // without one): read here from LDS, the bias costs no global load in the run
+    // loop, where a load would wait for the previous runs' stores.
+    for (int i = tid; i < (pb - pa + 1) * (KK + 1); i += kThreads) {
+        const int p = pa + i / (KK + 1), t = i - (i / (KK + 1)) * (KK + 1);
         const int o = p - fdiv(p, g.fd_cout) * g.Cout;
-        ws[i] = to_f32(w[(int64_t)o * KK + t]);
+        ws[i] = t < KK ? to_f32(w[(int64_t)o * KK + t]) : (bias ? to_f32(bias[o]) : 0.0f);
     }
     __syncthreads();
 
     for (int u = u0 + tid; u < u1; u += kThreads) {
         const int vr = fdiv(u, g.fd_rpr), rc = u - vr * g.RPR;
         const int p = fdiv(vr, g.fd_oh), oh = vr - p * g.OH;
-        const float b0 = bias ? to_f32(bias[p - fdiv(p, g.fd_cout) * g.Cout]) : 0.0f;
+        const float *wt = ws + (p - pa) * (KK + 1);
+        const float b0 = wt[KK];
         float acc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = b0;
-        const float *wt = ws + (p - pa) * KK;
         const LT *xrow = xs + (p * g.Hp + oh * S - R_lo) * g.WP + rc * (R * S);
 #pragma unroll
         for (int kh = 0; kh < K; ++kh) {
@@ -285,7 +287,7 @@ Plan make_plan(const Conv2dArgs &a)
         NR = std::min<int64_t>(NR, planes * Hp);
         const int64_t NP = std::min<int64_t>(crossings + 1, planes);
         *nr_out = NR;
-        return NR * WP * les + NP * K * K * (int64_t)sizeof(float);
+        return NR * WP * les + NP * (K * K + 1) * (int64_t)sizeof(float);
     };
     int64_t passes = 8, nr = 0;
     while (passes > 1 && lds_for(passes * kThreads, &nr) > kLdsTarget) --passes;

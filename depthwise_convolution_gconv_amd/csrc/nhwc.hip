@@ -86,6 +86,9 @@ dw2d_nhwc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     const int c0 = cb * kCT, c = c0 + lane;
     const int oh0 = th * Tile<K, S>::ROWS, ow0 = tw * TW;
     const int ih0 = oh0 * S - ph, iw0 = ow0 * S - pw;
+    // This channel's bias, loaded ahead of the staging from a valid address either
+    // way (a load after the staging would wait for it).
+    const float braw = to_f32(bias ? bias[min(c, C - 1)] : w[0]);
 
     // Filters [tap][channel] (zero past C).
     for (int i = tid; i < KK * kCT; i += kThreads) {
@@ -130,7 +133,7 @@ dw2d_nhwc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     __syncthreads();
 
     if (c >= C) return;
-    const float b0 = bias ? to_f32(bias[c]) : 0.0f;
+    const float b0 = bias ? braw : 0.0f;
 #pragma unroll
     for (int rr = 0; rr < RPW; ++rr) {
         const int lr = rg * RPW + rr, oh = oh0 + lr;   // row in the tile, output row
@@ -384,6 +387,13 @@ conv2d_nhwc_g4k3_row(const T *__restrict__ x, const T *__restrict__ w, const T *
 #pragma unroll
         for (int tp = 0; tp < 9; ++tp)
             wr[o][tp] = *reinterpret_cast<const uint2 *>(w + ((4 * k + o) * 9 + tp) * 4);
+    // The bias is read from a valid address either way (the filters when there is
+    // none) and issued with the other loads: a load under a branch would wait for
+    // every load before it.
+    const T *bp = bias ? bias + 4 * k : w + 4 * k;
+    uint16_t braw[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) braw[o] = __builtin_bit_cast(uint16_t, bp[o]);
     uint2 xr[3][kRowOut + 2];
 #pragma unroll
     for (int kh = 0; kh < 3; ++kh) {
@@ -399,7 +409,7 @@ conv2d_nhwc_g4k3_row(const T *__restrict__ x, const T *__restrict__ w, const T *
     }
     float b[4];
 #pragma unroll
-    for (int o = 0; o < 4; ++o) b[o] = bias ? to_f32(bias[4 * k + o]) : 0.0f;
+    for (int o = 0; o < 4; ++o) b[o] = bias ? to_f32(__builtin_bit_cast(T, braw[o])) : 0.0f;
     T *yrow = y + (((int64_t)n * OH + oh) * OW) * 4 * G + 4 * k;
 #pragma unroll
     for (int j = 0; j < kRowOut; ++j) {
