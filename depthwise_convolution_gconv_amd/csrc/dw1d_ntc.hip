@@ -169,6 +169,12 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
         const int i = tid + j * kThreads;
         RawLoad<16>::run(wrs, i < NWP ? (uint32_t)(((int64_t)c0 * K + (int64_t)i * WVE) * sizeof(T)) : kOOB, e[j]);
     }
+    // This thread's bias, with the filters: a buffer load of no records when there is
+    // no bias (it reads zero), so no branch, which would wait for every load before it.
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(bias ? bias : w), (short)0, bias ? (int)((int64_t)C * sizeof(T)) : 0, 0x00020000);
+    uint32_t bz[1];
+    RawLoad<sizeof(T)>::run(brs, (uint32_t)((c0 + lane) * sizeof(T)), bz);   // zero past channel C
     const int64_t xbase = (int64_t)bi * T_in * C;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
@@ -194,7 +200,7 @@ dw1d_btc_tile(const T *__restrict__ x, const T *__restrict__ w, const T *__restr
     for (int k = 0; k < K; ++k) wr[k] = ws[lane * K + (FLIP ? K - 1 - k : k)];
     const int c = c0 + lane;
     const bool cok = c < C;
-    const float b0 = (bias && cok) ? to_f32(bias[c]) : 0.0f;
+    const float b0 = elem_f32<T>(bz, 0);
     __syncthreads();   // every thread has its taps; the area now takes the inputs
 
 #pragma unroll
