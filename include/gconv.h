@@ -41,8 +41,9 @@
  *            (channels_last weight order), stride/pad/dilation = {h, w},
  *            y = {N,OH,OW,Cout}.  The implicit-GEMM route runs fp16/bf16 with C/g a
  *            multiple of 16, Cout/g a multiple of 4, the grouped output order, x
- *            and w 16-byte and y 8-byte aligned (its MFMA fragments load straight
- *            from x and w); otherwise GCONV_ERR_UNSUPPORTED when forced.
+ *            and w 16-byte and y 8-byte aligned (its 16-byte fragment loads need
+ *            whole, aligned 8-channel runs of x and w); otherwise
+ *            GCONV_ERR_UNSUPPORTED when forced.
  *    Output length per axis: floor((L + 2p - d*(K-1) - 1)/s) + 1.
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
