@@ -236,6 +236,10 @@ NHWC_IGEMM = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (1, 128, 64, 6, 7, 3, 3, 2, 1, 1, 1, True),       # 576 elements per filter: filters from global memory
     (1, 64, 64, 4, 300, 3, 3, 2, 1, 1, 1, True),      # 300-wide rows: input halo too large, filters in LDS
     (3, 64, 64, 5, 7, 3, 3, 2, 2, 1, 1, True),        # stride 2, tiles across several images
+    # Strips of several position tiles per workgroup (next tile's halo prefetched):
+    (1, 4096, 1024, 32, 32, 3, 3, 256, 1, 1, 1, True),   # 4 filters per group: unstaged stores
+    (1, 4096, 2048, 30, 30, 3, 3, 256, 1, 1, 1, True),   # 8 filters per group, ragged last tile
+    (2, 64, 384, 96, 96, 3, 3, 4, 1, 1, 1, True),        # 96 filters per group: two filter tiles
 ]
 
 
