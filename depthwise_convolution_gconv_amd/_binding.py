@@ -339,13 +339,18 @@ def gconv_dw1d_bwd_filter(x, dy, K: int, stride=1, pad=0, dilation=1, bias: bool
     if tuple(dw.shape) != w_shape or (db is not None and tuple(db.shape) != (C,)):
         raise GconvError(ERR_SHAPE, "dw must be [C,1,K] and db [C]")
     need = gconv_dw1d_bwd_filter_workspace(tuple(x.shape), w_shape, stride, pad, dilation, x.dtype)
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise GconvError(ERR_INVALID_ARG, "workspace must be a contiguous GPU tensor")
     s, p, d = _geom("ntc", stride, pad, dilation)
     with torch.cuda.device(x.device):
         st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        if own_ws and stream is not None:
+            # The kernels use the workspace on `stream`: the caching allocator must
+            # not hand its memory out again before that stream's work is done.
+            workspace.record_stream(st)
         _check(lib().gconv_dw1d_bwd_filter(_vp(x.data_ptr()), _arr(_i64, x.shape), _vp(dy.data_ptr()),
                                            _arr(_i64, w_shape), _vp(dw.data_ptr()),
                                            _vp(db.data_ptr() if db is not None else 0), s, p, d,
