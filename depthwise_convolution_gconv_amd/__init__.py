@@ -6,6 +6,7 @@ include/gconv.h); this package is its Python binding.  Importing the package
 does not load the library; the first call does, and raises if it is missing.
 """
 from ._binding import (  # noqa: F401
+    DW1D_BWD_FILTER_SCRATCH_BYTES,
     EXPORTS,
     GconvError,
     GconvLaunchError,
@@ -18,6 +19,7 @@ from ._binding import (  # noqa: F401
     gconv_autotune_clear,
     gconv_dw1d_bwd_data,
     gconv_dw1d_bwd_filter,
+    gconv_dw1d_bwd_filter_noalloc,
     gconv_dw1d_bwd_filter_workspace,
     gconv_fwd,
     gconv_fwd_ex,

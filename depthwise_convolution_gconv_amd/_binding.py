@@ -27,6 +27,7 @@ ORDERS = {"grouped": 0, "interleaved": 1}
 # Every symbol include/gconv.h declares.
 EXPORTS = ("gconv_out_shape", "gconv_select_route", "gconv_fwd", "gconv_fwd_route", "gconv_fwd_ex",
            "gconv_dw1d_bwd_data", "gconv_dw1d_bwd_filter_workspace", "gconv_dw1d_bwd_filter",
+           "gconv_dw1d_bwd_filter_noalloc",
            "gconv_autotune", "gconv_autotune_clear",
            "gconv_last_kernel", "gconv_status_string", "gconv_last_error")
 
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
         L.gconv_dw1d_bwd_filter.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _vp, _i32p, _i32p, _i32p, _i32,
                                             _vp, ctypes.c_size_t, _vp]
         L.gconv_dw1d_bwd_filter.restype = _i32
+        L.gconv_dw1d_bwd_filter_noalloc.argtypes = [_vp, _i64p, _vp, _i64p, _vp, _vp, _i32p, _i32p, _i32p, _i32,
+                                                    _vp]
+        L.gconv_dw1d_bwd_filter_noalloc.restype = _i32
         L.gconv_autotune.argtypes = conv + [_i32, _vp, _i32p]
         L.gconv_autotune.restype = _i32
         L.gconv_autotune_clear.argtypes = []
@@ -356,6 +360,36 @@ def gconv_dw1d_bwd_filter(x, dy, K: int, stride=1, pad=0, dilation=1, bias: bool
                                            _vp(db.data_ptr() if db is not None else 0), s, p, d,
                                            DTYPES[x.dtype], _vp(workspace.data_ptr()),
                                            workspace.numel() * workspace.element_size(), _vp(st.cuda_stream)))
+    return dw, db
+
+
+# Bytes of the library's own device scratch behind gconv_dw1d_bwd_filter_noalloc
+# (GCONV_DW1D_BWD_FILTER_SCRATCH_BYTES in gconv.h).
+DW1D_BWD_FILTER_SCRATCH_BYTES = 16 << 20
+
+
+def gconv_dw1d_bwd_filter_noalloc(x, dy, K: int, stride=1, pad=0, dilation=1, dw=None, db=None, bias: bool = True,
+                                  stream=None):
+    """gconv_dw1d_bwd_filter through the entry point that allocates nothing: the
+    partial sums go to the library's per-GPU scratch array.  dw (and db when
+    `bias`) must be passed in: this call allocates no tensor either.  Calls that
+    overlap on one GPU race.  Returns (dw, db or None)."""
+    _check_tensors(x, dy=dy, dw=dw, db=db)
+    if dw is None or (bias and db is None):
+        raise GconvError(ERR_INVALID_ARG, "dw (and db when bias=True) must be given")
+    B, T, C = x.shape
+    w_shape = (C, 1, int(K))
+    if tuple(dw.shape) != w_shape or (db is not None and tuple(db.shape) != (C,)):
+        raise GconvError(ERR_SHAPE, "dw must be [C,1,K] and db [C]")
+    if tuple(dy.shape[:1]) != (B,) or dy.dim() != 3 or dy.shape[2] != C:
+        raise GconvError(ERR_SHAPE, f"dy has shape {tuple(dy.shape)}, expected [{B}, To, {C}]")
+    s, p, d = _geom("ntc", stride, pad, dilation)
+    with torch.cuda.device(x.device):
+        st = stream if stream is not None else torch.cuda.current_stream(x.device)
+        _check(lib().gconv_dw1d_bwd_filter_noalloc(_vp(x.data_ptr()), _arr(_i64, x.shape), _vp(dy.data_ptr()),
+                                                   _arr(_i64, w_shape), _vp(dw.data_ptr()),
+                                                   _vp(db.data_ptr() if db is not None else 0), s, p, d,
+                                                   DTYPES[x.dtype], _vp(st.cuda_stream)))
     return dw, db
 
 

@@ -25,6 +25,8 @@ gconv_status_t fail(gconv_status_t s, const char *fmt, long long a = 0, long lon
 }
 
 constexpr int64_t kDimMax = std::numeric_limits<int32_t>::max();
+static_assert(GCONV_DW1D_BWD_FILTER_SCRATCH_BYTES == gconv::kWgradScratchBytes,
+              "the header states the scratch size the library holds");
 
 // Length of one output axis; < 1 means the window never fits.
 int64_t out_len(int64_t L, int64_t K, int64_t s, int64_t p, int64_t d)
@@ -512,6 +514,44 @@ gconv_status_t gconv_dw1d_bwd_filter(const void *x, const int64_t *x_shape, cons
         return fail(GCONV_ERR_INVALID_ARG, "dw, db, the workspace, x and dy must not overlap");
     const char *kname = "";
     const hipError_t err = gconv::launch_dw1d_bwd_filter(a, x, dy, dw, db, workspace, &kname);
+    if (err != hipSuccess)
+        return fail(GCONV_ERR_LAUNCH, "kernel launch failed: HIP error %lld", (long long)err);
+    g_last_kernel = kname;
+    return GCONV_OK;
+}
+
+gconv_status_t gconv_dw1d_bwd_filter_noalloc(const void *x, const int64_t *x_shape, const void *dy,
+                                             const int64_t *w_shape, void *dw, void *db, const int32_t *stride,
+                                             const int32_t *pad, const int32_t *dilation, gconv_dtype_t dtype,
+                                             void *hip_stream)
+{
+    g_last_error[0] = '\0';
+    Geometry g;
+    const gconv_status_t st = dw1d_geometry(x_shape, w_shape, stride, pad, dilation, dtype, &g);
+    if (st != GCONV_OK) return st;
+    const gconv::Dw1dArgs a = dw1d_args(g, nullptr, dtype, hip_stream);
+    size_t need = 0;
+    if (!gconv::dw1d_wgrad_plan(a, &need))
+        return fail(GCONV_ERR_UNSUPPORTED, "filter gradient: filter length above 64 or sizes beyond the "
+                    "library's index range");
+    if (need > gconv::kWgradScratchBytes)
+        return fail(GCONV_ERR_UNSUPPORTED, "filter gradient without allocation: this geometry needs %lld bytes "
+                    "of scratch, the library holds %lld (use gconv_dw1d_bwd_filter with a workspace)",
+                    (long long)need, (long long)gconv::kWgradScratchBytes);
+    if (!dw) return fail(GCONV_ERR_INVALID_ARG, "NULL dw pointer");
+    if (g.B > 0 && (!x || !dy)) return fail(GCONV_ERR_INVALID_ARG, "NULL x or dy pointer");
+    const size_t es = elem_size(dtype);
+    const size_t nx = es * (size_t)(g.B * g.T * g.C), ndy = es * (size_t)(g.B * g.To * g.C);
+    const size_t ndw = es * (size_t)(g.C * g.K), ndb = db ? es * (size_t)g.C : 0;
+    if (overlaps(dw, ndw, x, nx) || overlaps(dw, ndw, dy, ndy) || overlaps(dw, ndw, db, ndb) ||
+        overlaps(db, ndb, x, nx) || overlaps(db, ndb, dy, ndy))
+        return fail(GCONV_ERR_INVALID_ARG, "dw, db, x and dy must not overlap");
+    void *ws = nullptr;
+    hipError_t err = gconv::wgrad_scratch(&ws);
+    if (err != hipSuccess)
+        return fail(GCONV_ERR_LAUNCH, "device address of the scratch array: HIP error %lld", (long long)err);
+    const char *kname = "";
+    err = gconv::launch_dw1d_bwd_filter(a, x, dy, dw, db, ws, &kname);
     if (err != hipSuccess)
         return fail(GCONV_ERR_LAUNCH, "kernel launch failed: HIP error %lld", (long long)err);
     g_last_kernel = kname;

@@ -89,6 +89,11 @@ hipError_t launch_dw1d_bwd_data(const Dw1dArgs &a, const void *dy, void *dx, con
 bool dw1d_wgrad_plan(const Dw1dArgs &a, size_t *ws_bytes);
 hipError_t launch_dw1d_bwd_filter(const Dw1dArgs &a, const void *x, const void *dy, void *dw, void *db,
                                   void *ws, const char **kname);
+// Size of the library's own device scratch for the filter gradient (one copy per
+// GPU), and its device address on the current device (looked up once per device;
+// no allocation).
+constexpr size_t kWgradScratchBytes = size_t(16) << 20;
+hipError_t wgrad_scratch(void **addr);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

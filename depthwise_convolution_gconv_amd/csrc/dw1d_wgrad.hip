@@ -19,10 +19,19 @@
 //    the tiles are summed in order (16-byte loads of 4 channels), then combined
 //    in a fixed order and rounded once to the tensor dtype.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 
 namespace gconv {
+
+// Device scratch of gconv_dw1d_bwd_filter_noalloc (the per-tile partial sums),
+// for callers that cannot allocate.  Every GPU the library runs on holds its own
+// copy until the process ends; host code never passes this name to a kernel (in
+// host code it is only a stand-in), it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kWgradScratchBytes];
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -312,6 +321,29 @@ bool dw1d_wgrad_plan(const Dw1dArgs &a, size_t *ws_bytes)
     const Plan pl = make_plan(a);
     if (pl.ok) *ws_bytes = pl.ws_bytes;
     return pl.ok;
+}
+
+// Device address of `scratch` on the current device, looked up once per device
+// (each GPU holds the array at its own address).
+hipError_t wgrad_scratch(void **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_dw1d_bwd_filter(const Dw1dArgs &a, const void *x, const void *dy, void *dw, void *db,

@@ -48,9 +48,11 @@
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream)
  *    and the call returns without synchronising.
  *  - The library keeps no state between calls apart from a thread-local error
- *    string and the route cache of gconv_autotune (empty unless it is called),
- *    allocates no device memory and is safe to call from several host threads
- *    at once.
+ *    string, the route cache of gconv_autotune (empty unless it is called) and
+ *    the device scratch array of gconv_dw1d_bwd_filter_noalloc (static device
+ *    memory, one copy per GPU).  It allocates no device memory and is safe to
+ *    call from several host threads at once (gconv_dw1d_bwd_filter_noalloc
+ *    calls that overlap on one GPU excepted).
  *  - Errors: argument and shape errors are detected on the host before anything
  *    is enqueued, and leave y untouched.  A zero-sized batch (N == 0 or B == 0)
  *    is valid and enqueues nothing; x and y may then be NULL.  No C++ exception
@@ -180,6 +182,26 @@ gconv_status_t gconv_dw1d_bwd_filter(const void *x, const int64_t *x_shape, cons
                                      const int32_t *stride, const int32_t *pad,
                                      const int32_t *dilation, gconv_dtype_t dtype,
                                      void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* gconv_dw1d_bwd_filter for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the per-tile partial sums go to a scratch array the library holds in device
+ * memory, GCONV_DW1D_BWD_FILTER_SCRATCH_BYTES bytes per GPU, kept until the
+ * process ends (its device address is looked up once per device, on the first
+ * call there).  The call allocates nothing.  Arguments, results and errors are
+ * those of gconv_dw1d_bwd_filter without the workspace; a geometry whose
+ * gconv_dw1d_bwd_filter_workspace exceeds the scratch size is
+ * GCONV_ERR_UNSUPPORTED, checked before anything is enqueued.  Every call on one
+ * GPU uses that GPU's one array: calls whose work overlaps in time on the same
+ * GPU (other streams, other host threads) race and give wrong results; order
+ * them on one stream.  The array holds the last call's partial sums; nothing in
+ * it needs clearing (each call writes every entry it reads). */
+#define GCONV_DW1D_BWD_FILTER_SCRATCH_BYTES (16u << 20)
+gconv_status_t gconv_dw1d_bwd_filter_noalloc(const void *x, const int64_t *x_shape, const void *dy,
+                                             const int64_t *w_shape, void *dw, void *db,
+                                             const int32_t *stride, const int32_t *pad,
+                                             const int32_t *dilation, gconv_dtype_t dtype,
+                                             void *hip_stream);
 
 /* Order of the output channels.  The neon issue "Grouped convolutions" (ibmua's
  * reply on output ordering) names two: the usual group-contiguous order

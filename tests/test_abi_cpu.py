@@ -217,3 +217,26 @@ def test_unknown_output_order_is_rejected_before_launch():
                         B._vp(0), B._vp(1 << 24), s, p, d, 2, 0, 0, 0, 7, B._vp(0))
     assert rc == B.ERR_INVALID_ARG
     assert "order" in gc.gconv_last_error()
+
+
+def test_bwd_filter_noalloc_rejects_a_geometry_beyond_its_scratch_before_launch():
+    # 64 x 1024 steps in tiles of 64 need 1024 x 32 x 512 x 4 bytes of partial sums,
+    # more than the library's scratch array: rejected on the host (fake pointers).
+    L = B.lib()
+    need = gc.gconv_dw1d_bwd_filter_workspace((64, 1024, 512), (512, 1, 31), 1, 15, 1, "f32")
+    assert need > gc.DW1D_BWD_FILTER_SCRATCH_BYTES
+    s, p, d = B._geom("ntc", 1, 15, 1)
+    st = L.gconv_dw1d_bwd_filter_noalloc(B._vp(16), B._arr(B._i64, (64, 1024, 512)), B._vp(1 << 30),
+                                         B._arr(B._i64, (512, 1, 31)), B._vp(1 << 24), B._vp(0), s, p, d, 0,
+                                         B._vp(0))
+    assert st == B.ERR_UNSUPPORTED
+    assert "scratch" in gc.gconv_last_error()
+    # the Conformer shape fits
+    assert gc.gconv_dw1d_bwd_filter_workspace((8, 1024, 512), (512, 1, 31), 1, 15, 1, "f32") <= \
+        gc.DW1D_BWD_FILTER_SCRATCH_BYTES
+
+
+def test_header_states_the_noalloc_scratch_size():
+    text = open(os.path.join(ROOT, "include", "gconv.h")).read()
+    m = re.search(r"#define GCONV_DW1D_BWD_FILTER_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == gc.DW1D_BWD_FILTER_SCRATCH_BYTES
