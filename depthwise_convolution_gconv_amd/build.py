@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgconv.so")
 
-SOURCES = ["api.cpp", "direct2d.hip", "dw2d.hip", "dw1d_ntc.hip", "dw1d_wgrad.hip", "nhwc.hip", "igemm_nhwc.hip", "igemm.hip", "igemm_f32.hip"]
+SOURCES = ["api.cpp", "direct2d.hip", "dw2d.hip", "dw1d_ntc.hip", "dw1d_wgrad.hip", "nhwc.hip", "igemm_nhwc.hip", "igemm.hip", "igemm_rows.hip", "igemm_f32.hip"]
 HEADERS = ["common.hpp", "fastdiv.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

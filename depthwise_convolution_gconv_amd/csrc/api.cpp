@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI of libgconv: validation, output shape, route selection
 // and launch.  Everything here runs on the host; the arithmetic is in the HIP
-// kernels (direct2d.hip, dw2d.hip, dw1d_ntc.hip, igemm.hip, igemm_f32.hip).
+// kernels (direct2d.hip, dw2d.hip, dw1d_ntc.hip, dw1d_wgrad.hip, nhwc.hip,
+// igemm.hip, igemm_rows.hip, igemm_nhwc.hip, igemm_f32.hip).
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -244,7 +245,9 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
     } else if (nchw) {
         gconv::Conv2dArgs a = conv2d_args(g, x, w, bias, y, dtype, stream);
         a.interleaved = order == GCONV_ORDER_INTERLEAVED;
-        const bool igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
+        const bool rows_ok = dtype != GCONV_F32 && gconv::igemm_rows_supported(a);
+        const bool igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a)
+                                                 : rows_ok || gconv::igemm_supported(a);
         if (route == GCONV_ROUTE_AUTO) {
             gconv_route_t t;
             route = (tuned_route(g, dtype, &t) && (t != GCONV_ROUTE_IGEMM || igemm_ok)) ? t
@@ -255,7 +258,9 @@ gconv_status_t run(const void *x, const int64_t *x_shape, const void *w, const i
                 return fail(GCONV_ERR_UNSUPPORTED, "the implicit-GEMM route does not cover this geometry "
                             "(3x3 or 1x1 kernels, C/g a multiple of 8 (fp16/bf16) or 4 (fp32), halo tile "
                             "within LDS)");
-            err = dtype == GCONV_F32 ? gconv::launch_igemm_f32(a, &kname) : gconv::launch_igemm(a, &kname);
+            err = dtype == GCONV_F32 ? gconv::launch_igemm_f32(a, &kname)
+                  : rows_ok          ? gconv::launch_igemm_rows(a, &kname)
+                                     : gconv::launch_igemm(a, &kname);
         } else if (gconv::dw2d_supported(a)) {
             err = gconv::launch_dw2d(a, &kname);   // depthwise (C/g = 1), stride 1 or 2
         } else {
@@ -342,7 +347,8 @@ gconv_status_t gconv_select_route(const int64_t *x_shape, const int64_t *w_shape
     alignas(16) static const char dummy[16] = {0};
     if (layout == GCONV_LAYOUT_NCHW) {
         const gconv::Conv2dArgs a = conv2d_args(g, dummy, dummy, nullptr, nullptr, dtype, nullptr);
-        igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a) : gconv::igemm_supported(a);
+        igemm_ok = dtype == GCONV_F32 ? gconv::igemm_f32_supported(a)
+                                      : gconv::igemm_rows_supported(a) || gconv::igemm_supported(a);
     } else if (layout == GCONV_LAYOUT_NHWC) {
         igemm_ok = gconv::igemm_nhwc_supported(conv2d_args(g, dummy, dummy, nullptr, nullptr, dtype, nullptr));
     }

@@ -81,6 +81,8 @@ hipError_t launch_igemm_nhwc(const Conv2dArgs &a, const char **kname);          
 hipError_t launch_dw2d(const Conv2dArgs &a, const char **kname);
 bool igemm_supported(const Conv2dArgs &a);            // fp16 / bf16
 hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);
+bool igemm_rows_supported(const Conv2dArgs &a);       // fp16 / bf16, 3x3, unit column stride and dilation
+hipError_t launch_igemm_rows(const Conv2dArgs &a, const char **kname);
 bool igemm_f32_supported(const Conv2dArgs &a);        // fp32
 hipError_t launch_igemm_f32(const Conv2dArgs &a, const char **kname);
 hipError_t launch_dw1d(const Dw1dArgs &a, const char **kname);

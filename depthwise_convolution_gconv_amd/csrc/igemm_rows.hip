@@ -1,0 +1,703 @@
+// igemm_rows.hip -- implicit-GEMM grouped conv2d (NCHW, 3x3 filters, unit column
+// stride and dilation) on the gfx950 matrix cores, each lane owning a run of 8
+// consecutive output columns.
+//
+// Per group k the convolution is the product
+//     Y_k[o][m] = sum_kk W_k[o][kk] * A_k[kk][m],   kk = (input channel, tap),
+// over the output positions m of the group's Cout/g filters, A_k being the im2col
+// matrix of the group's input channels.  The discuss.pytorch.org thread "F.conv2d
+// runs x15 slower in mixed-precision/half-precision mode" traces the slow fp16
+// grouped conv to grouped convs not reaching the tensor cores; here every group's
+// contraction runs on v_mfma_f32_32x32x16_{f16,bf16} and A_k is never written out
+// (the neon issue "Grouped convolutions" on explicit im2col being wasteful).
+//
+// Runs.  Each output row is cut into runs of 8 consecutive columns (the last run
+// of a row may be partial).  In a wave, lane l32 (and its partner l32 + 32, which
+// holds the other 8 channels of each K step) owns one run, and MFMA block mb
+// (mb < 8) computes column mb of every run.  v_mfma_f32_32x32x16 leaves lane l32
+// with column l32 of the 32 filter rows of a block, so after the K loop a lane
+// holds 8 consecutive outputs of each of its filters: one 16-byte store per filter
+// straight from the accumulators, 512 contiguous bytes per half-wave.  For filter
+// row kh the B operands of the taps kw = 0, 1, 2 of block mb are the input columns
+// ow0 + mb + kw of one halo row: a window of 10 positions x 8 channels (10 16-byte
+// LDS reads) feeds all 24 B operands of the filter row.
+//
+// Tile: 4 waves.  FW (1 or 2) waves across the filters, 64 each (2 blocks of 32),
+// and 4/FW across the runs, 32 each: 128 runs x 64 filters, or 64 runs x 128
+// filters of one group.  Every wave issues 16 MFMAs per K step.
+//
+// K loop: chunks of 16 input channels, then the 9 taps; one MFMA step = one tap x
+// 16 channels.  While chunk c computes, chunk c+1 is staged into the other LDS
+// stage:
+//  * input: a zero-padded halo of whole input rows, [row][column][16 channels], so
+//    that one B fragment (8 channels of one position) is one 16-byte read; loaded 8
+//    channel rows x VW columns per task and transposed in registers with v_perm;
+//  * filters: the chunk of a 32-filter block is 32 runs of 16 channels x 9 taps (288
+//    contiguous bytes of w each).  One wave copies them straight into LDS (buffer
+//    loads with an LDS destination, 16 bytes per lane) and transposes them in place:
+//    each lane reads one filter's 8 channels x 9 taps (9 16-byte reads at a 144-byte
+//    lane stride, free of bank conflicts), forms the 9 units of 8 channels at one tap
+//    with v_perm, and writes them back where the A operand reads expect them.  Each
+//    wave only touches its own block's bytes, so no barrier is needed between the
+//    copy and the transpose.
+// The halo and filter images live in separate LDS arrays, so the compiler waits for
+// the LDS-destination loads only before the filter reads, not before every read.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+#include "fastdiv.hpp"
+
+namespace gconv {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#define GCONV_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+constexpr int kThreads = 256;
+constexpr int kLdsUnits = 160 * 1024 / 16;   // 16-byte units of LDS per workgroup (one per CU)
+constexpr int kBlockUnits = 576;             // one 32-filter block's chunk: 32 x 16 ch x 9 taps x 2 B
+constexpr int kSubUnits = 288;               // one 16-filter half of it
+constexpr int kRun = 8;                      // output columns per run
+constexpr int kWin = kRun + 2;               // window positions of one filter row (3 taps)
+constexpr uint32_t kOOB = 0x80000000u;       // byte offset past num_records: loads return 0
+
+template <int FW> constexpr int kFU = 2 * FW * kBlockUnits;              // filter units per stage
+template <int FW> constexpr int kHU = (kLdsUnits - 2 * kFU<FW>) / 2;     // halo units per stage
+
+template <typename T> struct Mfma;
+template <> struct Mfma<_Float16> {
+    static __device__ __forceinline__ f32x16 run(uint4 a, uint4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<__bf16> {
+    static __device__ __forceinline__ f32x16 run(uint4 a, uint4 b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <typename T> __device__ __forceinline__ float half_to_f32(uint32_t hbits);
+template <> __device__ __forceinline__ float half_to_f32<_Float16>(uint32_t hbits)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)hbits);
+}
+template <> __device__ __forceinline__ float half_to_f32<__bf16>(uint32_t hbits)
+{
+    return __builtin_bit_cast(float, hbits << 16);
+}
+// Two fp32 values rounded to nearest even into one dword of T (a in the low half).
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
+}
+template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+}
+
+// One accumulator copied out of its accumulation register at this point of the
+// program (otherwise the allocator moves all of them into VGPRs at once).
+__device__ __forceinline__ float acc_read(float v)
+{
+    float r;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+    return r;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Halo map: 16-byte half `hf` (channels 0-7 or 8-15) of the 32-byte slot s, with one
+// spare unit after every 8 slots.  Slots 8 apart are 17 units apart, so the 16 lanes
+// of a half-wave reading the same window position of 16 runs hit 16 different
+// units modulo 16: no bank conflicts when the runs lie on one row.
+__device__ __forceinline__ int halo_unit(int s, int hf) { return 2 * s + hf + (s >> 3); }
+__host__ __device__ inline int halo_units(int slots) { return 2 * slots + slots / 8; }
+
+// Filter image: per 16-filter half-block, per tap, 32 units; filter f (< 16) and
+// channel half hh at unit 2f + (hh ^ bit 3 of f).  The A-operand read (16 lanes on
+// 16 consecutive filters, one channel half) and the transposing write (16 lanes on
+// 8 filters x 2 halves) both hit 16 different units modulo 16.
+__device__ __forceinline__ int fimg_unit(int f, int hh) { return 2 * f + (hh ^ ((f >> 3) & 1)); }
+
+// VW consecutive 16-bit elements of one input row, as VW/2 dwords.
+template <int VW> struct VecLoad;
+template <> struct VecLoad<8> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, uint32_t *d)
+    {
+        const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
+        d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
+    }
+};
+template <> struct VecLoad<4> {
+    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, uint32_t *d)
+    {
+        const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
+        d[0] = u.x; d[1] = u.y;
+    }
+};
+
+// Dword of element v of row ra (low half) and element v of row rb (high half); each
+// row holds VW 16-bit elements in VW/2 dwords.
+template <int v>
+__device__ __forceinline__ uint32_t col_pair(const uint32_t *ra, const uint32_t *rb)
+{
+    constexpr uint32_t b = 2 * (v & 1);
+    constexpr uint32_t sel = ((b + 5) << 24) | ((b + 4) << 16) | ((b + 1) << 8) | b;
+    return __builtin_amdgcn_perm(rb[v >> 1], ra[v >> 1], sel);
+}
+
+// Column v of 8 channel rows d[0..7] as one 16-byte unit of 8 channels, written to
+// halo slot slot0 + v, half oct.
+template <int VW, int DW, int v>
+__device__ __forceinline__ void write_octets(uint4 *hs, int slot0, int oct, const uint32_t (*d)[DW])
+{
+    hs[halo_unit(slot0 + v, oct)] = make_uint4(col_pair<v>(d[0], d[1]), col_pair<v>(d[2], d[3]),
+                                               col_pair<v>(d[4], d[5]), col_pair<v>(d[6], d[7]));
+    if constexpr (v + 1 < VW) write_octets<VW, DW, v + 1>(hs, slot0, oct, d);
+}
+
+struct RowsGeom {
+    int N, C, H, W, Cout, Cg, Ng, OH, OW;
+    int sh, ph, pw, dh;
+    int Hp;                  // H + 2*ph: rows of one zero-padded image in the virtual row space
+    int RPR, NRUN;           // runs per output row; N*OH*RPR runs in all (< 2^31)
+    int NR, SROW;            // halo rows; slots per halo row (a multiple of 8)
+    int kh_units;            // unit step of one filter row in the halo: 17 * dh * SROW / 8
+    int nseg, xtasks;        // VW-wide segments per input row; staging tasks = 2*NR*nseg
+    int npad;                // halo columns of a row outside the image: [0, pw) and [pw + W, SROW)
+    int m_tiles, n_tiles, groups, nchunks, tiles, tiles_per_xcd;
+    int sg;                  // output store width in elements: 8 (16 bytes), 4 (8 bytes) or 1
+    int ocs, okg;            // channel of filter j of group k: j*ocs + k*okg
+    uint32_t w_bytes, b_bytes;
+    FastDiv fd_oh, fd_rpr, fd_hp, fd_nseg, fd_nr, fd_mt, fd_nt;
+};
+
+template <typename T, int FW, int XR, int VW, bool SG8>
+__global__ void __launch_bounds__(kThreads, 1)
+igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+               T *__restrict__ y, RowsGeom g)
+{
+    constexpr int BN = 64 * FW;              // filters per tile
+    constexpr int PW = 4 / FW;               // waves across the runs
+    constexpr int RT = 32 * PW;              // runs per tile
+    constexpr int DW = VW / 2;               // dwords per staged row segment
+    constexpr int NTW = BN / 32;             // waves that stage a 32-filter block each
+    constexpr int FU = kFU<FW>;
+    constexpr int HU = kHU<FW>;
+    // Input halo and filter image, two pipeline stages each, as four LDS arrays: the
+    // compiler tracks LDS-destination loads per array, and with the stage known at
+    // compile time in each copy of the chunk body, reads of the current stage never
+    // wait for the copies into the next one.
+    __shared__ uint4 hal0[HU], hal1[HU];
+    __shared__ uint4 fim0[FU], fim1[FU];
+    auto hal = [&](auto st) -> uint4 * {
+        if constexpr (decltype(st)::value == 0) return hal0; else return hal1;
+    };
+    auto fim = [&](auto st) -> uint4 * {
+        if constexpr (decltype(st)::value == 0) return fim0; else return fim1;
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hf = lane >> 5, l32 = lane & 31;
+    const int pwv = wave / FW, fwv = wave % FW;
+    const int OHW = g.OH * g.OW;
+    const int HW = g.H * g.W;
+
+    // Persistent tile walk: workgroup b runs on XCD b % 8, which owns a contiguous
+    // range of tiles; its workgroups walk the range together, so the tiles in flight
+    // on one XCD are neighbours sharing halo rows and filters in its L2.
+    const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+    const int nbx = ((int)gridDim.x - xcd + 7) >> 3;
+    const int t_lo = xcd * g.tiles_per_xcd;
+    const int t_hi = min(t_lo + g.tiles_per_xcd, g.tiles);
+    int tile = t_lo + rank;
+    if (tile >= t_hi) return;   // uniform over the workgroup
+
+    // Input staging tasks (channel octet, halo row, VW-wide segment); task i of this
+    // thread is tid + i*256.
+    int xrr[XR], xoct[XR], xslot0[XR], xcol[XR];
+    bool xtask[XR];
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+        const int tk = tid + i * kThreads;
+        xtask[i] = tk < g.xtasks;
+        xrr[i] = xoct[i] = xslot0[i] = xcol[i] = 0;
+        if (xtask[i]) {
+            const int rest = fdiv(tk, g.fd_nseg);
+            const int sgm = fmod_q(tk, rest, g.fd_nseg);
+            xoct[i] = fdiv(rest, g.fd_nr);
+            xrr[i] = fmod_q(rest, xoct[i], g.fd_nr);
+            xcol[i] = sgm * VW;
+            xslot0[i] = xrr[i] * g.SROW + g.pw + xcol[i];
+        }
+    }
+    // Transpose: lane = (filter tf, channel half th) of the wave's block.
+    const int tf = lane >> 1, th = lane & 1;
+    const int traw = 18 * tf + 9 * th;                                    // first raw unit
+    const int tdst = (tf >> 4) * kSubUnits + fimg_unit(tf & 15, th);      // tap-0 unit
+    // A operand: filter fwv*64 + nb*32 + l32, channel half hf, tap t at
+    // aub + nb*576 + t*32.
+    const int aub = (fwv * 4 + (l32 >> 4)) * kSubUnits + fimg_unit(l32 & 15, hf);
+
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, g.w_bytes);
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(bias, g.b_bytes);
+
+    struct TileState {
+        int k, nt, run0, R_lo, n_first;
+        int fbase;   // w row of this wave's first staged filter (k*Ng + nt*BN + 32*wave)
+        int nfw;     // filters of this wave's staged block that exist
+        __amdgpu_buffer_rsrc_t xr;
+        uint32_t xvo[XR];
+    };
+    auto tile_state = [&](int t) {
+        TileState s;
+        const int bq = fdiv(t, g.fd_mt);
+        const int mt = fmod_q(t, bq, g.fd_mt);
+        s.k = fdiv(bq, g.fd_nt);
+        s.nt = fmod_q(bq, s.k, g.fd_nt);
+        s.run0 = mt * RT;
+        const int Rf = fdiv(s.run0, g.fd_rpr);          // first output row (n*OH + oh)
+        s.n_first = fdiv(Rf, g.fd_oh);
+        const int oh_first = fmod_q(Rf, s.n_first, g.fd_oh);
+        s.R_lo = s.n_first * g.Hp + oh_first * g.sh;
+        s.fbase = s.k * g.Ng + s.nt * BN + 32 * wave;
+        s.nfw = min(32, max(0, g.Ng - s.nt * BN - 32 * wave));
+        s.xr = make_rsrc(x + ((int64_t)s.n_first * g.C + (int64_t)s.k * g.Cg) * HW, 0x7fffffffu);
+#pragma unroll
+        for (int i = 0; i < XR; ++i) {
+            s.xvo[i] = kOOB;
+            if (xtask[i]) {
+                const int R = s.R_lo + xrr[i];
+                const int n = fdiv(R, g.fd_hp);
+                const int ih = fmod_q(R, n, g.fd_hp) - g.ph;
+                if (n < g.N && ih >= 0 && ih < g.H)
+                    s.xvo[i] = (uint32_t)((((int64_t)(n - s.n_first) * g.C + 8 * xoct[i]) * HW +
+                                           (int64_t)ih * g.W + xcol[i]) * 2);
+            }
+        }
+        return s;
+    };
+
+    uint32_t d[XR][8][DW];   // staged input rows of the next step
+    uint32_t E[36];          // a filter run being transposed: 8 channels x 9 taps
+    // Filter copy instruction i (< 9) of one pipeline step (tile s, chunk ch) into
+    // stage stg, by a staging wave: pieces 64i + lane of the wave's block, piece q
+    // being bytes 16*(q % 18) of filter q / 18's 288-byte run.
+    auto filter_copy = [&](const TileState &s, int ch, auto stg, bool any, int i) {
+        const int c0 = ch * 16;
+        const int q = 64 * i + lane;
+        const int pf = (q * 3641) >> 16;    // q / 18 for q < 576
+        const int pj = q - 18 * pf;
+        const bool ok = any && pf < s.nfw && (pj < 9 || c0 + 8 < g.Cg);   // channels 8-15 exist
+        const uint32_t off = ok ? (uint32_t)(((s.fbase + pf) * g.Cg + c0) * 18 + 16 * pj) : kOOB;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, GCONV_LDS(fim(stg) + kBlockUnits * wave + 64 * i), 16, off,
+                                                 0, 0, 0);
+    };
+    // Input load j (< 8*XR) of one pipeline step into registers: task j/8, channel row j%8.
+    auto input_load = [&](const TileState &s, int ch, bool any, int j) {
+        const int r = j >> 3, e = j & 7;
+        const int c0 = ch * 16;
+        const bool ok = any && xtask[r] && c0 + 8 * xoct[r] + e < g.Cg;
+        VecLoad<VW>::run(s.xr, ok ? s.xvo[r] : kOOB, (uint32_t)(c0 + e) * HW * 2, d[r][e]);
+    };
+    // Transpose of this wave's block in stage stg, in place: read u (< 9) brings raw
+    // unit u of the lane's run (8 channels x 9 taps); write t (< 9) forms the unit of
+    // the 8 channels at tap t.  Every read of the wave comes before its first write
+    // (the writes land on units other lanes read).
+    auto transpose_read = [&](auto stg, int u) {
+        const uint4 v = fim(stg)[kBlockUnits * wave + traw + u];
+        E[4 * u] = v.x; E[4 * u + 1] = v.y; E[4 * u + 2] = v.z; E[4 * u + 3] = v.w;
+    };
+    auto transpose_write = [&](auto stg, int t) {
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // channels 2q, 2q+1 at tap t: elements 18q + t and 18q + 9 + t of the run
+            const int e0 = 18 * q + t, e1 = e0 + 9;
+            const uint32_t a = 2 * (e0 & 1), b = 4 + 2 * (e1 & 1);
+            const uint32_t sel = ((b + 1) << 24) | (b << 16) | ((a + 1) << 8) | a;
+            o[q] = __builtin_amdgcn_perm(E[e1 >> 1], E[e0 >> 1], sel);
+        }
+        fim(stg)[kBlockUnits * wave + tdst + 32 * t] = make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    // Staging write o (< XR*VW) into stage stg: column o % VW of task o / VW as one
+    // unit of 8 channels; a thread without that task writes the spare unit.
+    auto input_write = [&](auto stg, int o) {
+        const int r = o / VW, v = o % VW;
+        const uint32_t *ra = d[r][0], *rb = d[r][1], *rc = d[r][2], *rd = d[r][3];
+        const uint32_t *re = d[r][4], *rf = d[r][5], *rg = d[r][6], *rh = d[r][7];
+        const uint32_t bsel = 2 * (v & 1);
+        const uint32_t sel = ((bsel + 5) << 24) | ((bsel + 4) << 16) | ((bsel + 1) << 8) | bsel;
+        const int w2 = v >> 1;
+        const uint4 val = make_uint4(__builtin_amdgcn_perm(rb[w2], ra[w2], sel), __builtin_amdgcn_perm(rd[w2], rc[w2], sel),
+                                     __builtin_amdgcn_perm(rf[w2], re[w2], sel), __builtin_amdgcn_perm(rh[w2], rg[w2], sel));
+        const int unit = xtask[r] ? halo_unit(xslot0[r] + v, xoct[r]) : HU - 1;
+        hal(stg)[unit] = val;
+    };
+
+    // Halo columns outside the image are zero in both stages for the whole kernel
+    // (staging writes only columns [pw, pw + W)).
+    for (int j = tid; j < g.NR * g.npad; j += kThreads) {
+        const int row = j / g.npad, pc = j - row * g.npad;
+        const int col = pc < g.pw ? pc : pc - g.pw + g.pw + g.W;
+        const int s = row * g.SROW + col;
+        hal0[halo_unit(s, 0)] = make_uint4(0, 0, 0, 0);
+        hal0[halo_unit(s, 1)] = make_uint4(0, 0, 0, 0);
+        hal1[halo_unit(s, 0)] = make_uint4(0, 0, 0, 0);
+        hal1[halo_unit(s, 1)] = make_uint4(0, 0, 0, 0);
+    }
+
+    TileState ts = tile_state(tile);
+    if (NTW == 4 || wave < NTW) {
+#pragma unroll
+        for (int i = 0; i < 9; ++i) filter_copy(ts, 0, S0{}, true, i);
+    }
+#pragma unroll
+    for (int j = 0; j < 8 * XR; ++j) input_load(ts, 0, true, j);
+    if (NTW == 4 || wave < NTW) {
+#pragma unroll
+        for (int u = 0; u < 9; ++u) transpose_read(S0{}, u);
+#pragma unroll
+        for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
+#pragma unroll
+        for (int t = 0; t < 9; ++t) transpose_write(S0{}, t);
+    }
+#pragma unroll
+    for (int o = 0; o < XR * VW; ++o) input_write(S0{}, o);
+    __syncthreads();
+
+    for (;;) {
+        // This lane's run and its halo and output addresses.
+        const int run = ts.run0 + pwv * 32 + l32;
+        const bool run_ok = run < g.NRUN;
+        const int rc = min(run, g.NRUN - 1);
+        const int R = fdiv(rc, g.fd_rpr);
+        const int jr = fmod_q(rc, R, g.fd_rpr);
+        const int n = fdiv(R, g.fd_oh);
+        const int oh = fmod_q(R, n, g.fd_oh);
+        const int ow0 = kRun * jr;
+        const int ub = 17 * (((n * g.Hp + oh * g.sh - ts.R_lo) * g.SROW + ow0) >> 3) + hf;
+
+        f32x16 acc[2][8];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[nb][mb][r] = 0.0f;
+
+        const int next_tile = tile + nbx;
+        const bool has_next = next_tile < t_hi;
+        TileState nts = ts;
+        // One chunk: computes from stage CUR and stages the next pipeline step into
+        // the other one (instantiated once per stage, so every LDS array is named
+        // statically).
+        auto chunk = [&](auto cur, int ch) {
+            using CUR = decltype(cur);
+            using NXT = std::integral_constant<int, 1 - CUR::value>;
+            const NXT nst{};
+            const bool last = ch + 1 == g.nchunks;
+            if (last && has_next) nts = tile_state(next_tile);
+            // Next pipeline step: chunk ch+1 of this tile, or chunk 0 of the next tile.
+            const TileState src = last ? nts : ts;
+            const int nch = last ? 0 : ch + 1;
+            const bool more = !last || has_next;
+
+            const uint4 *hs = hal(cur);
+            const uint4 *fs = fim(cur);
+            uint4 win[kWin], af[2][2];
+            // First the operands of the first MFMAs, then the rest of the window.
+            af[0][0] = fs[aub];
+            win[0] = hs[ub];
+            af[0][1] = fs[aub + kBlockUnits];
+#pragma unroll
+            for (int e = 1; e < kWin; ++e) win[e] = hs[ub + 2 * e + (e >> 3)];
+            __builtin_amdgcn_sched_barrier(0);
+            // The chunk as 9 taps x 16 slots; slot i of tap t is MFMA i (block mb =
+            // i / 2, nb = i % 2) followed by its share of the staging work, in this
+            // order (the scheduling barriers keep it):
+            //  * slots 0-1: the next tap's A operands;
+            //  * the window of the next filter row, each position read into its register
+            //    right after the MFMA that last uses it in this row (position 0 after
+            //    tap kw = 0, position 1 after kw = 1, position 2 + mb after block mb of
+            //    kw = 2), at least 16 MFMAs before its first use;
+            //  * taps 0-4 from slot 3 on: the global loads of the next pipeline step,
+            //    one every 4 (or 3) slots: the input rows, then the filter copies;
+            //  * tap 5: the transpose reads; taps 6-8: its 9 unit writes (every fourth
+            //    slot) and the input staging writes (odd slots).
+            constexpr int NVM = (NTW == 4 ? 9 : 0) + 8 * XR;   // global loads per step
+#pragma unroll
+            for (int t = 0; t < 9; ++t) {
+                const int kh = t / 3, kw = t % 3;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int mb = i >> 1, nb = i & 1;
+                    acc[nb][mb] = Mfma<T>::run(af[t & 1][nb], win[mb + kw], acc[nb][mb]);
+                    if (i < 2 && t < 8) af[(t + 1) & 1][i] = fs[aub + i * kBlockUnits + 32 * (t + 1)];
+                    if (kh < 2 && nb == 1 && (kw == 2 || mb == 0)) {
+                        const int e = mb + kw;   // its last use in this row was this MFMA
+                        win[e] = hs[ub + (kh + 1) * g.kh_units + 2 * e + (e >> 3)];
+                    }
+                    // Global loads: the input rows first, then the filter copies, one
+                    // every OS slots from slot 3 of tap 0 on (taps 0-4).
+                    constexpr int OS = NVM <= 17 ? 4 : 3;
+                    const int sl = 16 * t + i - 3;
+                    if (sl >= 0 && sl % OS == 0 && sl / OS < NVM) {
+                        const int o = sl / OS;
+                        if (o < 8 * XR) input_load(src, nch, more, o);
+                        else if (NTW == 4) filter_copy(src, nch, nst, more, o - 8 * XR);
+                    }
+                    if (NTW == 4) {
+                        if (t == 5 && i >= 1 && i <= 9) transpose_read(nst, i - 1);
+                        if (t == 6 && i == 0) {
+                            // every transpose read has returned before the first write
+#pragma unroll
+                            for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
+                        }
+                        if (((t == 6 || t == 7) && i % 4 == 0) || (t == 8 && i == 0))
+                            transpose_write(nst, (t - 6) * 4 + i / 4);
+                    }
+                    if (t >= 6 && (i & 1) == 1) {
+                        const int ow = (t - 6) * 8 + i / 2;
+                        if (ow < XR * VW) input_write(nst, ow);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if (NTW != 4) {
+                // Fewer staging waves than waves: the filter copy and its transpose are
+                // done by waves 0 .. NTW-1 outside the scheduled taps.
+                if (wave < NTW) {
+#pragma unroll
+                    for (int i = 0; i < 9; ++i) filter_copy(src, nch, nst, more, i);
+#pragma unroll
+                    for (int u = 0; u < 9; ++u) transpose_read(nst, u);
+#pragma unroll
+                    for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
+#pragma unroll
+                    for (int tt = 0; tt < 9; ++tt) transpose_write(nst, tt);
+                }
+            }
+            __syncthreads();
+        };
+        // An even number of chunks (planned), so every tile starts on stage 0.
+        for (int ch = 0; ch < g.nchunks; ch += 2) {
+            chunk(S0{}, ch);
+            chunk(S1{}, ch + 1);
+        }
+
+        // Epilogue: + bias in fp32, one rounding to T, stored straight from the
+        // accumulators: 8 consecutive outputs of one filter per lane and row.
+        if (run_ok) {
+            // Filters this lane's rows cover: the wave's 64 from fb0, those below Ng.
+            const int fb0 = ts.nt * BN + fwv * 64;
+            // The output addresses are formed here, not hoisted to the tile start where
+            // they would hold registers through the K loop.
+            int ybase = oh * g.OW + ow0;
+            int64_t fstep = (int64_t)g.ocs * OHW;   // between consecutive filters
+            asm volatile("" : "+v"(ybase), "+s"(fstep));
+            T *yrow = y + ((int64_t)n * g.Cout + (int64_t)fb0 * g.ocs + (int64_t)ts.k * g.okg) * OHW + ybase;
+            auto store_rows = [&](auto has_bias) {
+                uint2 bz[2][4];
+                if constexpr (decltype(has_bias)::value) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int on = fb0 + nb * 32 + 8 * q + 4 * hf;
+                            const uint32_t off = on < g.Ng ? (uint32_t)((ts.k * g.Ng + on) * 2) : kOOB;
+                            bz[nb][q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(br, off, 0, 0));
+                        }
+                }
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = nb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+                        if (fb0 + row >= g.Ng) continue;
+                        float v[8];
+#pragma unroll
+                        for (int mb = 0; mb < 8; ++mb) v[mb] = acc_read(acc[nb][mb][r]);
+                        if constexpr (decltype(has_bias)::value) {
+                            const uint32_t dwd = (r & 2) ? bz[nb][r >> 2].y : bz[nb][r >> 2].x;
+                            const float b0 = half_to_f32<T>((r & 1) ? (dwd >> 16) : (dwd & 0xffffu));
+#pragma unroll
+                            for (int mb = 0; mb < 8; ++mb) v[mb] += b0;
+                        }
+                        T *yp = yrow + row * fstep;
+                        if constexpr (SG8) {
+                            store_nt(reinterpret_cast<uint4 *>(yp),
+                                     make_uint4(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]), pack2<T>(v[4], v[5]),
+                                                pack2<T>(v[6], v[7])));
+                        } else if (g.sg == 4) {
+                            store_nt(reinterpret_cast<uint2 *>(yp), make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3])));
+                            if (ow0 + 4 < g.OW)
+                                store_nt(reinterpret_cast<uint2 *>(yp + 4),
+                                         make_uint2(pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7])));
+                        } else {
+#pragma unroll
+                            for (int mb = 0; mb < 8; ++mb)
+                                if (ow0 + mb < g.OW) yp[mb] = from_f32<T>(v[mb]);
+                        }
+                    }
+            };
+            if (bias)
+                store_rows(std::true_type{});
+            else
+                store_rows(std::false_type{});
+        }
+        if (!has_next) break;
+        tile = next_tile;
+        ts = nts;
+    }
+}
+
+struct RowsPlan {
+    RowsGeom g;
+    int FW, XR, VW;
+    bool ok;
+};
+
+RowsPlan make_rows_plan(const Conv2dArgs &a)
+{
+    RowsPlan pl{};
+    pl.ok = false;
+    if (a.dtype != DT_F16 && a.dtype != DT_BF16) return pl;
+    if (a.KH != 3 || a.KW != 3 || a.sw != 1 || a.dw != 1) return pl;
+    RowsGeom &g = pl.g;
+    g.N = (int)a.N; g.C = (int)a.C; g.H = (int)a.H; g.W = (int)a.W; g.Cout = (int)a.Cout;
+    g.Cg = (int)(a.C / a.groups); g.Ng = (int)(a.Cout / a.groups);
+    g.OH = (int)a.OH; g.OW = (int)a.OW;
+    g.sh = a.sh; g.ph = a.ph; g.pw = a.pw; g.dh = a.dh;
+    g.groups = (int)a.groups;
+    // Filters: a chunk of one filter is 16 channels x 9 taps = 288 contiguous bytes,
+    // copied in 16-byte pieces (C/g a multiple of 8 keeps every piece aligned).
+    if (g.Cg % 8 != 0 || (reinterpret_cast<uintptr_t>(a.w) & 15) != 0) return pl;
+    const int64_t w_bytes = a.Cout * (int64_t)g.Cg * 18;
+    if (w_bytes >= (int64_t(1) << 31)) return pl;
+    g.w_bytes = (uint32_t)w_bytes;
+    g.b_bytes = 0;
+    if (a.bias) {
+        if (g.Ng % 4 != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 7) != 0) return pl;
+        g.b_bytes = (uint32_t)(a.Cout * 2);
+    }
+    // 64 filters per wave and two waves across the filters.  (With at most 64 filters
+    // per group the filter copy would be done by 2 of the 4 waves outside the
+    // scheduled taps; such layers stay on the implicit GEMM of igemm.hip.)
+    if (g.Ng <= 64) return pl;
+    pl.FW = 2;
+    const int RT = 32 * (4 / pl.FW);
+    g.Hp = (int)(a.H + 2 * a.ph);
+    g.RPR = (int)ceil_div(a.OW, 8);
+    const int64_t NRUN = a.N * a.OH * (int64_t)g.RPR;
+    if (NRUN >= (int64_t(1) << 31) - 2 * RT || a.N * (int64_t)g.Hp + 3 * (int64_t)a.dh + 1024 >= (int64_t(1) << 31))
+        return pl;
+    g.NRUN = (int)NRUN;
+    // Output rows a tile's RT runs can touch, image boundaries among them, and the
+    // resulting bound on the padded input rows of its halo.
+    const bool aligned = g.RPR <= RT && RT % g.RPR == 0;
+    const int64_t V = aligned ? RT / g.RPR : (RT - 1) / g.RPR + 2;
+    const int64_t crossings = V <= 1 ? 0 : (aligned && g.OH % V == 0) ? 0 : (V - 2) / g.OH + 1;
+    const int64_t gap = std::max<int64_t>(0, (int64_t)g.Hp - (int64_t)g.OH * g.sh);
+    int64_t NR = (V - 1) * g.sh + crossings * gap + 2 * (int64_t)g.dh + 1;
+    NR = std::min<int64_t>(NR, a.N * (int64_t)g.Hp);
+    const int64_t WL = 8 * (int64_t)g.RPR + 2;   // padded columns the runs' windows read
+    const int64_t SROW = (WL + 7) / 8 * 8;
+    if (NR * SROW >= (int64_t(1) << 24)) return pl;
+    const int HU = pl.FW == 2 ? kHU<2> : kHU<1>;
+    if (halo_units((int)(NR * SROW)) > HU - 1) return pl;   // the last unit is the spare one
+    g.NR = (int)NR; g.SROW = (int)SROW;
+    g.kh_units = 17 * g.dh * g.SROW / 8;
+    if ((int64_t)17 * g.dh * (SROW / 8) * 2 + halo_units((int)(NR * SROW)) >= (int64_t(1) << 30)) return pl;
+    g.npad = g.pw + (int)(SROW - g.pw - g.W);
+    // Input rows in VW-wide segments (whole rows: W a multiple of VW).
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
+    pl.VW = (g.W % 8 == 0 && xa % 16 == 0) ? 8 : (g.W % 4 == 0 && xa % 8 == 0) ? 4 : 0;
+    if (pl.VW == 0) return pl;
+    g.nseg = g.W / pl.VW;
+    int64_t xtasks = 2 * NR * g.nseg;
+    if (pl.VW == 8 && xtasks > kThreads && (xa % 8) == 0) {   // 16 dwords of staging registers at most
+        pl.VW = 4;
+        g.nseg = g.W / 4;
+        xtasks = 2 * NR * g.nseg;
+    }
+    pl.XR = (int)ceil_div(xtasks, kThreads);
+    if (pl.XR * pl.VW > 8) return pl;
+    g.xtasks = (int)xtasks;
+    const int64_t HW = (int64_t)g.H * g.W;
+    if ((crossings + 1) * (int64_t)g.C * HW * 2 >= (int64_t(1) << 31) || (int64_t)(g.Cg + 16) * HW * 2 >= (int64_t(1) << 31))
+        return pl;
+    const uintptr_t ya = reinterpret_cast<uintptr_t>(a.y);
+    g.sg = (g.OW % 8 == 0 && ya % 16 == 0) ? 8 : (g.OW % 4 == 0 && ya % 8 == 0) ? 4 : 1;
+    g.ocs = a.interleaved ? g.groups : 1;
+    g.okg = a.interleaved ? 1 : g.Ng;
+    g.m_tiles = (int)ceil_div(NRUN, RT);
+    g.n_tiles = (int)ceil_div(g.Ng, 64 * pl.FW);
+    g.nchunks = (int)ceil_div(g.Cg, 16);
+    if (g.nchunks % 2 != 0) return pl;   // the chunk loop is unrolled over the two stages
+    const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.groups;
+    if (tiles >= (int64_t(1) << 31)) return pl;
+    g.tiles = (int)tiles;
+    g.tiles_per_xcd = (int)ceil_div(tiles, 8);
+    g.fd_oh = make_fastdiv((uint32_t)g.OH);
+    g.fd_rpr = make_fastdiv((uint32_t)g.RPR);
+    g.fd_hp = make_fastdiv((uint32_t)g.Hp);
+    g.fd_nseg = make_fastdiv((uint32_t)g.nseg);
+    g.fd_nr = make_fastdiv((uint32_t)g.NR);
+    g.fd_mt = make_fastdiv((uint32_t)g.m_tiles);
+    g.fd_nt = make_fastdiv((uint32_t)g.n_tiles);
+    pl.ok = true;
+    return pl;
+}
+
+template <typename T, int FW, int XR, int VW, bool SG8>
+hipError_t run(const Conv2dArgs &a, const RowsPlan &pl)
+{
+    int dev = 0, cus = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    // Persistent grid: one workgroup per CU (the LDS footprint allows no more).
+    const int64_t blocks = std::min<int64_t>(pl.g.tiles, std::max(cus, 8));
+    hipLaunchKernelGGL((igemm_rows_fwd<T, FW, XR, VW, SG8>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, pl.g);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_typed(const Conv2dArgs &a, const RowsPlan &pl)
+{
+    // (XR, VW) = (1, 8) or (at most 2, 4): 8 channel rows x 16 bytes of staged input
+    // per thread, at most.
+    if (pl.g.sg == 8) return pl.VW == 8 ? run<T, 2, 1, 8, true>(a, pl) : run<T, 2, 2, 4, true>(a, pl);
+    return pl.VW == 8 ? run<T, 2, 1, 8, false>(a, pl) : run<T, 2, 2, 4, false>(a, pl);
+}
+
+}  // namespace
+
+bool igemm_rows_supported(const Conv2dArgs &a) { return make_rows_plan(a).ok; }
+
+hipError_t launch_igemm_rows(const Conv2dArgs &a, const char **kname)
+{
+    const RowsPlan pl = make_rows_plan(a);
+    if (!pl.ok) return hipErrorInvalidValue;
+    *kname = "igemm_rows_mfma32x32x16";
+    return a.dtype == DT_F16 ? run_typed<_Float16>(a, pl) : run_typed<__bf16>(a, pl);
+}
+
+}  // namespace gconv
