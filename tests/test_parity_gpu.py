@@ -18,6 +18,11 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "f16": 1e-2, "bf16": 1e-2}
+# Regression bound, well inside the bar above, near what the kernels reach: the
+# single rounding of a 16-bit output alone is up to 2^-11 (fp16) or 2^-9 (bf16) of
+# max|r|, and fp32 accumulation adds little; a dropped product or tap (of order
+# 1/sqrt(fan-in) of an output) exceeds it.
+REG = {"f32": 1e-4, "f16": 1e-3, "bf16": 4e-3}
 TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
@@ -28,6 +33,22 @@ def normwise(y, r):
     assert np.isfinite(y).all()
     den = np.abs(r).max()
     return float(np.abs(y - r).max() / (den if den > 0 else 1.0))
+
+
+def elementwise(y, r):
+    """max |y - r| / |r| over the outputs with |r| > 1e-3 max|r| (a diagnostic)."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    big = np.abs(r) > 1e-3 * np.abs(r).max()
+    return float((np.abs(y - r)[big] / np.abs(r)[big]).max()) if big.any() else 0.0
+
+
+def check(y, r, dt, label=""):
+    """The bar and the regression bound, with both error measures printed."""
+    nw = normwise(y, r)
+    print(f"{label} {dt}: normwise {nw:.3e}, elementwise over |r| > 1e-3 max|r| {elementwise(y, r):.3e}")
+    assert nw <= TOL[dt] and nw <= REG[dt], (label, dt, nw)
+    return True
 
 
 def gpu(t):
@@ -85,10 +106,9 @@ def test_sweep_vs_oracle(ci, dt):
     for route in routes:
         y = run_conv2d(x, w, b, s, p, d, g, route)
         outs[route] = y
-        err = normwise(as_f64(y.cpu()), r)
-        assert err <= TOL[dt], (route, err)
+        assert check(as_f64(y.cpu()), r, dt, route)
     if len(outs) == 2:  # the two routes agree with each other to the same bar
-        assert normwise(as_f64(outs["igemm"].cpu()), as_f64(outs["direct"].cpu())) <= TOL[dt]
+        assert normwise(as_f64(outs["igemm"].cpu()), as_f64(outs["direct"].cpu())) <= 2 * REG[dt]
 
 
 # More tiles than the chip runs workgroups (256), so every workgroup of the implicit
@@ -112,7 +132,7 @@ def test_igemm_many_tiles_per_workgroup(ci, dt):
     r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=1, padding=K // 2, dilation=1, groups=g)
     y = run_conv2d(x, w, b, 1, K // 2, 1, g, "igemm")
     assert gc.gconv_last_kernel().startswith("igemm")
-    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+    assert check(as_f64(y.cpu()), r, dt)
 
 
 DW_SWEEP = [  # B, T, C, K, stride, pad, dil, bias
@@ -140,7 +160,7 @@ def test_dw1d_sweep_vs_oracle(ci, dt):
     r = oracle.dwconv1d_btc(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=p, dilation=d)
     y = gc.dwconv1d_btc(gpu(x), gpu(w), gpu(b), stride=s, padding=p, dilation=d)
     torch.cuda.synchronize()
-    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+    assert check(as_f64(y.cpu()), r, dt)
 
 
 # Depthwise conv2d (C/g = 1): the dw2d_rows kernel where its plan applies (K in
@@ -179,7 +199,7 @@ def test_dw2d_sweep_vs_oracle(ci, dt):
     y = run_conv2d(x, w, b, s, p, 1, C, "auto")
     expect = "dw2d_rows" if K in (3, 5, 7) and s in (1, 2) else "direct2d_tiled"
     assert gc.gconv_last_kernel() == expect
-    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+    assert check(as_f64(y.cpu()), r, dt)
 
 
 # Channels-last (NHWC) conv2d: the depthwise tile kernel where it applies, the
@@ -222,7 +242,7 @@ def test_nhwc_sweep_vs_oracle(ci, dt):
     row = dt != "f32" and sw == 1 and dw_ == 1
     g4k = ("conv2d_nhwc_g4k3_row" if row else "conv2d_nhwc_g4k3") if (KH, KW) == (3, 3) else "conv2d_nhwc_g4"
     assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else g4k if g4 else "conv2d_nhwc_generic")
-    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+    assert check(as_f64(y.cpu()), r, dt)
 
 
 NHWC_IGEMM = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
@@ -255,10 +275,10 @@ def test_nhwc_igemm_vs_oracle(ci, dt):
     y = gc.gconv_fwd_route(gpu(x), gpu(w), gpu(b), s, p, d, g, "nhwc", route="igemm")
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "igemm_nhwc_mfma32x32x16"
-    assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+    assert check(as_f64(y.cpu()), r, dt)
     yd = gc.gconv_fwd_route(gpu(x), gpu(w), gpu(b), s, p, d, g, "nhwc", route="direct")
     torch.cuda.synchronize()
-    assert normwise(as_f64(y.cpu()), as_f64(yd.cpu())) <= TOL[dt]   # the two routes agree
+    assert normwise(as_f64(y.cpu()), as_f64(yd.cpu())) <= 2 * REG[dt]   # the two routes agree
 
 
 def test_nhwc_implicit_gemm_route_limits():
@@ -294,7 +314,7 @@ def test_interleaved_output_order_vs_oracle(ci):
         y = gc.gconv_fwd_ex(gpu(x), gpu(w), gpu(b), 1, K // 2, 1, g, "nchw", route=route, out_order="interleaved")
         torch.cuda.synchronize()
         assert gc.gconv_last_kernel().startswith(kern), gc.gconv_last_kernel()
-        assert normwise(as_f64(y.cpu()), r) <= TOL[dt]
+        assert check(as_f64(y.cpu()), r, dt)
 
 
 def test_interleaved_output_order_nhwc_and_naive():
@@ -308,7 +328,7 @@ def test_interleaved_output_order_nhwc_and_naive():
     y = gc.gconv_fwd_ex(gpu(x), gpu(w), gpu(b), 1, 1, 1, g, "nhwc", out_order="interleaved")
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "conv2d_nhwc_generic"
-    assert normwise(as_f64(y.cpu()), r) <= TOL["f32"]
+    assert check(as_f64(y.cpu()), r, "f32")
     # NCHW naive kernel (a dilation whose halo tile does not fit the tiled kernel's LDS).
     x2 = draw((1, 4, 112, 112), 1.0, 7991, "f32")
     w2 = draw((6, 2, 3, 3), 1.0 / 18, 8991, "f32")
@@ -316,7 +336,7 @@ def test_interleaved_output_order_nhwc_and_naive():
     y2 = gc.gconv_fwd_ex(gpu(x2), gpu(w2), None, 1, 0, 55, 2, "nchw", route="direct", out_order="interleaved")
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "direct2d_naive"
-    assert normwise(as_f64(y2.cpu()), r2) <= TOL["f32"]
+    assert check(as_f64(y2.cpu()), r2, "f32")
 
 
 def test_autotune_records_a_route_and_auto_calls_follow_it():
@@ -331,12 +351,12 @@ def test_autotune_records_a_route_and_auto_calls_follow_it():
     y = torch.full((2, 64, 28, 28), float("nan"), dtype=torch.float16, device="cuda")
     best = gc.gconv_autotune(xg, wg, bg, 1, 1, 1, 2, "nchw", reps=3, y=y)
     assert best in ("direct", "igemm")
-    assert normwise(as_f64(y.cpu()), r) <= TOL["f16"]            # y holds the chosen route's result
+    assert check(as_f64(y.cpu()), r, "f16")            # y holds the chosen route's result
     assert gc.gconv_select_route(x.shape, w.shape, 1, 1, 1, 2, "nchw", "f16") == best
     y2 = gc.gconv_fwd(xg, wg, bg, 1, 1, 1, 2, "nchw")
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel().startswith("igemm") == (best == "igemm")
-    assert normwise(as_f64(y2.cpu()), r) <= TOL["f16"]
+    assert check(as_f64(y2.cpu()), r, "f16")
     gc.gconv_autotune_clear()
     assert gc.gconv_select_route(x.shape, w.shape, 1, 1, 1, 2, "nchw", "f16") == heur
 
@@ -364,7 +384,7 @@ def test_dw2d_unaligned_output_and_input():
     gc.gconv_fwd(xu, gpu(w), gpu(b), 2, 1, 1, C, "nchw", y=yu)
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "dw2d_rows"
-    assert normwise(as_f64(yu.cpu()), r) <= TOL["f32"]
+    assert check(as_f64(yu.cpu()), r, "f32")
 
 
 def test_dw1d_unaligned_filters_use_the_window_kernel():
@@ -382,11 +402,11 @@ def test_dw1d_unaligned_filters_use_the_window_kernel():
     y = gc.dwconv1d_btc(gpu(x), wu, gpu(b), stride=1, padding=15, dilation=1)
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "dw1d_btc_window"
-    assert normwise(as_f64(y.cpu()), r) <= TOL["f32"]
+    assert check(as_f64(y.cpu()), r, "f32")
     y2 = gc.dwconv1d_btc(gpu(x), gpu(w), gpu(b), stride=1, padding=15, dilation=1)
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "dw1d_btc_tile"
-    assert normwise(as_f64(y2.cpu()), r) <= TOL["f32"]
+    assert check(as_f64(y2.cpu()), r, "f32")
 
 
 # ---------------------------------------------------------------- backward of the depthwise conv1d
@@ -417,9 +437,9 @@ def test_dw1d_backward_vs_oracle(ci, dt):
     torch.cuda.synchronize()
     rdx = oracle.dwconv1d_btc_bwd_data(as_f64(dy), as_f64(w), T, s, p, d)
     rdw, rdb = oracle.dwconv1d_btc_bwd_filter(as_f64(x), as_f64(dy), K, s, p, d)
-    assert normwise(as_f64(dx.cpu()), rdx) <= TOL[dt]
-    assert normwise(as_f64(dw.cpu()), rdw) <= TOL[dt]
-    assert normwise(as_f64(db.cpu()), rdb) <= TOL[dt]
+    assert check(as_f64(dx.cpu()), rdx, dt)
+    assert check(as_f64(dw.cpu()), rdw, dt)
+    assert check(as_f64(db.cpu()), rdb, dt)
 
 
 def test_dw1d_backward_kernels_and_determinism():
@@ -492,18 +512,25 @@ def test_workload_full_size(name):
     yc = as_f64(y.cpu())
     xd, wd, bd = as_f64(x), as_f64(w), as_f64(b)
     macs = int(np.prod(yc.shape)) * int(np.prod(wl.w_shape[1:]))
-    if macs <= 3e8:
+    # In full where the oracle finishes in seconds, and for the ensemble layer
+    # (51.4 M outputs, about 30 G multiply-adds: some 15 s on 16 cores); the two
+    # headline layers (38.7 G multiply-adds each) on a sample here, the fp16 one in
+    # full in test_igemm_rows_gpu.py.
+    if macs <= 3e8 or name == "c5_ensemble_f16":
         if wl.layout == "ntc":
             r = oracle.dwconv1d_btc(xd, wd, bd, wl.stride, wl.pad, wl.dilation)
         else:
             r = oracle.conv2d(xd, wd, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         err = normwise(yc, r)
+        ew = elementwise(yc, r)
     else:
         idx = _sample_idx(yc.size, 20000, 4242 + wl.index)
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         err = normwise(yc.ravel()[idx], r)
-    print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e}")
-    assert err <= TOL[wl.dtype]
+        ew = elementwise(yc.ravel()[idx], r)
+    print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e} "
+          f"elementwise over |r| > 1e-3 max|r| {ew:.3e}")
+    assert err <= TOL[wl.dtype] and err <= REG[wl.dtype]
 
 
 @pytest.mark.parametrize("name", sorted(NEXT_WORKLOADS))
@@ -529,8 +556,9 @@ def test_next_workload_full_size(name):
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         assert gc.gconv_last_kernel() == "dw2d_rows"
     err = normwise(yc.ravel()[idx], r)
-    print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e}")
-    assert err <= TOL[wl.dtype]
+    print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e} "
+          f"elementwise over |r| > 1e-3 max|r| {elementwise(yc.ravel()[idx], r):.3e}")
+    assert err <= TOL[wl.dtype] and err <= REG[wl.dtype]
 
 
 # ---------------------------------------------------------------- properties
