@@ -309,6 +309,120 @@ def autotune_entries(workloads, steps):
     return out
 
 
+_PEAKS = None
+
+
+def peaks_lib():
+    """libgconv_peaks.so: the MFMA-only loop and streaming-copy kernels (csrc/peaks.hip)."""
+    global _PEAKS
+    if _PEAKS is None:
+        import ctypes
+        path = os.path.join(ROOT, "depthwise_convolution_gconv_amd", "libgconv_peaks.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build with python -m depthwise_convolution_gconv_amd.build")
+        L = ctypes.CDLL(path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.gconv_peak_mfma_flop.argtypes = [i32, i32]
+        L.gconv_peak_mfma_flop.restype = ctypes.c_double
+        L.gconv_peak_mfma.argtypes = [i32, vp, i32, i32, vp, vp]
+        L.gconv_peak_mfma.restype = i32
+        L.gconv_peak_stream_copy.argtypes = [vp, vp, i64, i32, vp]
+        L.gconv_peak_stream_copy.restype = i32
+        L.gconv_peak_tile_copy.argtypes = [vp, vp, i64, i32, vp]
+        L.gconv_peak_tile_copy.restype = i32
+        _PEAKS = L
+    return _PEAKS
+
+
+def mfma_peak(kind, iters=20000, reps=3):
+    """Matrix-core rate of an MFMA-only loop (kind 0: fp16 32x32x16, 1: fp32 32x32x2),
+    one workgroup of 4 waves per CU, in TFLOP/s, and the core clock during the loop
+    (shader clock counter over the 100 MHz real-time counter, wave 0 of workgroup 0)."""
+    import torch
+    L = peaks_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(4, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    assert L.gconv_peak_mfma(kind, out.data_ptr(), cus, 100, clk.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        assert L.gconv_peak_mfma(kind, out.data_ptr(), cus, iters, clk.data_ptr(), st) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    c = clk.cpu().tolist()
+    ghz = (c[2] - c[0]) / ((c[3] - c[1]) / 100e6) / 1e9 if c[3] > c[1] else None
+    return {"tflops": round(L.gconv_peak_mfma_flop(kind, iters) * cus / t / 1e12, 1),
+            "clock_ghz": None if ghz is None else round(ghz, 3), "cus": cus}
+
+
+def stream_peak_gbs(nbytes=1 << 30, reps=10):
+    """HBM bandwidth (read + write bytes per second) of the library's own streaming
+    copy: 16-byte loads, 4 in flight per thread, non-temporal 16-byte stores."""
+    import torch
+    L = peaks_lib()
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    st = torch.cuda.current_stream().cuda_stream
+    n16 = nbytes // 16
+    assert L.gconv_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16, 8 * cus, st) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        L.gconv_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16, 8 * cus, st)
+    e1.record()
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(src[:1024], dst[:1024]))
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    if not ok:
+        raise RuntimeError("stream copy check failed")
+    return round(gbs, 1)
+
+
+def tile_copy_floor(rows, C, steps=200, rotate_bytes=512 << 20):
+    """Per-launch time of a plain copy of a rows x C fp32 tensor on the grid of the
+    (batch, steps, channels) depthwise kernel (tiles of 32 rows x 64 channels, one
+    workgroup each, 16-byte loads, non-temporal stores), rotated over cold buffer
+    sets and replayed from a HIP graph like the convolution itself."""
+    import torch
+    L = peaks_lib()
+    nbytes = rows * C * 4
+    nsets = min(32, max(1, math.ceil(rotate_bytes / (2 * nbytes))))
+    bufs = [(torch.ones(rows * C, dtype=torch.float32, device="cuda"),
+             torch.empty(rows * C, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
+    gs = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gs):
+        for a, b in bufs:
+            L.gconv_peak_tile_copy(a.data_ptr(), b.data_ptr(), rows, C, gs.cuda_stream)
+    with torch.cuda.stream(gs):
+        graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(bufs[0][0], bufs[0][1]):
+        raise RuntimeError("tile copy check failed")
+    reps = max(1, round(steps / nsets))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(gs):
+        e0.record(gs)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(gs)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nsets)
+    del graph, bufs
+    torch.cuda.empty_cache()
+    return {"us_per_launch": round(us, 2), "gb_per_s": round(2 * nbytes / (us * 1e-6) / 1e9, 1),
+            "bytes_per_launch": 2 * nbytes}
+
+
 def copy_peak_gbs(nbytes=1 << 30, reps=10):
     """HBM bandwidth a plain device copy reaches on this GPU (read + write bytes per
     second), the measured counterpart of the published 8 TB/s."""
