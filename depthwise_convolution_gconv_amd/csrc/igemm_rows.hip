@@ -212,7 +212,8 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in a scalar register
     const int hf = lane >> 5, l32 = lane & 31;
     const int pwv = wave / FW, fwv = wave % FW;
     const int OHW = g.OH * g.OW;
@@ -293,27 +294,30 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         return s;
     };
 
-    uint32_t d[XR][8][DW];   // staged input rows of the next step
+    // Staged input rows, two sets: while chunk c writes step c+1's rows (loaded
+    // during chunk c-1) into LDS, step c+2's rows arrive in the other set, a whole
+    // chunk ahead of their use.
+    uint32_t d[2][XR][8][DW];
     uint32_t E[36];          // a filter run being transposed: 8 channels x 9 taps
     // Filter copy instruction i (< 9) of one pipeline step (tile s, chunk ch) into
     // stage stg, by a staging wave: pieces 64i + lane of the wave's block, piece q
     // being bytes 16*(q % 18) of filter q / 18's 288-byte run.
-    auto filter_copy = [&](const TileState &s, int ch, auto stg, bool any, int i) {
-        const int c0 = ch * 16;
+    // (Every chunk holds 16 channels: C/g is a multiple of 32 here.)  The lane's piece
+    // of copy instruction i is filter pf[i] of the block, bytes 16*pj[i] of its run:
+    // a byte offset pf*18*C/g + 16*pj from the block's first filter, the same in every
+    // tile and chunk; the tile and chunk add a uniform offset.
+    auto filter_copy = [&](const TileState &s, int ch, auto stg, int i) {
         const int q = 64 * i + lane;
         const int pf = (q * 3641) >> 16;    // q / 18 for q < 576
-        const int pj = q - 18 * pf;
-        const bool ok = any && pf < s.nfw && (pj < 9 || c0 + 8 < g.Cg);   // channels 8-15 exist
-        const uint32_t off = ok ? (uint32_t)(((s.fbase + pf) * g.Cg + c0) * 18 + 16 * pj) : kOOB;
+        const uint32_t off = pf < s.nfw ? (uint32_t)(pf * g.Cg * 18 + 16 * (q - 18 * pf)) : kOOB;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, GCONV_LDS(fim(stg) + kBlockUnits * wave + 64 * i), 16, off,
-                                                 0, 0, 0);
+                                                 (uint32_t)(s.fbase * g.Cg + ch * 16) * 18, 0, 0);
     };
     // Input load j (< 8*XR) of one pipeline step into registers: task j/8, channel row j%8.
-    auto input_load = [&](const TileState &s, int ch, bool any, int j) {
+    auto input_load = [&](auto set, const TileState &s, int ch, int j) {
         const int r = j >> 3, e = j & 7;
-        const int c0 = ch * 16;
-        const bool ok = any && xtask[r] && c0 + 8 * xoct[r] + e < g.Cg;
-        VecLoad<VW>::run(s.xr, ok ? s.xvo[r] : kOOB, (uint32_t)(c0 + e) * HW * 2, d[r][e]);
+        VecLoad<VW>::run(s.xr, xtask[r] ? s.xvo[r] : kOOB, (uint32_t)(ch * 16 + e) * HW * 2,
+                         d[decltype(set)::value][r][e]);
     };
     // Transpose of this wave's block in stage stg, in place: read u (< 9) brings raw
     // unit u of the lane's run (8 channels x 9 taps); write t (< 9) forms the unit of
@@ -337,10 +341,11 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     };
     // Staging write o (< XR*VW) into stage stg: column o % VW of task o / VW as one
     // unit of 8 channels; a thread without that task writes the spare unit.
-    auto input_write = [&](auto stg, int o) {
+    auto input_write = [&](auto set, auto stg, int o) {
+        constexpr int SET = decltype(set)::value;
         const int r = o / VW, v = o % VW;
-        const uint32_t *ra = d[r][0], *rb = d[r][1], *rc = d[r][2], *rd = d[r][3];
-        const uint32_t *re = d[r][4], *rf = d[r][5], *rg = d[r][6], *rh = d[r][7];
+        const uint32_t *ra = d[SET][r][0], *rb = d[SET][r][1], *rc = d[SET][r][2], *rd = d[SET][r][3];
+        const uint32_t *re = d[SET][r][4], *rf = d[SET][r][5], *rg = d[SET][r][6], *rh = d[SET][r][7];
         const uint32_t bsel = 2 * (v & 1);
         const uint32_t sel = ((bsel + 5) << 24) | ((bsel + 4) << 16) | ((bsel + 1) << 8) | bsel;
         const int w2 = v >> 1;
@@ -365,10 +370,12 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     TileState ts = tile_state(tile);
     if (NTW == 4 || wave < NTW) {
 #pragma unroll
-        for (int i = 0; i < 9; ++i) filter_copy(ts, 0, S0{}, true, i);
+        for (int i = 0; i < 9; ++i) filter_copy(ts, 0, S0{}, i);
     }
 #pragma unroll
-    for (int j = 0; j < 8 * XR; ++j) input_load(ts, 0, true, j);
+    for (int j = 0; j < 8 * XR; ++j) input_load(S0{}, ts, 0, j);
+#pragma unroll
+    for (int j = 0; j < 8 * XR; ++j) input_load(S1{}, ts, 1, j);   // step 1, written during chunk 0
     if (NTW == 4 || wave < NTW) {
 #pragma unroll
         for (int u = 0; u < 9; ++u) transpose_read(S0{}, u);
@@ -378,7 +385,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         for (int t = 0; t < 9; ++t) transpose_write(S0{}, t);
     }
 #pragma unroll
-    for (int o = 0; o < XR * VW; ++o) input_write(S0{}, o);
+    for (int o = 0; o < XR * VW; ++o) input_write(S0{}, S0{}, o);
     __syncthreads();
 
     for (;;) {
@@ -403,7 +410,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 
         const int next_tile = tile + nbx;
         const bool has_next = next_tile < t_hi;
-        TileState nts = ts;
+        const TileState nts = has_next ? tile_state(next_tile) : ts;
         // One chunk: computes from stage CUR and stages the next pipeline step into
         // the other one (instantiated once per stage, so every LDS array is named
         // statically).
@@ -412,11 +419,12 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             using NXT = std::integral_constant<int, 1 - CUR::value>;
             const NXT nst{};
             const bool last = ch + 1 == g.nchunks;
-            if (last && has_next) nts = tile_state(next_tile);
-            // Next pipeline step: chunk ch+1 of this tile, or chunk 0 of the next tile.
+            // Next pipeline step: chunk ch+1 of this tile, or chunk 0 of the next tile
+            // (its filters are copied now); the input rows two steps ahead.
             const TileState src = last ? nts : ts;
             const int nch = last ? 0 : ch + 1;
-            const bool more = !last || has_next;
+            const TileState src2 = ch + 2 < g.nchunks ? ts : nts;
+            const int nch2 = ch + 2 < g.nchunks ? ch + 2 : ch + 2 - g.nchunks;
 
             const uint4 *hs = hal(cur);
             const uint4 *fs = fim(cur);
@@ -436,10 +444,11 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             //    right after the MFMA that last uses it in this row (position 0 after
             //    tap kw = 0, position 1 after kw = 1, position 2 + mb after block mb of
             //    kw = 2), at least 16 MFMAs before its first use;
-            //  * taps 0-4 from slot 3 on: the global loads of the next pipeline step,
-            //    one every 4 (or 3) slots: the input rows, then the filter copies;
-            //  * tap 5: the transpose reads; taps 6-8: its 9 unit writes (every fourth
-            //    slot) and the input staging writes (odd slots).
+            //  * from slot 3 of tap 0 on, every second slot: the global loads of the
+            //    next pipeline step, the input rows (from memory, first touch) before
+            //    the filter copies (from L2);
+            //  * taps 6-8, odd slots: the input staging writes; tap 6: the transpose
+            //    reads; taps 7-8: its 9 unit writes.
             constexpr int NVM = (NTW == 4 ? 9 : 0) + 8 * XR;   // global loads per step
 #pragma unroll
             for (int t = 0; t < 9; ++t) {
@@ -453,28 +462,27 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                         const int e = mb + kw;   // its last use in this row was this MFMA
                         win[e] = hs[ub + (kh + 1) * g.kh_units + 2 * e + (e >> 3)];
                     }
-                    // Global loads: the input rows first, then the filter copies, one
-                    // every OS slots from slot 3 of tap 0 on (taps 0-4).
-                    constexpr int OS = NVM <= 17 ? 4 : 3;
+                    // Global loads: the input rows, then the filter copies, one every
+                    // second slot from slot 3 of tap 0 on.
                     const int sl = 16 * t + i - 3;
-                    if (sl >= 0 && sl % OS == 0 && sl / OS < NVM) {
-                        const int o = sl / OS;
-                        if (o < 8 * XR) input_load(src, nch, more, o);
-                        else if (NTW == 4) filter_copy(src, nch, nst, more, o - 8 * XR);
+                    if (sl >= 0 && (sl & 1) == 0 && sl / 2 < NVM) {
+                        const int o = sl / 2;
+                        if (o < 8 * XR) input_load(cur, src2, nch2, o);
+                        else if (NTW == 4) filter_copy(src, nch, nst, o - 8 * XR);
                     }
                     if (NTW == 4) {
-                        if (t == 5 && i >= 1 && i <= 9) transpose_read(nst, i - 1);
-                        if (t == 6 && i == 0) {
+                        if (t == 6 && i >= 2 && i <= 10) transpose_read(nst, i - 2);
+                        if (t == 7 && i == 0) {
                             // every transpose read has returned before the first write
 #pragma unroll
                             for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
                         }
-                        if (((t == 6 || t == 7) && i % 4 == 0) || (t == 8 && i == 0))
-                            transpose_write(nst, (t - 6) * 4 + i / 4);
+                        if ((t == 7 && i % 4 == 0) || (t == 8 && i % 3 == 0 && i < 15))
+                            transpose_write(nst, t == 7 ? i / 4 : 4 + i / 3);
                     }
                     if (t >= 6 && (i & 1) == 1) {
                         const int ow = (t - 6) * 8 + i / 2;
-                        if (ow < XR * VW) input_write(nst, ow);
+                        if (ow < XR * VW) input_write(nst, nst, ow);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -484,7 +492,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                 // done by waves 0 .. NTW-1 outside the scheduled taps.
                 if (wave < NTW) {
 #pragma unroll
-                    for (int i = 0; i < 9; ++i) filter_copy(src, nch, nst, more, i);
+                    for (int i = 0; i < 9; ++i) filter_copy(src, nch, nst, i);
 #pragma unroll
                     for (int u = 0; u < 9; ++u) transpose_read(nst, u);
 #pragma unroll
@@ -586,8 +594,10 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
     g.sh = a.sh; g.ph = a.ph; g.pw = a.pw; g.dh = a.dh;
     g.groups = (int)a.groups;
     // Filters: a chunk of one filter is 16 channels x 9 taps = 288 contiguous bytes,
-    // copied in 16-byte pieces (C/g a multiple of 8 keeps every piece aligned).
-    if (g.Cg % 8 != 0 || (reinterpret_cast<uintptr_t>(a.w) & 15) != 0) return pl;
+    // copied in 16-byte pieces.
+    // C/g a multiple of 32: every chunk holds 16 channels and the chunk loop, unrolled
+    // over the two stages, takes an even number of them.
+    if (g.Cg % 32 != 0 || (reinterpret_cast<uintptr_t>(a.w) & 15) != 0) return pl;
     const int64_t w_bytes = a.Cout * (int64_t)g.Cg * 18;
     if (w_bytes >= (int64_t(1) << 31)) return pl;
     g.w_bytes = (uint32_t)w_bytes;
@@ -648,8 +658,7 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
     g.okg = a.interleaved ? 1 : g.Ng;
     g.m_tiles = (int)ceil_div(NRUN, RT);
     g.n_tiles = (int)ceil_div(g.Ng, 64 * pl.FW);
-    g.nchunks = (int)ceil_div(g.Cg, 16);
-    if (g.nchunks % 2 != 0) return pl;   // the chunk loop is unrolled over the two stages
+    g.nchunks = g.Cg / 16;
     const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.groups;
     if (tiles >= (int64_t(1) << 31)) return pl;
     g.tiles = (int)tiles;
