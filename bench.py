@@ -83,11 +83,47 @@ def alg_bytes(wl):
     return n * es
 
 
-def compute_peak(wl, route):
-    """(bound name, peak TFLOP/s) of the arithmetic unit the route runs on."""
-    if route == "igemm":
-        return "mfma", PEAK_TFLOPS[wl.dtype]
-    return "alu", PEAK_TFLOPS["f32"]
+# Arithmetic unit and peak of each kernel (TFLOP/s), with the derivation.  The
+# vector-ALU figures hold for the plain (non-packed) instructions the kernels are
+# built with: the measurement loops show gfx950 issuing a wave64 v_fma_f32 every
+# ~2.3 cycles per SIMD at 8 waves per SIMD (the published fp32 vector peak
+# assumes 2 cycles) and a wave64 v_dot2_f32_f16 every ~4.3 cycles.
+CLOCK_GHZ, CUS = 2.4, 256
+UNITS = {
+    "mfma32x32x16": ("mfma", None, "published dense fp16/bf16 MFMA peak (v_mfma_f32_32x32x16_{f16,bf16}, "
+                     "32768 FLOP per 32 cycles per SIMD, 256 CUs x 4 SIMDs x 2.4 GHz)"),
+    "mfma32x32x2": ("mfma", 157.3, "published fp32 MFMA peak (v_mfma_f32_32x32x2_f32)"),
+    "mfma4x4x4": ("mfma", 518.0, "v_mfma_f32_4x4x4_16b_{f16,bf16} has no published peak: 2048 FLOP per "
+                  "instruction, which the MFMA-only loop issues every 9.7 cycles per SIMD (518 TFLOP/s "
+                  "measured at 2.4 GHz)"),
+    "dot2": ("alu", 157.3, "v_dot2_f32_{f16,bf16}: 64 lanes x 4 FLOP per 4 cycles per SIMD, 256 CUs x 4 SIMDs "
+             "x 2.4 GHz"),
+    "valu": ("alu", 157.3, "published fp32 vector peak (64 lanes x 2 FLOP per 2 cycles per SIMD, 256 CUs x 4 "
+             "SIMDs x 2.4 GHz), which plain v_fma_f32 nearly reaches on gfx950 (measured 2.3 cycles per "
+             "wave64 instruction)"),
+}
+
+
+def kernel_unit(kernel, dtype):
+    """Key into UNITS of the arithmetic a kernel runs on."""
+    if kernel.endswith("mfma32x32x16"):
+        return "mfma32x32x16"
+    if kernel.endswith("mfma32x32x2"):
+        return "mfma32x32x2"
+    if kernel == "direct2d_g4" and dtype != "f32":
+        return "mfma4x4x4"
+    if kernel == "conv2d_nhwc_g4k3_row" and dtype != "f32":
+        return "dot2"
+    return "valu"
+
+
+def compute_peak(wl, kernel):
+    """(bound name, peak TFLOP/s, derivation) of the arithmetic unit the kernel runs on."""
+    unit = kernel_unit(kernel, wl.dtype)
+    bound, peak, how = UNITS[unit]
+    if unit == "mfma32x32x16":
+        peak = PEAK_TFLOPS[wl.dtype]
+    return bound, round(peak, 1), how
 
 
 def source_digest(kernel_file):
@@ -101,6 +137,7 @@ KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_rows_mfma32x32x16"
                 "direct2d_g4": "direct2d.hip", "direct2d_tiled": "direct2d.hip",
                 "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip",
                 "dw1d_btc_tile": "dw1d_ntc.hip", "dw1d_btc_window": "dw1d_ntc.hip",
+                "dw1d_btc_tile_flip": "dw1d_ntc.hip",
                 "dw1d_btc_generic": "dw1d_ntc.hip", "dw2d_nhwc_tile": "nhwc.hip",
                 "igemm_nhwc_mfma32x32x16": "igemm_nhwc.hip", "conv2d_nhwc_g4": "nhwc.hip",
                 "conv2d_nhwc_g4k3": "nhwc.hip", "conv2d_nhwc_g4k3_row": "nhwc.hip",
@@ -185,27 +222,59 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20, route=None):
     torch.cuda.synchronize()
     if not torch.equal(outs[0], ref0):
         raise RuntimeError("graph replay differs from the eager result")
-    reps = max(1, round(steps / nsets))
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with torch.cuda.stream(gstream):   # replay() launches on the current stream
-        g0.record(gstream)
-        for _ in range(reps):
-            graph.replay()
-        g1.record(gstream)
-    torch.cuda.synchronize()
-    kernel_ms = g0.elapsed_time(g1) / (reps * nsets)
+    # One event pair per replay: each replay is one sample (the average launch of
+    # one pass over the buffer sets), at least 20 of them.
+    reps = max(20, round(steps / nsets))
+    cold = replay_samples(graph, gstream, reps, nsets)
     del graph
-    return {"step_ms": step_ms, "kernel_ms_avg": kernel_ms, "graph_launches": reps * nsets,
-            "wall_s": wall, "kernel": kernel, "rotation_sets": nsets}
+    # Hot cache: the call on one buffer set, repeated back to back, so its operands
+    # stay in the L2 / Infinity Cache between launches.
+    # The graph holds several launches, so that one replay's own start-up cost is
+    # spread as it is for the cold graph.
+    hot_n = max(nsets, 8)
+    hot_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(hot_graph, stream=gstream):
+        for _ in range(hot_n):
+            gcalls[0]()
+    with torch.cuda.stream(gstream):
+        hot_graph.replay()
+    torch.cuda.synchronize()
+    hot = replay_samples(hot_graph, gstream, max(20, round(steps / hot_n)), hot_n)
+    del hot_graph
+    return {"step_ms": step_ms, "kernel_ms_avg": sum(cold) / len(cold), "kernel_samples": cold,
+            "hot_samples": hot, "graph_launches": reps * nsets, "wall_s": wall, "kernel": kernel,
+            "rotation_sets": nsets}
+
+
+def replay_samples(graph, stream, reps, launches):
+    """Replays `graph` `reps` times on `stream`, one HIP event pair around each
+    replay; returns the per-launch milliseconds of each replay."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):   # replay() launches on the current stream
+        for e0, e1 in evs:
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) / launches for e0, e1 in evs]
+
+
+def stats(samples_ms):
+    """Median, p10, p90 (ms) and the count of a list of samples."""
+    import numpy as np
+    a = np.asarray(samples_ms, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "samples": int(a.size)}
 
 
 def measure_dw1d_backward(wl, kind, steps, rotate_bytes=512 << 20):
     """Per-call device time of the input gradient (kind "data") or the filter and
     bias gradients (kind "filter", two kernels per call) of the depthwise conv1d of
     workload `wl`, from a replayed HIP graph of one call per rotating buffer set
-    (events on the replay stream).  Returns (ms per call, kernel name)."""
+    (one event pair per replay on the replay stream).  Returns (per-call ms of each
+    replay, kernel name)."""
     import torch
     import depthwise_convolution_gconv_amd as gc
     from depthwise_convolution_gconv_amd.workloads import draw, make_inputs
@@ -245,19 +314,12 @@ def measure_dw1d_backward(wl, kind, steps, rotate_bytes=512 << 20):
     with torch.cuda.graph(graph, stream=gstream):
         for st in sets:
             call(st)
-    reps = max(1, round(steps / nsets))
-    g0 = torch.cuda.Event(enable_timing=True)
-    g1 = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(gstream):
         graph.replay()
     torch.cuda.synchronize()
-    with torch.cuda.stream(gstream):
-        g0.record(gstream)
-        for _ in range(reps):
-            graph.replay()
-        g1.record(gstream)
-    torch.cuda.synchronize()
-    return g0.elapsed_time(g1) / (reps * nsets), kernel
+    samples = replay_samples(graph, gstream, max(20, round(steps / nsets)), nsets)
+    del graph
+    return samples, kernel
 
 
 def bwd_bytes(wl, kind):
@@ -271,20 +333,24 @@ def bwd_bytes(wl, kind):
     return (B * T * C + B * To * C + C * K + C) * es
 
 
-def bwd_entry(wl, kind, steps, name=None):
-    ms, kernel = measure_dw1d_backward(wl, kind, steps)
+def bwd_entry(wl, kind, steps, name=None, peaks=None):
+    samples, kernel = measure_dw1d_backward(wl, kind, steps)
+    ms = sum(samples) / len(samples)
     byts = bwd_bytes(wl, kind)
     B, T, C = wl.x_shape
     K = wl.w_shape[2]
     To = (T + 2 * wl.pad - wl.dilation * (K - 1) - 1) // wl.stride + 1
     f = 2 * B * To * C * K
     gbs = byts / (ms * 1e-3) / 1e9
-    return {"kernel": kernel, "kernel_ms_avg": round(ms, 5), "tflops": round(f / (ms * 1e-3) / 1e12, 3),
-            "gb_per_s": round(gbs, 1),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": counters_traffic(name, "dw1d_ntc.hip" if kind == "data" else "dw1d_wgrad.hip")
-                         if name else None}}
+    rf = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+          "frac": round(gbs / PEAK_HBM_GBS, 4),
+          "traffic": counters_traffic(name, "dw1d_ntc.hip" if kind == "data" else "dw1d_wgrad.hip")
+          if name else None}
+    if peaks:
+        rf["measured_peak"] = peaks["hbm_stream_copy"]["gb_per_s"]
+        rf["frac_of_measured"] = round(gbs / rf["measured_peak"], 4)
+    return {"kernel": kernel, "kernel_ms_avg": round(ms, 5), "kernel_ms": stats(samples),
+            "tflops": round(f / (ms * 1e-3) / 1e12, 3), "gb_per_s": round(gbs, 1), "roofline": rf}
 
 
 def autotune_entries(workloads, steps):
@@ -326,7 +392,7 @@ def peaks_lib():
         L.gconv_peak_mfma_flop.restype = ctypes.c_double
         L.gconv_peak_mfma.argtypes = [i32, vp, i32, i32, vp, vp]
         L.gconv_peak_mfma.restype = i32
-        L.gconv_peak_stream_copy.argtypes = [vp, vp, i64, i32, vp]
+        L.gconv_peak_stream_copy.argtypes = [vp, vp, i64, vp]
         L.gconv_peak_stream_copy.restype = i32
         L.gconv_peak_tile_copy.argtypes = [vp, vp, i64, i32, vp]
         L.gconv_peak_tile_copy.restype = i32
@@ -334,50 +400,82 @@ def peaks_lib():
     return _PEAKS
 
 
-def mfma_peak(kind, iters=20000, reps=3):
-    """Matrix-core rate of an MFMA-only loop (kind 0: fp16 32x32x16, 1: fp32 32x32x2),
-    one workgroup of 4 waves per CU, in TFLOP/s, and the core clock during the loop
-    (shader clock counter over the 100 MHz real-time counter, wave 0 of workgroup 0)."""
+# Loops of the measurement library: name -> (kind, FLOP per instruction per wave,
+# workgroups of 4 waves per CU, i.e. waves per SIMD).  Each runs at the
+# occupancy where its rate levels off: two waves per SIMD for the long 32x32
+# MFMAs (one leaves the issue gaps between instructions open), four for the
+# short 4x4x4 MFMA, eight for the vector-ALU loops (one wave's loop bookkeeping
+# issues beside the others' arithmetic).
+PEAK_LOOPS = {"mfma_f16_32x32x16": (0, 2 * 32 * 32 * 16, 2), "mfma_f32_32x32x2": (1, 2 * 32 * 32 * 2, 2),
+              "mfma_f16_4x4x4_16b": (2, 2 * 16 * 64, 4), "mfma_bf16_4x4x4_16b": (3, 2 * 16 * 64, 4),
+              "valu_fma_f32": (4, 2 * 64, 8), "valu_dot2_f16": (5, 4 * 64, 8)}
+
+
+def mfma_peak(kind, flop_per_instr, wgs_per_cu=1, iters=20000, reps=3):
+    """Rate of an arithmetic-only loop of the measurement library (PEAK_LOOPS),
+    `wgs_per_cu` workgroups of 4 waves per CU, in TFLOP/s; the core clock during the
+    loop (shader clock counter over the 100 MHz real-time counter, wave 0 of
+    workgroup 0); and the cycles one SIMD spends per instruction at that clock."""
     import torch
     L = peaks_lib()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    out = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    blocks = cus * wgs_per_cu
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     clk = torch.zeros(4, dtype=torch.int64, device="cuda")
     st = torch.cuda.current_stream().cuda_stream
-    assert L.gconv_peak_mfma(kind, out.data_ptr(), cus, 100, clk.data_ptr(), st) == 0
+    assert L.gconv_peak_mfma(kind, out.data_ptr(), blocks, 100, clk.data_ptr(), st) == 0
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        assert L.gconv_peak_mfma(kind, out.data_ptr(), cus, iters, clk.data_ptr(), st) == 0
+        assert L.gconv_peak_mfma(kind, out.data_ptr(), blocks, iters, clk.data_ptr(), st) == 0
     e1.record()
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) * 1e-3 / reps
     c = clk.cpu().tolist()
     ghz = (c[2] - c[0]) / ((c[3] - c[1]) / 100e6) / 1e9 if c[3] > c[1] else None
-    return {"tflops": round(L.gconv_peak_mfma_flop(kind, iters) * cus / t / 1e12, 1),
-            "clock_ghz": None if ghz is None else round(ghz, 3), "cus": cus}
+    tflops = L.gconv_peak_mfma_flop(kind, iters) * blocks / t / 1e12
+    cyc = None
+    if ghz:
+        cyc = flop_per_instr * 4 / (tflops * 1e12 / (cus * ghz * 1e9))
+    return {"tflops": round(tflops, 1), "clock_ghz": None if ghz is None else round(ghz, 3),
+            "cycles_per_instr_per_simd": None if cyc is None else round(cyc, 2), "waves_per_simd": wgs_per_cu}
+
+
+def measure_peaks(conformer=None):
+    """What this GPU sustains: every arithmetic loop of PEAK_LOOPS, the library's
+    own streaming copy and torch's device copy of 1 GiB, and, given the Conformer
+    depthwise workload, a plain copy of its tensor on its kernel's tile grid."""
+    out = {name: mfma_peak(kind, fpi, wgs) for name, (kind, fpi, wgs) in PEAK_LOOPS.items()}
+    out["hbm_stream_copy"] = {"gb_per_s": stream_peak_gbs(),
+                              "how": "csrc/peaks.hip stream_copy, 1 GiB, 10 launches; read + write bytes"}
+    out["hbm_torch_copy"] = {"gb_per_s": copy_peak_gbs(), "how": "torch copy_ of 1 GiB, 10 launches"}
+    if conformer is not None:
+        B, T, C = conformer.x_shape
+        out["conformer_tile_copy"] = tile_copy_floor(B * T, C)
+    out["clock"] = {"ghz_during_mfma_f16_loop": out["mfma_f16_32x32x16"]["clock_ghz"],
+                    "ghz_during_valu_loop": out["valu_fma_f32"]["clock_ghz"], "peak_ghz": CLOCK_GHZ}
+    return out
 
 
 def stream_peak_gbs(nbytes=1 << 30, reps=10):
     """HBM bandwidth (read + write bytes per second) of the library's own streaming
-    copy: 16-byte loads, 4 in flight per thread, non-temporal 16-byte stores."""
+    copy: one non-temporal 16-byte load and store per thread."""
     import torch
     L = peaks_lib()
-    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    src = torch.arange(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
     st = torch.cuda.current_stream().cuda_stream
     n16 = nbytes // 16
-    assert L.gconv_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16, 8 * cus, st) == 0
+    assert L.gconv_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16, st) == 0
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        L.gconv_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16, 8 * cus, st)
+        L.gconv_peak_stream_copy(src.data_ptr(), dst.data_ptr(), n16, st)
     e1.record()
     torch.cuda.synchronize()
-    ok = bool(torch.equal(src[:1024], dst[:1024]))
+    ok = bool(torch.equal(src, dst))
     gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
@@ -408,19 +506,14 @@ def tile_copy_floor(rows, C, steps=200, rotate_bytes=512 << 20):
     torch.cuda.synchronize()
     if not torch.equal(bufs[0][0], bufs[0][1]):
         raise RuntimeError("tile copy check failed")
-    reps = max(1, round(steps / nsets))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(gs):
-        e0.record(gs)
-        for _ in range(reps):
-            graph.replay()
-        e1.record(gs)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * nsets)
+    samples = replay_samples(graph, gs, max(20, round(steps / nsets)), nsets)
     del graph, bufs
     torch.cuda.empty_cache()
+    us = 1e3 * sum(samples) / len(samples)
     return {"us_per_launch": round(us, 2), "gb_per_s": round(2 * nbytes / (us * 1e-6) / 1e9, 1),
-            "bytes_per_launch": 2 * nbytes}
+            "bytes_per_launch": 2 * nbytes, "ms_per_launch": stats(samples),
+            "how": "csrc/peaks.hip tile_copy: 32 x 64 fp32 tiles, one workgroup each, 16-byte loads and "
+                   "non-temporal stores, cold buffer sets replayed from a HIP graph"}
 
 
 def copy_peak_gbs(nbytes=1 << 30, reps=10):
@@ -444,26 +537,41 @@ def copy_peak_gbs(nbytes=1 << 30, reps=10):
     return round(gbs, 1)
 
 
-def with_copy_frac(rf, copy_gbs):
-    """Adds the fraction of the measured copy bandwidth to an HBM-bound roofline."""
-    if rf.get("unit") == "GB/s" and copy_gbs:
-        rf = dict(rf)
-        rf["frac_of_measured_copy"] = round(rf["achieved"] / copy_gbs, 4)
-    return rf
+MEASURED_KEY = {"mfma32x32x16": "mfma_f16_32x32x16", "mfma32x32x2": "mfma_f32_32x32x2",
+                "mfma4x4x4": "mfma_bf16_4x4x4_16b", "dot2": "valu_dot2_f16", "valu": "valu_fma_f32"}
 
 
-def roofline(wl, route, kernel_ms, traffic):
+def roofline(wl, kernel, kernel_ms, traffic, peaks=None):
+    """Roofline object of one kernel: the bound (HBM or the kernel's arithmetic unit,
+    whichever takes longer at the published peaks), the achieved rate from the
+    algorithmic FLOP or bytes and the average launch time, and its fraction of the
+    published peak; with `peaks` (measure_peaks()) also of the measured one."""
     f = flops(wl)
     byts = alg_bytes(wl)
-    cname, cpeak = compute_peak(wl, route)
+    cname, cpeak, how = compute_peak(wl, kernel)
     t_hbm = byts / (PEAK_HBM_GBS * 1e9)
     t_cmp = f / (cpeak * 1e12)
     t = kernel_ms * 1e-3
     if t_hbm >= t_cmp:
-        return {"bound": "hbm", "achieved": round(byts / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(byts / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic}
-    return {"bound": cname, "achieved": round(f / t / 1e12, 2), "peak": cpeak, "unit": "TFLOP/s",
-            "frac": round(f / t / 1e12 / cpeak, 4), "traffic": traffic}
+        rf = {"bound": "hbm", "achieved": round(byts / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": round(byts / t / 1e9 / PEAK_HBM_GBS, 4), "traffic": traffic,
+              "compute_peak": {"unit": kernel_unit(kernel, wl.dtype), "tflops": cpeak, "derivation": how}}
+        if peaks:
+            m = peaks["hbm_stream_copy"]["gb_per_s"]
+            rf["measured_peak"] = m
+            rf["frac_of_measured"] = round(rf["achieved"] / m, 4)
+        return rf
+    rf = {"bound": cname, "achieved": round(f / t / 1e12, 2), "peak": cpeak, "unit": "TFLOP/s",
+          "frac": round(f / t / 1e12 / cpeak, 4), "traffic": traffic, "peak_derivation": how}
+    if peaks:
+        key = MEASURED_KEY[kernel_unit(kernel, wl.dtype)]
+        if wl.dtype == "f16" and key == "mfma_bf16_4x4x4_16b":
+            key = "mfma_f16_4x4x4_16b"
+        m = peaks[key]["tflops"]
+        rf["measured_peak"] = m
+        rf["measured_peak_of"] = key
+        rf["frac_of_measured"] = round(rf["achieved"] / m, 4)
+    return rf
 
 
 def cpu_baseline(wl, target_s=10.0):
@@ -512,16 +620,39 @@ def kernel_file(kernel):
     return KERNEL_FILES[kernel]
 
 
-def measure_entry(wl, steps):
+def timing(m):
+    """Timing object of one workload for the JSON line."""
+    return {"avg_per_launch": round(m["kernel_ms_avg"], 5), "cold": stats(m["kernel_samples"]),
+            "hot": stats(m["hot_samples"]), "graph_launches": m["graph_launches"],
+            "rotation_sets": m["rotation_sets"],
+            "how": "HIP graph of one call per cold buffer set, one event pair per replay on the replay "
+                   "stream (cold); one buffer set replayed back to back (hot, operands in L2 / Infinity Cache)"}
+
+
+def measure_entry(wl, steps, peaks=None):
     """Timing and roofline of one non-headline workload (a dict for the JSON line)."""
     route = route_of(wl)
     m = measure(wl, max(20, steps // 2), 5)
-    rf = roofline(wl, route, m["kernel_ms_avg"], counters_traffic(wl.name, kernel_file(m["kernel"])))
-    return {"route": route, "kernel": m["kernel"], "ms_per_step": round(m["step_ms"], 5),
-            "kernel_ms_avg": round(m["kernel_ms_avg"], 5),
-            "tflops": round(flops(wl) / (m["kernel_ms_avg"] * 1e-3) / 1e12, 3),
-            "gb_per_s": round(alg_bytes(wl) / (m["kernel_ms_avg"] * 1e-3) / 1e9, 1),
-            "roofline": rf}
+    rf = roofline(wl, m["kernel"], m["kernel_ms_avg"], counters_traffic(wl.name, kernel_file(m["kernel"])), peaks)
+    e = {"route": route, "kernel": m["kernel"], "ms_per_step": round(m["step_ms"], 5),
+         "kernel_ms": timing(m),
+         "tflops": round(flops(wl) / (m["kernel_ms_avg"] * 1e-3) / 1e12, 3),
+         "gb_per_s": round(alg_bytes(wl) / (m["kernel_ms_avg"] * 1e-3) / 1e9, 1),
+         "roofline": rf}
+    floor = conformer_floor(wl, m, peaks)
+    if floor:
+        e["tile_copy_floor"] = floor
+    return e
+
+
+def conformer_floor(wl, m, peaks):
+    """For the Conformer depthwise workload: its kernel time against the plain copy of
+    the same tensor on the same tile grid (measure_peaks)."""
+    if not peaks or "conformer_tile_copy" not in peaks or wl.name != "c3_dw1d_btc_f32":
+        return None
+    fl = peaks["conformer_tile_copy"]["us_per_launch"]
+    return {"copy_us_per_launch": fl, "kernel_us_per_launch": round(m["kernel_ms_avg"] * 1e3, 2),
+            "kernel_over_copy": round(m["kernel_ms_avg"] * 1e3 / fl, 3)}
 
 
 def main():
@@ -532,6 +663,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured peaks (arithmetic loops, copies)")
+    ap.add_argument("--peaks-only", action="store_true", help="only print the measured peaks")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--backward", choices=["data", "filter"], default=None,
                     help="only time the backward of the Conformer depthwise conv1d (input or filter gradient)")
@@ -564,8 +697,12 @@ def main():
     if args.backward:
         print(json.dumps({"backward": args.backward, "workload": "c3_dw1d_btc_f32",
                           **bwd_entry(WORKLOADS["c3_dw1d_btc_f32"], args.backward, args.steps,
-                                      f"n5_dw1d_bwd_data_f32" if args.backward == "data"
+                                      "n5_dw1d_bwd_data_f32" if args.backward == "data"
                                       else "n6_dw1d_bwd_filter_f32")}))
+        return
+
+    if args.peaks_only:
+        print(json.dumps({"measured_peaks": measure_peaks(WORKLOADS["c3_dw1d_btc_f32"])}))
         return
 
     name = args.workload or HEADLINE
@@ -573,6 +710,7 @@ def main():
     route = route_of(wl)
     m = measure(wl, args.steps, args.warmup)
     kfile = kernel_file(m["kernel"])
+    peaks = None if args.no_peaks else measure_peaks(WORKLOADS["c3_dw1d_btc_f32"])
     f = flops(wl)
     value = f / (m["step_ms"] * 1e-3) / 1e12
     out = {
@@ -593,33 +731,29 @@ def main():
                    "layout": wl.layout, "route": route, "kernel": m["kernel"],
                    "rotation_sets": m["rotation_sets"]},
         "gb_per_s": round(alg_bytes(wl) / (m["step_ms"] * 1e-3) / 1e9, 1),
-        "kernel_ms": {"avg_per_launch": round(m["kernel_ms_avg"], 5), "graph_launches": m["graph_launches"],
-                      "how": "HIP graph of one call per buffer set, replayed; events on the replay stream"},
-        "roofline": roofline(wl, route, m["kernel_ms_avg"], counters_traffic(name, kfile)),
+        "kernel_ms": timing(m),
+        "roofline": roofline(wl, m["kernel"], m["kernel_ms_avg"], counters_traffic(name, kfile), peaks),
     }
+    floor = conformer_floor(wl, m, peaks)
+    if floor:
+        out["tile_copy_floor"] = floor
+    if peaks:
+        out["measured_peaks"] = peaks
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     if not args.no_others:
-        copy_gbs = copy_peak_gbs()
-        out["measured_peaks"] = {"hbm_copy_GBs": copy_gbs,
-                                 "how": "torch device copy of 1 GiB, 10 repetitions; read + write bytes"}
-        out["others"] = {oname: measure_entry(owl, args.steps)
+        out["others"] = {oname: measure_entry(owl, args.steps, peaks)
                          for oname, owl in WORKLOADS.items() if oname != name}
         # Strided depthwise layers (beyond the five workloads above).
-        out["next"] = {oname: measure_entry(owl, args.steps)
+        out["next"] = {oname: measure_entry(owl, args.steps, peaks)
                        for oname, owl in NEXT_WORKLOADS.items() if oname != name}
         # Per-shape route tuning: each route that runs the workload, timed as above,
         # beside the static choice and the route gconv_autotune records.
-        for group in ("others", "next"):
-            for v in out[group].values():
-                v["roofline"] = with_copy_frac(v["roofline"], copy_gbs)
         out["autotune"] = autotune_entries(WORKLOADS, args.steps)
         # Backward of the Conformer depthwise conv1d (same shapes as its forward).
         conf = WORKLOADS["c3_dw1d_btc_f32"]
         for bname, kind in (("n5_dw1d_bwd_data_f32", "data"), ("n6_dw1d_bwd_filter_f32", "filter")):
-            e = bwd_entry(conf, kind, args.steps, bname)
-            e["roofline"] = with_copy_frac(e["roofline"], copy_gbs)
-            out["next"][bname] = e
+            out["next"][bname] = bwd_entry(conf, kind, args.steps, bname, peaks)
     print(json.dumps(out))
 
 

@@ -407,6 +407,31 @@ def test_dw1d_unaligned_filters_use_the_window_kernel():
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == "dw1d_btc_tile"
     assert check(as_f64(y2.cpu()), r, "f32")
+    # x 4 bytes past a 16-byte boundary: the tile kernel with element loads
+    xb = torch.empty(B_ * T * C + 1, device="cuda")
+    xu = xb[1:].view(B_, T, C)
+    xu.copy_(x.cuda())
+    y3 = gc.dwconv1d_btc(xu, gpu(w), gpu(b), stride=1, padding=15, dilation=1)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "dw1d_btc_tile"
+    assert check(as_f64(y3.cpu()), r, "f32")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_dw1d_many_tiles_ragged_steps_and_channels(dt):
+    # 13 x 1500 steps x 200 channels, K = 31: 2444 tiles of 32 steps x 64 channels
+    # (more than the chip holds at once), a ragged last tile in every sequence
+    # (1500 = 46 x 32 + 28) and a last channel block 8 channels wide.
+    B_, T, C, K = 13, 1500, 200, 31
+    x = draw((B_, T, C), 1.0, 7610, dt)
+    w = draw((C, 1, K), 1.0 / K, 8610, dt)
+    b = draw((C,), 0.01, 9610, dt)
+    print(f"dw1d many tiles {dt}", flush=True)
+    r = oracle.dwconv1d_btc(as_f64(x), as_f64(w), as_f64(b), stride=1, padding=15, dilation=1)
+    y = gc.dwconv1d_btc(gpu(x), gpu(w), gpu(b), stride=1, padding=15, dilation=1)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "dw1d_btc_tile"
+    assert check(as_f64(y.cpu()), r, dt)
 
 
 # ---------------------------------------------------------------- backward of the depthwise conv1d
