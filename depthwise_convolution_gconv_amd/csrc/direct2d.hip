@@ -1,4 +1,5 @@
-// direct2d.hip -- direct grouped conv2d (NCHW) on the vector ALUs.
+// direct2d.hip -- direct grouped conv2d (NCHW): two kernels on the vector ALUs and
+// one, for 4-in / 4-out groups, on the 4x4x4 matrix-core instructions.
 //
 // Direct route.  The group index is folded into the launch grid instead of one
 // launch per group: the neon issue "Grouped convolutions" proposes offsetting
@@ -6,7 +7,7 @@
 // its replies note that launching one kernel per group costs a fixed overhead
 // per launch that swamps small layers.
 //
-// Two kernels:
+// Three kernels:
 //  * direct2d_tiled: one workgroup = (image n, group k, block of NB output
 //    channels, TH x TW output tile).  The group's input channels are staged
 //    chunk by chunk into LDS as a zero-filled halo tile (coalesced loads along

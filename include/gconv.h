@@ -104,14 +104,31 @@ typedef enum {
 } gconv_route_t;
 
 /* Output shape of a convolution.  y_shape receives 4 (NCHW, NHWC) or 3 (NTC) values.
- * Returns GCONV_OK, GCONV_ERR_INVALID_ARG or GCONV_ERR_SHAPE; no device work. */
+ * Each spatial or time axis has floor((L + 2p - d(K-1) - 1) / s) + 1 outputs: the
+ * length torch.nn.functional.conv2d gives the layer timed by the poster's script in
+ * the discuss.pytorch.org thread "F.conv2d runs x15 slower in mixed-precision/
+ * half-precision mode" (3x3, padding 3//2: same size), and nn.Conv1d the 'same'
+ * padded depthwise conv of speechbrain issue #2733 (K = 31, padding 15).  Channels:
+ * Cout (NCHW, NHWC) or C (NTC).
+ * Returns GCONV_OK, GCONV_ERR_INVALID_ARG (null pointer, non-positive size, groups
+ * not dividing C and Cout, w not [Cout, C/g, ...]) or GCONV_ERR_SHAPE (an axis with
+ * fewer than one output); no device work. */
 gconv_status_t gconv_out_shape(const int64_t *x_shape, const int64_t *w_shape,
                                const int32_t *stride, const int32_t *pad,
                                const int32_t *dilation, int32_t groups,
                                gconv_layout_t layout, int64_t *y_shape);
 
 /* The route GCONV_ROUTE_AUTO takes for this geometry and dtype (written to
- * *route; never GCONV_ROUTE_AUTO).  Same validation and return codes as
+ * *route; never GCONV_ROUTE_AUTO).  A route recorded by gconv_autotune for this
+ * geometry comes first.  Otherwise NCHW and NHWC layers with enough reduction depth
+ * and filters per group (C/g*KH*KW >= 64 and Cout/g >= 16) whose implicit-GEMM plan
+ * exists take GCONV_ROUTE_IGEMM: the discuss.pytorch.org thread "F.conv2d runs x15
+ * slower in mixed-precision/half-precision mode" traces the slow fp16 grouped conv to
+ * grouped convs not reaching the tensor cores, so these run per group on the matrix
+ * cores.  Smaller groups, where a matrix tile would be mostly padding, and every NTC
+ * call take GCONV_ROUTE_DIRECT, the kernels with the group index in the launch grid
+ * (neon issue "Grouped convolutions", the reply proposing to offset the pointers by
+ * blockIdx times the group stride).  Same validation and return codes as
  * gconv_out_shape; no device work. */
 gconv_status_t gconv_select_route(const int64_t *x_shape, const int64_t *w_shape,
                                   const int32_t *stride, const int32_t *pad,
@@ -260,7 +277,8 @@ void gconv_autotune_clear(void);
  * an empty batch).  The string has static storage. */
 const char *gconv_last_kernel(void);
 
-/* Fixed English text for a status code.  Static storage. */
+/* Fixed English text for a status code.  Static storage.  (The status codes and the
+ * error text are this library's own conventions; the pages define none.) */
 const char *gconv_status_string(gconv_status_t status);
 
 /* Detail of the last non-OK status returned on this host thread ("" if none).
