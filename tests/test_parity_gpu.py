@@ -182,6 +182,8 @@ DW2D_SWEEP = [  # N, C, M (filters per channel), H, W, K, stride, pad, bias
     (4, 16, 1, 50, 40, 3, 1, 1, True),    # tens of workgroups, each crossing plane boundaries
     (2, 32, 1, 64, 44, 3, 2, 1, True),
     (3, 24, 2, 30, 28, 5, 1, 2, True),    # two filters per channel over many workgroups
+    (2, 4, 1, 16, 32, 7, 2, 3, True),     # 7x7, stride 2, 16-byte staging loads in 16-bit
+    (2, 4, 2, 12, 16, 3, 2, 1, False),    # two filters per channel, stride 2, 16-byte runs in 16-bit
     (1, 4, 1, 9, 9, 3, 3, 1, True),       # stride 3: not this kernel (tiled)
     (1, 4, 1, 9, 9, 4, 1, 1, True),       # even filter: not this kernel (tiled)
 ]
