@@ -188,34 +188,63 @@ template <> struct Mfma4<__bf16> {
 template <typename T> __device__ __forceinline__ uint32_t bits16(T v) { return __builtin_bit_cast(uint16_t, v); }
 
 constexpr int kG4Waves = kThreads / 64;
-constexpr int kG4MaxPos = 1024;   // positions of one padded slab image (8 KB of LDS per wave)
+constexpr int kG4MaxPos = 1024;   // positions of one padded slab image
 constexpr int kG4Filters = 36;    // LDS entries of a group's filters: [tap][output][4 inputs]
+constexpr int kG4Step = 62;       // output anchors per pass: lanes 62 and 63 only supply shifted operands
 
-// One wave per (image, group) slab.  Per tap, the 16 MFMA blocks of a wave each
-// take 4 consecutive output positions: A = the group's 4 x 4 filter matrix at that
-// tap (the same in every block), B = the 4 input channels of each position at the
-// tap's offset (one 8-byte LDS entry per lane), D = the 4 outputs of the lane's
-// position.
-// q / d for 0 <= q < 1024 and 1 <= d <= 339 as (q * m) >> 20 with m = ceil(2^20 / d):
+// q / d for 0 <= q < 2048 and 1 <= d <= 400 as (q * m) >> 20 with m = ceil(2^20 / d):
 // exact on that range (checked exhaustively on the host side of the tests).
 __device__ __forceinline__ int g4_div(int q, uint32_t m) { return (int)(((uint32_t)q * m) >> 20); }
 
+// The value lane + 1 holds (lane 63 keeps its own; its result is not used).
+__device__ __forceinline__ uint2 g4_next_lane(uint2 v)
+{
+    return make_uint2((uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0x130, 0xf, 0xf, false),
+                      (uint32_t)__builtin_amdgcn_update_dpp((int)v.y, (int)v.y, 0x130, 0xf, 0xf, false));
+}
+
+// LDS entries (8 bytes each) of one wave's slab: the padded image and the entries
+// past it that the last pass's lanes may read, the filters, and the staged outputs.
+struct G4Lds {
+    int img, total;
+};
+__host__ __device__ inline G4Lds g4_lds(int HP, int WP, int OH, int OW)
+{
+    const int na = (OH - 1) * WP + OW;                           // anchors up to the last output
+    const int npass = (na + kG4Step - 1) / kG4Step;
+    const int reach = kG4Step * (npass - 1) + 64 + 2 * WP + 2;   // entries any lane of any pass reads
+    const int img = ((HP * WP > reach ? HP * WP : reach) + 1) & ~1;   // even: the outputs' entries pair up 16-byte aligned
+    return G4Lds{img, img + kG4Filters + OH * OW};
+}
+
+// One wave per (image, group) slab.  The slab's 4 channels go to LDS as a
+// zero-bordered image of 8-byte entries (4 channels of a position), written in one
+// pass: the image positions from the loaded pairs, the border positions as zeros.
+// Output positions are anchors a = oh * WP + ow of the padded image (the window's
+// top-left entry); tap (kh, kw) of anchor a reads entry a + kh*WP + kw.  Per pass
+// and filter row, one 8-byte LDS read gives each lane its kw = 0 operand and the
+// kw = 1, 2 operands are the next lanes' values (a whole-wave DPP shift by one
+// lane, twice), so a pass of 62 anchors takes 3 reads instead of 9.  Each tap is
+// one 4x4x4 MFMA for the 16 blocks of 4 anchors: A = the group's 4 x 4 filter
+// matrix at that tap, B = the 4 input channels of each anchor, D = the 4 outputs
+// of the lane's anchor, fp32 accumulation.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
             T *__restrict__ y, int G, int H, int W, int OH, int OW, int ph, int pw, int slabs,
-            uint32_t mw, uint32_t mow, int ocs, int okg, int ystage)
+            uint32_t mw, uint32_t mwp, int ocs, int okg, int ystage)
 {
-    extern __shared__ uint2 g4s[];
+    extern __shared__ __attribute__((aligned(16))) uint2 g4s[];
     const int HP = H + 2 * ph, WP = W + 2 * pw;
+    const G4Lds L = g4_lds(HP, WP, OH, OW);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     const int slab = blockIdx.x * kG4Waves + wave;
     if (slab >= slabs) return;   // whole wave; this kernel has no workgroup barrier
-    uint2 *xs = g4s + wave * (HP * WP + kG4Filters + OH * OW);
-    uint2 *fs = xs + HP * WP;
-    uint16_t *ys = reinterpret_cast<uint16_t *>(fs + kG4Filters);   // [4][OH*OW] staged outputs
-    const int HW = H * W, C = 4 * G;
+    uint2 *xs = g4s + wave * L.total;
+    uint2 *fs = xs + L.img;
+    uint2 *ys = fs + kG4Filters;   // [OH*OW][4 outputs] staged outputs
+    const int HW = H * W, C = 4 * G, OHW = OH * OW;
     const int n = slab / G, k = slab - n * G;
     auto wave_sync = [&]() {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -249,10 +278,22 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
     if (!bias) b0 = g4_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
 
-    // The padded image (zero border) with the 4 channels of a position in one
-    // 8-byte entry, and the filters as [tap][output] entries of 4 inputs.
-    for (int i = lane; i < HP * WP; i += 64) xs[i] = make_uint2(0, 0);
-    wave_sync();
+    // The padded image: border positions zero (the ph top and bottom rows, then the
+    // pw left and right columns of every image row), image positions from the pairs.
+    const int nborder = HP * WP - HW;
+    for (int i = lane; i < nborder; i += 64) {
+        int hp, wp;
+        if (i < 2 * ph * WP) {
+            const int r = i / WP;
+            hp = r < ph ? r : H + r;
+            wp = i - r * WP;
+        } else {
+            const int j = i - 2 * ph * WP, r = j / (2 * pw), sd = j - r * (2 * pw);
+            hp = ph + r;
+            wp = sd < pw ? sd : W + sd;
+        }
+        xs[hp * WP + wp] = make_uint2(0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < kMaxL; ++j) {
         const int q = lane + 64 * j;
@@ -283,33 +324,49 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
     for (int t = 0; t < 9; ++t) fa[t] = fs[t * 4 + (lane & 3)];
 
-    T *yg = y + ((int64_t)n * C + k * okg) * OH * OW;   // filter o of the group: channel o*ocs + k*okg
-    for (int p0 = 0; p0 < OH * OW; p0 += 64) {
-        const int p = min(p0 + lane, OH * OW - 1);
-        const int oh = g4_div(p, mow), ow = p - oh * OW;
-        const uint2 *xp = xs + oh * WP + ow;
+    const int na = (OH - 1) * WP + OW;
+    T *yg = y + ((int64_t)n * C + k * okg) * OHW;   // filter o of the group: channel o*ocs + k*okg
+    for (int a0 = 0; a0 < na; a0 += kG4Step) {
+        const int a = a0 + lane;
         g4_f32x4 acc = b0;
 #pragma unroll
-        for (int kh = 0; kh < 3; ++kh)
-#pragma unroll
-            for (int kw = 0; kw < 3; ++kw) acc = Mfma4<T>::run(fa[kh * 3 + kw], xp[kh * WP + kw], acc);
-        if (p0 + lane < OH * OW) {
+        for (int kh = 0; kh < 3; ++kh) {
+            const uint2 v0 = xs[a + kh * WP];
+            const uint2 v1 = g4_next_lane(v0);
+            const uint2 v2 = g4_next_lane(v1);
+            acc = Mfma4<T>::run(fa[kh * 3 + 0], v0, acc);
+            acc = Mfma4<T>::run(fa[kh * 3 + 1], v1, acc);
+            acc = Mfma4<T>::run(fa[kh * 3 + 2], v2, acc);
+        }
+        const int oh = g4_div(a, mwp), ow = a - oh * WP;
+        if (lane < kG4Step && a < na && ow < OW) {
+            const int p = oh * OW + ow;
             if (ystage) {
-#pragma unroll
-                for (int o = 0; o < 4; ++o) ys[o * OH * OW + p] = bits16(from_f32<T>(acc[o]));
+                ys[p] = make_uint2(bits16(from_f32<T>(acc[0])) | (bits16(from_f32<T>(acc[1])) << 16),
+                                   bits16(from_f32<T>(acc[2])) | (bits16(from_f32<T>(acc[3])) << 16));
             } else {
 #pragma unroll
-                for (int o = 0; o < 4; ++o) store_nt(yg + (int64_t)o * ocs * OH * OW + p, from_f32<T>(acc[o]));
+                for (int o = 0; o < 4; ++o) store_nt(yg + (int64_t)o * ocs * OHW + p, from_f32<T>(acc[o]));
             }
         }
     }
     if (ystage) {
-        // The group's 4 output planes are one contiguous, 8-byte aligned run of y:
-        // written as whole 8-byte pieces (the 2-byte stores above would reach HBM as
-        // partial lines, the stores being non-temporal).
+        // The group's 4 output planes are one contiguous, 8-byte aligned run of y
+        // (OH*OW a multiple of 4): each lane takes 4 consecutive positions (LDS
+        // entries of 4 outputs) and writes one 8-byte piece per output plane (2-byte
+        // stores would reach HBM as partial lines, the stores being non-temporal).
         wave_sync();
-        const uint2 *ys2 = reinterpret_cast<const uint2 *>(ys);
-        for (int i = lane; i < OH * OW; i += 64) store_nt(reinterpret_cast<uint2 *>(yg) + i, ys2[i]);
+        for (int i = lane; 4 * i < OHW; i += 64) {
+            const uint4 pa = *reinterpret_cast<const uint4 *>(ys + 4 * i);       // positions 4i, 4i+1
+            const uint4 pb = *reinterpret_cast<const uint4 *>(ys + 4 * i + 2);   // positions 4i+2, 4i+3
+            // output o of a position: the low (o even) or high half of dword o / 2 of its entry
+            const uint32_t lo = 0x05040100u, hi = 0x07060302u;
+            uint2 *yo = reinterpret_cast<uint2 *>(yg) + i;
+            store_nt(yo, make_uint2(__builtin_amdgcn_perm(pa.z, pa.x, lo), __builtin_amdgcn_perm(pb.z, pb.x, lo)));
+            store_nt(yo + OHW / 4, make_uint2(__builtin_amdgcn_perm(pa.z, pa.x, hi), __builtin_amdgcn_perm(pb.z, pb.x, hi)));
+            store_nt(yo + OHW / 2, make_uint2(__builtin_amdgcn_perm(pa.w, pa.y, lo), __builtin_amdgcn_perm(pb.w, pb.y, lo)));
+            store_nt(yo + 3 * (OHW / 4), make_uint2(__builtin_amdgcn_perm(pa.w, pa.y, hi), __builtin_amdgcn_perm(pb.w, pb.y, hi)));
+        }
     }
 }
 
@@ -320,13 +377,14 @@ bool g4_applies(const Conv2dArgs &a)
         return false;
     } else {
         const int64_t Cg = a.C / a.groups, Ng = a.Cout / a.groups;
-        return Cg == 4 && Ng == 4 && a.KH == 3 && a.KW == 3 && a.sh == 1 && a.sw == 1 && a.dh == 1 &&
-               a.dw == 1 && a.ph <= 1 && a.pw <= 1 && (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= kG4MaxPos &&
-               // image, filters and staged outputs of 4 waves within 64 KB of LDS
-               kG4Waves * ((a.H + 2 * a.ph) * (a.W + 2 * a.pw) + kG4Filters + a.OH * a.OW) * 8 <= 64 * 1024 &&
-               a.W <= 339 && a.OW <= 339 &&
-               (a.H * a.W) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 3) == 0 &&
-               a.N * a.groups < (int64_t(1) << 30);
+        if (!(Cg == 4 && Ng == 4 && a.KH == 3 && a.KW == 3 && a.sh == 1 && a.sw == 1 && a.dh == 1 && a.dw == 1 &&
+              a.ph <= 1 && a.pw <= 1 && (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= kG4MaxPos && a.W <= 339 &&
+              (a.H * a.W) % 2 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 3) == 0 &&
+              a.N * a.groups < (int64_t(1) << 30)))
+            return false;
+        // image, filters and staged outputs of 4 waves within 64 KB of LDS
+        const G4Lds L = g4_lds((int)(a.H + 2 * a.ph), (int)(a.W + 2 * a.pw), (int)a.OH, (int)a.OW);
+        return (int64_t)kG4Waves * L.total * 8 <= 64 * 1024;
     }
 }
 
@@ -336,15 +394,17 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
     if constexpr (sizeof(T) == 2) {
         if (!g4_applies<T>(a)) goto tiled;
         const int slabs = (int)(a.N * a.groups);
-        const size_t lds = (size_t)kG4Waves * ((a.H + 2 * a.ph) * (a.W + 2 * a.pw) + kG4Filters + a.OH * a.OW) *
-                           sizeof(uint2);
+        const G4Lds L = g4_lds((int)(a.H + 2 * a.ph), (int)(a.W + 2 * a.pw), (int)a.OH, (int)a.OW);
+        const size_t lds = (size_t)kG4Waves * L.total * sizeof(uint2);
+        const int WP = (int)(a.W + 2 * a.pw);
         *kname = "direct2d_g4";
         hipLaunchKernelGGL((direct2d_g4<T>), dim3((unsigned)ceil_div(slabs, kG4Waves)), dim3(kThreads), lds,
                            a.stream, (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y,
                            (int)a.groups, (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, slabs,
-                           (uint32_t)(((1u << 20) + a.W - 1) / a.W), (uint32_t)(((1u << 20) + a.OW - 1) / a.OW),
+                           (uint32_t)(((1u << 20) + a.W - 1) / a.W), (uint32_t)(((1u << 20) + WP - 1) / WP),
                            a.interleaved ? (int)a.groups : 1, a.interleaved ? 1 : 4,
-                           (!a.interleaved && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0) ? 1 : 0);
+                           (!a.interleaved && (reinterpret_cast<uintptr_t>(a.y) & 7) == 0 &&
+                            (a.OH * a.OW) % 4 == 0) ? 1 : 0);
         return hipGetLastError();
     }
 tiled:

@@ -52,10 +52,10 @@ def test_fastdiv_is_exact_below_2_pow_31():
 
 
 def test_small_multiply_shift_division_is_exact():
-    # The fully grouped 3x3 kernel divides positions q < 1024 by an image width
-    # d <= 339 as (q * ceil(2^20 / d)) >> 20; every pair of that range is checked.
+    # The fully grouped 3x3 kernel divides positions q < 2048 by an image row width
+    # d <= 400 as (q * ceil(2^20 / d)) >> 20; every pair of that range is checked.
     import numpy as np
-    q = np.arange(1024, dtype=np.uint64)
-    for d in range(1, 340):
+    q = np.arange(2048, dtype=np.uint64)
+    for d in range(1, 401):
         m = np.uint64(((1 << 20) + d - 1) // d)
         assert np.array_equal((q * m) >> np.uint64(20), q // np.uint64(d)), d

@@ -111,6 +111,41 @@ def test_sweep_vs_oracle(ci, dt):
         assert normwise(as_f64(outs["igemm"].cpu()), as_f64(outs["direct"].cpu())) <= 2 * REG[dt]
 
 
+# The 4-in / 4-out kernel (direct2d_g4, 16-bit, 3x3, stride 1): the operands of
+# taps kw = 1, 2 come from the neighbouring lanes, 62 output anchors per pass.
+G4_CASES = [  # N, C, H, W, pad (h, w), bias, y offset in elements
+    (2, 16, 15, 14, (1, 1), True, 0),     # 210 outputs per plane: element stores
+    (1, 32, 28, 28, (1, 1), True, 0),     # 30 x 30 padded image, 14 passes
+    (2, 16, 10, 6, (1, 0), False, 0),     # padding rows only
+    (2, 16, 6, 10, (0, 1), True, 0),      # padding columns only
+    (3, 16, 7, 10, (1, 1), True, 1),      # y 2 bytes past alignment: element stores
+    (2, 64, 14, 14, (1, 1), True, 0),     # the fully grouped workload's planes
+    (1, 8, 2, 2, (1, 1), True, 0),        # 2 x 2 image: one pass, most lanes idle
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(G4_CASES)))
+def test_g4_kernel_vs_oracle(ci, dt):
+    N, C, H, W, pad, has_b, yoff = G4_CASES[ci]
+    g = C // 4
+    seed = 30 * ci + {"f16": 1, "bf16": 2}[dt]
+    x = draw((N, C, H, W), 1.0, 7300 + seed, dt)
+    w = draw((C, 4, 3, 3), 1.0 / 36, 8300 + seed, dt)
+    b = draw((C,), 0.01, 9300 + seed, dt) if has_b else None
+    print(f"g4 case {G4_CASES[ci]} {dt}", flush=True)
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=1, padding=pad, dilation=1, groups=g)
+    n = r.size
+    buf = torch.full((n + 8,), float("nan"), dtype=x.dtype, device="cuda")
+    y = buf[yoff:yoff + n].view(r.shape)
+    gc.gconv_fwd(gpu(x), gpu(w), gpu(b), 1, pad, 1, g, "nchw", y=y)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == "direct2d_g4"
+    yc = as_f64(y.cpu())
+    assert normwise(yc, r) <= TOL[dt] and normwise(yc, r) <= REG[dt], normwise(yc, r)
+    assert bool(torch.isnan(buf[yoff + n:]).all()) and (yoff == 0 or bool(torch.isnan(buf[:yoff]).all()))
+
+
 # More tiles than the chip runs workgroups (256), so every workgroup of the implicit
 # GEMM takes several tiles in turn; with at most 64 filters per group a tile's outputs
 # are stored while the next tile computes.  Compared in full.
