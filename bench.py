@@ -14,9 +14,11 @@ Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize().  Inputs are seeded synthetic tensors already resident
 in HBM; successive steps rotate over enough copies of the input/output buffers
 (>= 512 MB in total) that a step never finds its operands in the 256 MB
-Infinity Cache.  The same calls are also captured into a HIP graph (one per
-buffer set) and replayed; HIP events on the replay stream give the average
-device duration of one launch, which the roofline object uses.
+Infinity Cache.  The same calls are also captured into a HIP graph (the buffer
+sets in turn, at least 16 launches) and replayed, one HIP event pair on the
+replay stream around each replay: each replay is one sample of the per-launch
+device time (median, p10, p90 reported), and their mean is what the roofline
+object uses.  A hot-cache figure repeats the call on one buffer set.
 
 Prints ONE JSON line.  `value` is effective TFLOP/s (2*N*Cout*OH*OW*C/g*KH*KW per
 step, padding taps included, divided by the step time).
@@ -161,11 +163,14 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20, route=None):
 
     step_ms: `steps` back-to-back calls from Python (host validation, route
     selection and launch included), bracketed by one pair of HIP events on the
-    launch stream.  kernel_ms: the same calls captured once into a HIP graph (one
-    call per buffer set) and replayed until about `steps` launches ran, bracketed
-    by HIP events on the replay stream; that is the average device duration of
-    one launch without the host in the loop.  The graph's first replay is checked
-    bit for bit against the eager result of the same buffer set."""
+    launch stream.  kernel samples: the same calls captured once into a HIP graph
+    (the buffer sets in turn, at least 16 launches) and replayed at least 20
+    times (about `steps` launches), one pair of HIP events on the replay stream
+    around each replay; each sample is the average device duration of one launch
+    of that replay, without the host in the loop.  hot samples: the call on one
+    buffer set repeated back to back in a graph of its own.  The graph's first
+    replay is checked bit for bit against the eager result of the same buffer
+    set."""
     import torch
     import depthwise_convolution_gconv_amd as gc
     from depthwise_convolution_gconv_amd.workloads import make_inputs
@@ -207,31 +212,33 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20, route=None):
     wall = time.perf_counter() - wall0
     step_ms = t_start.elapsed_time(t_end) / steps
 
-    # graph replay: one launch per buffer set, no host work in between
+    # graph replay: the buffer sets in turn, at least 16 launches per graph (so that
+    # the start of a replay is spread over as many launches), no host work in between
     gstream = torch.cuda.Stream(dev)
     gcalls = [gc.PreparedCall(*t, wl.stride, wl.pad, wl.dilation, wl.groups, wl.layout, route=route,
                               stream=gstream) for t in sets]
+    glaunches = nsets * math.ceil(16 / nsets)
     graph = torch.cuda.CUDAGraph()
     outs[0].zero_()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph, stream=gstream):
-        for c in gcalls:
-            c()
+        for i in range(glaunches):
+            gcalls[i % nsets]()
     with torch.cuda.stream(gstream):
         graph.replay()
     torch.cuda.synchronize()
     if not torch.equal(outs[0], ref0):
         raise RuntimeError("graph replay differs from the eager result")
     # One event pair per replay: each replay is one sample (the average launch of
-    # one pass over the buffer sets), at least 20 of them.
-    reps = max(20, round(steps / nsets))
-    cold = replay_samples(graph, gstream, reps, nsets)
+    # its passes over the buffer sets), at least 20 of them.
+    reps = max(20, round(steps / glaunches))
+    cold = replay_samples(graph, gstream, reps, glaunches)
     del graph
     # Hot cache: the call on one buffer set, repeated back to back, so its operands
     # stay in the L2 / Infinity Cache between launches.
     # The graph holds several launches, so that one replay's own start-up cost is
     # spread as it is for the cold graph.
-    hot_n = max(nsets, 8)
+    hot_n = max(nsets, 16)
     hot_graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(hot_graph, stream=gstream):
         for _ in range(hot_n):
@@ -242,7 +249,7 @@ def measure(wl, steps, warmup, rotate_bytes=512 << 20, route=None):
     hot = replay_samples(hot_graph, gstream, max(20, round(steps / hot_n)), hot_n)
     del hot_graph
     return {"step_ms": step_ms, "kernel_ms_avg": sum(cold) / len(cold), "kernel_samples": cold,
-            "hot_samples": hot, "graph_launches": reps * nsets, "wall_s": wall, "kernel": kernel,
+            "hot_samples": hot, "graph_launches": reps * glaunches, "wall_s": wall, "kernel": kernel,
             "rotation_sets": nsets}
 
 
@@ -625,8 +632,9 @@ def timing(m):
     return {"avg_per_launch": round(m["kernel_ms_avg"], 5), "cold": stats(m["kernel_samples"]),
             "hot": stats(m["hot_samples"]), "graph_launches": m["graph_launches"],
             "rotation_sets": m["rotation_sets"],
-            "how": "HIP graph of one call per cold buffer set, one event pair per replay on the replay "
-                   "stream (cold); one buffer set replayed back to back (hot, operands in L2 / Infinity Cache)"}
+            "how": "HIP graph of the cold buffer sets in turn (at least 16 launches), one event pair per "
+                   "replay on the replay stream (cold); one buffer set repeated back to back (hot, operands "
+                   "in L2 / Infinity Cache)"}
 
 
 def measure_entry(wl, steps, peaks=None):
