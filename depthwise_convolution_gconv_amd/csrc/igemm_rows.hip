@@ -62,11 +62,17 @@ constexpr int kThreads = 256;
 constexpr int kLdsUnits = 160 * 1024 / 16;   // 16-byte units of LDS per workgroup (one per CU)
 constexpr int kBlockUnits = 576;             // one 32-filter block's chunk: 32 x 16 ch x 9 taps x 2 B
 constexpr int kSubUnits = 288;               // one 16-filter half of it
+// LDS stride of a 16-filter half-block in the filter image: 288 units with 128
+// filters per tile; 320 with 64, where each wave stages one half-block with 5
+// copy instructions of 64 units (the last one's extra lanes write zeros into the
+// 32 padding units, not into the next half-block).
+template <int FW> constexpr int kSub = FW == 1 ? 320 : kSubUnits;
+template <int FW> constexpr int kBlk = 2 * kSub<FW>;                    // a 32-filter block
 constexpr int kRun = 8;                      // output columns per run
 constexpr int kWin = kRun + 2;               // window positions of one filter row (3 taps)
 constexpr uint32_t kOOB = 0x80000000u;       // byte offset past num_records: loads return 0
 
-template <int FW> constexpr int kFU = 2 * FW * kBlockUnits;              // filter units per stage
+template <int FW> constexpr int kFU = 2 * FW * kBlk<FW>;                 // filter units per stage
 template <int FW> constexpr int kHU = (kLdsUnits - 2 * kFU<FW>) / 2;     // halo units per stage
 
 template <typename T> struct Mfma;
@@ -174,6 +180,7 @@ struct RowsGeom {
     int sh, ph, pw, dh;
     int Hp;                  // H + 2*ph: rows of one zero-padded image in the virtual row space
     int RPR, NRUN;           // runs per output row; N*OH*RPR runs in all (< 2^31)
+    int RTU;                 // runs a tile covers (at most its 32*PW lanes): whole rows or images
     int NR, SROW;            // halo rows; slots per halo row (a multiple of 8)
     int kh_units;            // unit step of one filter row in the halo: 17 * dh * SROW / 8
     int nseg, xtasks;        // VW-wide segments per input row; staging tasks = 2*NR*nseg
@@ -194,7 +201,12 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     constexpr int PW = 4 / FW;               // waves across the runs
     constexpr int RT = 32 * PW;              // runs per tile
     constexpr int DW = VW / 2;               // dwords per staged row segment
-    constexpr int NTW = BN / 32;             // waves that stage a 32-filter block each
+    // Each wave stages a 32-filter block (128 filters per tile) or a 16-filter
+    // half-block (64): FPW filters, NFC copy instructions, SW units of the image.
+    constexpr int FPW = 32 * FW / 2;
+    constexpr int NFC = FW == 1 ? 5 : 9;
+    constexpr int SW = FW == 1 ? kSub<1> : kBlk<2>;
+    constexpr int SUB = kSub<FW>, BLK = kBlk<FW>;
     constexpr int FU = kFU<FW>;
     constexpr int HU = kHU<FW>;
     // Input halo and filter image, two pipeline stages each, as four LDS arrays: the
@@ -248,19 +260,21 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         }
     }
     // Transpose: lane = (filter tf, channel half th) of the wave's block.
-    const int tf = lane >> 1, th = lane & 1;
+    // (With 16-filter half-blocks, lanes 32-63 repeat lanes 0-31: the same reads and
+    // the same values written to the same units.)
+    const int tf = (lane >> 1) & (FPW - 1), th = lane & 1;
     const int traw = 18 * tf + 9 * th;                                    // first raw unit
-    const int tdst = (tf >> 4) * kSubUnits + fimg_unit(tf & 15, th);      // tap-0 unit
+    const int tdst = (tf >> 4) * SUB + fimg_unit(tf & 15, th);            // tap-0 unit
     // A operand: filter fwv*64 + nb*32 + l32, channel half hf, tap t at
-    // aub + nb*576 + t*32.
-    const int aub = (fwv * 4 + (l32 >> 4)) * kSubUnits + fimg_unit(l32 & 15, hf);
+    // aub + nb*BLK + t*32.
+    const int aub = (fwv * 4 + (l32 >> 4)) * SUB + fimg_unit(l32 & 15, hf);
 
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(w, g.w_bytes);
     const __amdgpu_buffer_rsrc_t br = make_rsrc(bias, g.b_bytes);
 
     struct TileState {
         int k, nt, run0, R_lo, n_first;
-        int fbase;   // w row of this wave's first staged filter (k*Ng + nt*BN + 32*wave)
+        int fbase;   // w row of this wave's first staged filter (k*Ng + nt*BN + FPW*wave)
         int nfw;     // filters of this wave's staged block that exist
         __amdgpu_buffer_rsrc_t xr;
         uint32_t xvo[XR];
@@ -271,13 +285,13 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         const int mt = fmod_q(t, bq, g.fd_mt);
         s.k = fdiv(bq, g.fd_nt);
         s.nt = fmod_q(bq, s.k, g.fd_nt);
-        s.run0 = mt * RT;
+        s.run0 = mt * g.RTU;
         const int Rf = fdiv(s.run0, g.fd_rpr);          // first output row (n*OH + oh)
         s.n_first = fdiv(Rf, g.fd_oh);
         const int oh_first = fmod_q(Rf, s.n_first, g.fd_oh);
         s.R_lo = s.n_first * g.Hp + oh_first * g.sh;
-        s.fbase = s.k * g.Ng + s.nt * BN + 32 * wave;
-        s.nfw = min(32, max(0, g.Ng - s.nt * BN - 32 * wave));
+        s.fbase = s.k * g.Ng + s.nt * BN + FPW * wave;
+        s.nfw = min(FPW, max(0, g.Ng - s.nt * BN - FPW * wave));
         s.xr = make_rsrc(x + ((int64_t)s.n_first * g.C + (int64_t)s.k * g.Cg) * HW, 0x7fffffffu);
 #pragma unroll
         for (int i = 0; i < XR; ++i) {
@@ -310,7 +324,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         const int q = 64 * i + lane;
         const int pf = (q * 3641) >> 16;    // q / 18 for q < 576
         const uint32_t off = pf < s.nfw ? (uint32_t)(pf * g.Cg * 18 + 16 * (q - 18 * pf)) : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, GCONV_LDS(fim(stg) + kBlockUnits * wave + 64 * i), 16, off,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, GCONV_LDS(fim(stg) + SW * wave + 64 * i), 16, off,
                                                  (uint32_t)(s.fbase * g.Cg + ch * 16) * 18, 0, 0);
     };
     // Input load j (< 8*XR) of one pipeline step into registers: task j/8, channel row j%8.
@@ -324,7 +338,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     // the 8 channels at tap t.  Every read of the wave comes before its first write
     // (the writes land on units other lanes read).
     auto transpose_read = [&](auto stg, int u) {
-        const uint4 v = fim(stg)[kBlockUnits * wave + traw + u];
+        const uint4 v = fim(stg)[SW * wave + traw + u];
         E[4 * u] = v.x; E[4 * u + 1] = v.y; E[4 * u + 2] = v.z; E[4 * u + 3] = v.w;
     };
     auto transpose_write = [&](auto stg, int t) {
@@ -337,7 +351,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             const uint32_t sel = ((b + 1) << 24) | (b << 16) | ((a + 1) << 8) | a;
             o[q] = __builtin_amdgcn_perm(E[e1 >> 1], E[e0 >> 1], sel);
         }
-        fim(stg)[kBlockUnits * wave + tdst + 32 * t] = make_uint4(o[0], o[1], o[2], o[3]);
+        fim(stg)[SW * wave + tdst + 32 * t] = make_uint4(o[0], o[1], o[2], o[3]);
     };
     // Staging write o (< XR*VW) into stage stg: column o % VW of task o / VW as one
     // unit of 8 channels; a thread without that task writes the spare unit.
@@ -368,31 +382,29 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     }
 
     TileState ts = tile_state(tile);
-    if (NTW == 4 || wave < NTW) {
 #pragma unroll
-        for (int i = 0; i < 9; ++i) filter_copy(ts, 0, S0{}, i);
-    }
+    for (int i = 0; i < NFC; ++i) filter_copy(ts, 0, S0{}, i);
 #pragma unroll
     for (int j = 0; j < 8 * XR; ++j) input_load(S0{}, ts, 0, j);
 #pragma unroll
     for (int j = 0; j < 8 * XR; ++j) input_load(S1{}, ts, 1, j);   // step 1, written during chunk 0
-    if (NTW == 4 || wave < NTW) {
 #pragma unroll
-        for (int u = 0; u < 9; ++u) transpose_read(S0{}, u);
+    for (int u = 0; u < 9; ++u) transpose_read(S0{}, u);
 #pragma unroll
-        for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
+    for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
 #pragma unroll
-        for (int t = 0; t < 9; ++t) transpose_write(S0{}, t);
-    }
+    for (int t = 0; t < 9; ++t) transpose_write(S0{}, t);
 #pragma unroll
     for (int o = 0; o < XR * VW; ++o) input_write(S0{}, S0{}, o);
     __syncthreads();
 
     for (;;) {
         // This lane's run and its halo and output addresses.
+        // (Lanes past the tile's runs or the last run redo the tile's last run, inside
+        // its halo, and store nothing.)
         const int run = ts.run0 + pwv * 32 + l32;
-        const bool run_ok = run < g.NRUN;
-        const int rc = min(run, g.NRUN - 1);
+        const bool run_ok = pwv * 32 + l32 < g.RTU && run < g.NRUN;
+        const int rc = min(run, min(ts.run0 + g.RTU, g.NRUN) - 1);
         const int R = fdiv(rc, g.fd_rpr);
         const int jr = fmod_q(rc, R, g.fd_rpr);
         const int n = fdiv(R, g.fd_oh);
@@ -432,7 +444,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             // First the operands of the first MFMAs, then the rest of the window.
             af[0][0] = fs[aub];
             win[0] = hs[ub];
-            af[0][1] = fs[aub + kBlockUnits];
+            af[0][1] = fs[aub + BLK];
 #pragma unroll
             for (int e = 1; e < kWin; ++e) win[e] = hs[ub + 2 * e + (e >> 3)];
             __builtin_amdgcn_sched_barrier(0);
@@ -449,7 +461,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             //    the filter copies (from L2);
             //  * taps 6-8, odd slots: the input staging writes; tap 6: the transpose
             //    reads; taps 7-8: its 9 unit writes.
-            constexpr int NVM = (NTW == 4 ? 9 : 0) + 8 * XR;   // global loads per step
+            constexpr int NVM = NFC + 8 * XR;   // global loads per step
 #pragma unroll
             for (int t = 0; t < 9; ++t) {
                 const int kh = t / 3, kw = t % 3;
@@ -457,7 +469,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                 for (int i = 0; i < 16; ++i) {
                     const int mb = i >> 1, nb = i & 1;
                     acc[nb][mb] = Mfma<T>::run(af[t & 1][nb], win[mb + kw], acc[nb][mb]);
-                    if (i < 2 && t < 8) af[(t + 1) & 1][i] = fs[aub + i * kBlockUnits + 32 * (t + 1)];
+                    if (i < 2 && t < 8) af[(t + 1) & 1][i] = fs[aub + i * BLK + 32 * (t + 1)];
                     if (kh < 2 && nb == 1 && (kw == 2 || mb == 0)) {
                         const int e = mb + kw;   // its last use in this row was this MFMA
                         win[e] = hs[ub + (kh + 1) * g.kh_units + 2 * e + (e >> 3)];
@@ -468,37 +480,21 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                     if (sl >= 0 && (sl & 1) == 0 && sl / 2 < NVM) {
                         const int o = sl / 2;
                         if (o < 8 * XR) input_load(cur, src2, nch2, o);
-                        else if (NTW == 4) filter_copy(src, nch, nst, o - 8 * XR);
+                        else filter_copy(src, nch, nst, o - 8 * XR);
                     }
-                    if (NTW == 4) {
-                        if (t == 6 && i >= 2 && i <= 10) transpose_read(nst, i - 2);
-                        if (t == 7 && i == 0) {
-                            // every transpose read has returned before the first write
+                    if (t == 6 && i >= 2 && i <= 10) transpose_read(nst, i - 2);
+                    if (t == 7 && i == 0) {
+                        // every transpose read has returned before the first write
 #pragma unroll
-                            for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
-                        }
-                        if ((t == 7 && i % 4 == 0) || (t == 8 && i % 3 == 0 && i < 15))
-                            transpose_write(nst, t == 7 ? i / 4 : 4 + i / 3);
+                        for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
                     }
+                    if ((t == 7 && i % 4 == 0) || (t == 8 && i % 3 == 0 && i < 15))
+                        transpose_write(nst, t == 7 ? i / 4 : 4 + i / 3);
                     if (t >= 6 && (i & 1) == 1) {
                         const int ow = (t - 6) * 8 + i / 2;
                         if (ow < XR * VW) input_write(nst, nst, ow);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            if (NTW != 4) {
-                // Fewer staging waves than waves: the filter copy and its transpose are
-                // done by waves 0 .. NTW-1 outside the scheduled taps.
-                if (wave < NTW) {
-#pragma unroll
-                    for (int i = 0; i < 9; ++i) filter_copy(src, nch, nst, i);
-#pragma unroll
-                    for (int u = 0; u < 9; ++u) transpose_read(nst, u);
-#pragma unroll
-                    for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
-#pragma unroll
-                    for (int tt = 0; tt < 9; ++tt) transpose_write(nst, tt);
                 }
             }
             __syncthreads();
@@ -606,11 +602,11 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
         if (g.Ng % 4 != 0 || (reinterpret_cast<uintptr_t>(a.bias) & 7) != 0) return pl;
         g.b_bytes = (uint32_t)(a.Cout * 2);
     }
-    // 64 filters per wave and two waves across the filters.  (With at most 64 filters
-    // per group the filter copy would be done by 2 of the 4 waves outside the
-    // scheduled taps; such layers stay on the implicit GEMM of igemm.hip.)
-    if (g.Ng <= 64) return pl;
-    pl.FW = 2;
+    // 64 filters per wave: two waves across the filters for more than 64 filters per
+    // group, one for 33 to 64 (fewer filters per group stay on the implicit GEMM of
+    // igemm.hip, whose tiles are narrower).
+    if (g.Ng <= 32) return pl;
+    pl.FW = g.Ng > 64 ? 2 : 1;
     const int RT = 32 * (4 / pl.FW);
     g.Hp = (int)(a.H + 2 * a.ph);
     g.RPR = (int)ceil_div(a.OW, 8);
@@ -618,11 +614,22 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
     if (NRUN >= (int64_t(1) << 31) - 2 * RT || a.N * (int64_t)g.Hp + 3 * (int64_t)a.dh + 1024 >= (int64_t(1) << 31))
         return pl;
     g.NRUN = (int)NRUN;
-    // Output rows a tile's RT runs can touch, image boundaries among them, and the
+    // Runs per tile: whole images when they fill at least 7/8 of the RT lanes, else
+    // whole rows when they do, else all RT.  (Whole images need no halo rows beyond
+    // their own, and no output line is shared by two tiles.)
+    const int64_t img = (int64_t)g.OH * g.RPR;
+    int64_t RTU = RT;
+    if (img <= RT && 8 * (RT / img * img) >= 7 * RT) RTU = RT / img * img;
+    else if (g.RPR <= RT && 8 * (RT / g.RPR * g.RPR) >= 7 * RT) RTU = RT / g.RPR * g.RPR;
+    g.RTU = (int)RTU;
+    // Output rows a tile's RTU runs can touch, image boundaries among them, and the
     // resulting bound on the padded input rows of its halo.
-    const bool aligned = g.RPR <= RT && RT % g.RPR == 0;
-    const int64_t V = aligned ? RT / g.RPR : (RT - 1) / g.RPR + 2;
-    const int64_t crossings = V <= 1 ? 0 : (aligned && g.OH % V == 0) ? 0 : (V - 2) / g.OH + 1;
+    const bool aligned = RTU % g.RPR == 0;
+    const int64_t V = aligned ? RTU / g.RPR : (RTU - 1) / g.RPR + 2;
+    const int64_t crossings = V <= 1                           ? 0
+                              : aligned && g.OH % V == 0       ? 0
+                              : aligned && V % g.OH == 0       ? V / g.OH - 1   // whole images
+                                                               : (V - 2) / g.OH + 1;
     const int64_t gap = std::max<int64_t>(0, (int64_t)g.Hp - (int64_t)g.OH * g.sh);
     int64_t NR = (V - 1) * g.sh + crossings * gap + 2 * (int64_t)g.dh + 1;
     NR = std::min<int64_t>(NR, a.N * (int64_t)g.Hp);
@@ -656,7 +663,7 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
     g.sg = (g.OW % 8 == 0 && ya % 16 == 0) ? 8 : (g.OW % 4 == 0 && ya % 8 == 0) ? 4 : 1;
     g.ocs = a.interleaved ? g.groups : 1;
     g.okg = a.interleaved ? 1 : g.Ng;
-    g.m_tiles = (int)ceil_div(NRUN, RT);
+    g.m_tiles = (int)ceil_div(NRUN, RTU);
     g.n_tiles = (int)ceil_div(g.Ng, 64 * pl.FW);
     g.nchunks = g.Cg / 16;
     const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.groups;
@@ -693,8 +700,12 @@ hipError_t run_typed(const Conv2dArgs &a, const RowsPlan &pl)
 {
     // (XR, VW) = (1, 8) or (at most 2, 4): 8 channel rows x 16 bytes of staged input
     // per thread, at most.
-    if (pl.g.sg == 8) return pl.VW == 8 ? run<T, 2, 1, 8, true>(a, pl) : run<T, 2, 2, 4, true>(a, pl);
-    return pl.VW == 8 ? run<T, 2, 1, 8, false>(a, pl) : run<T, 2, 2, 4, false>(a, pl);
+    auto pick = [&](auto fw) -> hipError_t {
+        constexpr int FW = decltype(fw)::value;
+        if (pl.g.sg == 8) return pl.VW == 8 ? run<T, FW, 1, 8, true>(a, pl) : run<T, FW, 2, 4, true>(a, pl);
+        return pl.VW == 8 ? run<T, FW, 1, 8, false>(a, pl) : run<T, FW, 2, 4, false>(a, pl);
+    };
+    return pl.FW == 2 ? pick(std::integral_constant<int, 2>{}) : pick(std::integral_constant<int, 1>{});
 }
 
 }  // namespace
