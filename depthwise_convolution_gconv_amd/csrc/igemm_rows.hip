@@ -70,7 +70,8 @@ template <int FW> constexpr int kSub = FW == 1 ? 320 : kSubUnits;
 template <int FW> constexpr int kBlk = 2 * kSub<FW>;                    // a 32-filter block
 constexpr int kRun = 8;                      // output columns per run
 constexpr int kWin = kRun + 2;               // window positions of one filter row (3 taps)
-constexpr uint32_t kOOB = 0x80000000u;       // byte offset past num_records: loads return 0
+constexpr uint32_t kOOB = 0x80000000u;       // byte offset past num_records: loads return 0, stores drop
+constexpr int kNT = 2;                       // cache policy of the output stores: non-temporal
 
 template <int FW> constexpr int kFU = 2 * FW * kBlk<FW>;                 // filter units per stage
 template <int FW> constexpr int kHU = (kLdsUnits - 2 * kFU<FW>) / 2;     // halo units per stage
@@ -383,6 +384,8 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 
     TileState ts = tile_state(tile);
 #pragma unroll
+    for (int i = 0; i < NFC; ++i) filter_copy(ts, 1, S1{}, i);   // chunk 1's (issued first: see below)
+#pragma unroll
     for (int i = 0; i < NFC; ++i) filter_copy(ts, 0, S0{}, i);
 #pragma unroll
     for (int j = 0; j < 8 * XR; ++j) input_load(S0{}, ts, 0, j);
@@ -398,7 +401,18 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     for (int o = 0; o < XR * VW; ++o) input_write(S0{}, S0{}, o);
     __syncthreads();
 
-    for (;;) {
+    // One tile: its chunks, then its output stores.
+    //
+    // Vector memory counts loads and stores in one in-order counter, so a wait for a
+    // load also waits for every store issued before it.  The filter copies that the
+    // transposes of a tile's first chunk wait for (chunk 1's filters) are therefore
+    // issued before the previous tile's output stores, not during the first chunk:
+    // that chunk then waits for its copies but for at most the oldest of the stores,
+    // and computes while the rest drain.  The first tile runs as a copy of its own, so
+    // that the wait counts the compiler derives at the loop's entry are those of a
+    // tile that follows another (an entry straight from the prologue, where no stores
+    // follow the copies, would set them for every tile).
+    auto tile_body = [&]() __attribute__((always_inline)) -> bool {
         // This lane's run and its halo and output addresses.
         // (Lanes past the tile's runs or the last run redo the tile's last run, inside
         // its halo, and store nothing.)
@@ -426,8 +440,9 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         // One chunk: computes from stage CUR and stages the next pipeline step into
         // the other one (instantiated once per stage, so every LDS array is named
         // statically).
-        auto chunk = [&](auto cur, int ch) {
+        auto chunk = [&](auto cur, int ch, auto first) {
             using CUR = decltype(cur);
+            constexpr bool FIRST = decltype(first)::value;   // copies no filters
             using NXT = std::integral_constant<int, 1 - CUR::value>;
             const NXT nst{};
             const bool last = ch + 1 == g.nchunks;
@@ -461,7 +476,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             //    the filter copies (from L2);
             //  * taps 6-8, odd slots: the input staging writes; tap 6: the transpose
             //    reads; taps 7-8: its 9 unit writes.
-            constexpr int NVM = NFC + 8 * XR;   // global loads per step
+            constexpr int NVM = (FIRST ? 0 : NFC) + 8 * XR;   // global loads per step
 #pragma unroll
             for (int t = 0; t < 9; ++t) {
                 const int kh = t / 3, kw = t % 3;
@@ -480,7 +495,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
                     if (sl >= 0 && (sl & 1) == 0 && sl / 2 < NVM) {
                         const int o = sl / 2;
                         if (o < 8 * XR) input_load(cur, src2, nch2, o);
-                        else filter_copy(src, nch, nst, o - 8 * XR);
+                        else if (!FIRST) filter_copy(src, nch, nst, o - 8 * XR);
                     }
                     if (t == 6 && i >= 2 && i <= 10) transpose_read(nst, i - 2);
                     if (t == 7 && i == 0) {
@@ -500,22 +515,35 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             __syncthreads();
         };
         // An even number of chunks (planned), so every tile starts on stage 0.
-        for (int ch = 0; ch < g.nchunks; ch += 2) {
-            chunk(S0{}, ch);
-            chunk(S1{}, ch + 1);
+        chunk(S0{}, 0, std::true_type{});
+        chunk(S1{}, 1, std::false_type{});
+        for (int ch = 2; ch < g.nchunks; ch += 2) {
+            chunk(S0{}, ch, std::false_type{});
+            chunk(S1{}, ch + 1, std::false_type{});
+        }
+        // The next tile's chunk-1 filters into stage 1, free since the barrier above.
+        // (None after the last tile: no copy into LDS may be in flight at the end.)
+        if (has_next) {
+#pragma unroll
+            for (int i = 0; i < NFC; ++i) filter_copy(nts, 1, S1{}, i);
         }
 
         // Epilogue: + bias in fp32, one rounding to T, stored straight from the
-        // accumulators: 8 consecutive outputs of one filter per lane and row.
-        if (run_ok) {
+        // accumulators: 8 consecutive outputs of one filter per lane and row.  The
+        // stores go through a buffer resource based at the tile's first image, and a
+        // lane or row with nothing to store gives an offset past its end, which the
+        // hardware drops: every lane issues the same stores and no branch skips them,
+        // so the wait counts derived after the epilogue hold on every path.
+        {
             // Filters this lane's rows cover: the wave's 64 from fb0, those below Ng.
             const int fb0 = ts.nt * BN + fwv * 64;
-            // The output addresses are formed here, not hoisted to the tile start where
-            // they would hold registers through the K loop.
-            int ybase = oh * g.OW + ow0;
-            int64_t fstep = (int64_t)g.ocs * OHW;   // between consecutive filters
+            const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + (int64_t)ts.n_first * g.Cout * OHW, 0x7fffffffu);
+            // Element offset of the lane's first output of filter fb0 from that image
+            // (below 2^30, planned), or -1.  Formed here, not hoisted to the tile start
+            // where it would hold registers through the K loop.
+            int ybase = run_ok ? ((n - ts.n_first) * g.Cout + fb0 * g.ocs + ts.k * g.okg) * OHW + oh * g.OW + ow0 : -1;
+            int fstep = g.ocs * OHW;   // between consecutive filters
             asm volatile("" : "+v"(ybase), "+s"(fstep));
-            T *yrow = y + ((int64_t)n * g.Cout + (int64_t)fb0 * g.ocs + (int64_t)ts.k * g.okg) * OHW + ybase;
             auto store_rows = [&](auto has_bias) {
                 uint2 bz[2][4];
                 if constexpr (decltype(has_bias)::value) {
@@ -533,7 +561,8 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = nb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-                        if (fb0 + row >= g.Ng) continue;
+                        const bool ok = ybase >= 0 && fb0 + row < g.Ng;
+                        const uint32_t yo = ok ? (uint32_t)(ybase + row * fstep) * 2u : kOOB;
                         float v[8];
 #pragma unroll
                         for (int mb = 0; mb < 8; ++mb) v[mb] = acc_read(acc[nb][mb][r]);
@@ -543,20 +572,22 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 #pragma unroll
                             for (int mb = 0; mb < 8; ++mb) v[mb] += b0;
                         }
-                        T *yp = yrow + row * fstep;
                         if constexpr (SG8) {
-                            store_nt(reinterpret_cast<uint4 *>(yp),
-                                     make_uint4(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]), pack2<T>(v[4], v[5]),
-                                                pack2<T>(v[6], v[7])));
+                            const uint4 o = make_uint4(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]),
+                                                       pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7]));
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(gconv_u32x4, o), yr, yo, 0, kNT);
                         } else if (g.sg == 4) {
-                            store_nt(reinterpret_cast<uint2 *>(yp), make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3])));
-                            if (ow0 + 4 < g.OW)
-                                store_nt(reinterpret_cast<uint2 *>(yp + 4),
-                                         make_uint2(pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7])));
+                            const uint2 o0 = make_uint2(pack2<T>(v[0], v[1]), pack2<T>(v[2], v[3]));
+                            const uint2 o1 = make_uint2(pack2<T>(v[4], v[5]), pack2<T>(v[6], v[7]));
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(gconv_u32x2, o0), yr, yo, 0, kNT);
+                            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(gconv_u32x2, o1), yr,
+                                                                  ow0 + 4 < g.OW ? yo + 8u : kOOB, 0, kNT);
                         } else {
 #pragma unroll
                             for (int mb = 0; mb < 8; ++mb)
-                                if (ow0 + mb < g.OW) yp[mb] = from_f32<T>(v[mb]);
+                                __builtin_amdgcn_raw_buffer_store_b16(
+                                    __builtin_bit_cast(unsigned short, from_f32<T>(v[mb])), yr,
+                                    ow0 + mb < g.OW ? yo + 2u * mb : kOOB, 0, kNT);
                         }
                     }
             };
@@ -565,10 +596,14 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
             else
                 store_rows(std::false_type{});
         }
-        if (!has_next) break;
+        if (!has_next) return false;
         tile = next_tile;
         ts = nts;
-    }
+        return true;
+    };
+    if (tile_body())
+        while (tile_body()) {
+        }
 }
 
 struct RowsPlan {
@@ -659,6 +694,7 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
     const int64_t HW = (int64_t)g.H * g.W;
     if ((crossings + 1) * (int64_t)g.C * HW * 2 >= (int64_t(1) << 31) || (int64_t)(g.Cg + 16) * HW * 2 >= (int64_t(1) << 31))
         return pl;
+    if ((crossings + 1) * (int64_t)g.Cout * g.OH * g.OW * 2 >= (int64_t(1) << 31)) return pl;   // output offsets
     const uintptr_t ya = reinterpret_cast<uintptr_t>(a.y);
     g.sg = (g.OW % 8 == 0 && ya % 16 == 0) ? 8 : (g.OW % 4 == 0 && ya % 8 == 0) ? 4 : 1;
     g.ocs = a.interleaved ? g.groups : 1;
