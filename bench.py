@@ -112,7 +112,7 @@ def kernel_unit(kernel, dtype):
         return "mfma32x32x16"
     if kernel.endswith("mfma32x32x2"):
         return "mfma32x32x2"
-    if kernel == "direct2d_g4" and dtype != "f32":
+    if kernel in ("direct2d_g4", "conv2d_nhwc_g4_mfma") and dtype != "f32":
         return "mfma4x4x4"
     if kernel == "conv2d_nhwc_g4k3_row" and dtype != "f32":
         return "dot2"
@@ -143,6 +143,7 @@ KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_rows_mfma32x32x16"
                 "dw1d_btc_generic": "dw1d_ntc.hip", "dw2d_nhwc_tile": "nhwc.hip",
                 "igemm_nhwc_mfma32x32x16": "igemm_nhwc.hip", "conv2d_nhwc_g4": "nhwc.hip",
                 "conv2d_nhwc_g4k3": "nhwc.hip", "conv2d_nhwc_g4k3_row": "nhwc.hip",
+                "conv2d_nhwc_g4_mfma": "nhwc.hip",
                 "conv2d_nhwc_generic": "nhwc.hip"}
 
 

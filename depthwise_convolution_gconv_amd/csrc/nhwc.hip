@@ -436,6 +436,215 @@ conv2d_nhwc_g4k3_row(const T *__restrict__ x, const T *__restrict__ w, const T *
     }
 }
 
+// conv2d_nhwc_g4_mfma<T, GPB>: 4 in / 4 out channels per group, 3 x 3, unit stride
+// and dilation, padding at most 1, 16-bit.  One workgroup per (image, block of GPB
+// groups = 4*GPB channels); the whole image of the block goes to LDS once.
+//  * Staging: 16-byte loads along C (8 channels = 2 groups of one position) are
+//    split into per-group planes of 8-byte entries (the 4 channels of a position),
+//    each plane a zero-bordered padded image.  In NHWC a group's 4 channels are
+//    already the 8 contiguous bytes of an entry, so no element is moved.
+//  * Products: as in direct2d_g4, on v_mfma_f32_4x4x4_16b: a wave takes a group,
+//    lanes take 64 consecutive anchors of its padded plane (anchor = the window's
+//    top-left entry), each tap is one MFMA with A = the group's 4 x 4 filter matrix
+//    at that tap (lane i%4 holds output i's 4 inputs, read straight from w) and
+//    B = the anchor's 4 channels; per filter row one LDS read gives the kw = 0
+//    operand and the kw = 1, 2 operands are the next lanes' values (DPP shifts).
+//  * Outputs: each anchor's 4 outputs (8 bytes) go to an LDS image of the block's
+//    outputs, [position][GPB + 1 entries] (an odd row stride: the 8-byte writes of
+//    64 consecutive positions fall on distinct banks), and the workgroup then
+//    stores it along C with 16-byte non-temporal stores.
+constexpr int kNG4Step = 62;   // anchors per pass (lanes 62, 63 only supply shifted operands)
+
+__host__ __device__ inline int nhwc_g4_img(int HP, int WP, int OH, int OW)
+{
+    const int na = (OH - 1) * WP + OW;                            // anchors up to the last output
+    const int npass = (na + kNG4Step - 1) / kNG4Step;
+    const int reach = kNG4Step * (npass - 1) + 64 + 2 * WP + 2;   // entries any lane of any pass reads
+    return (HP * WP > reach ? HP * WP : reach) | 1;               // odd: planes start on different banks
+}
+
+// q / d for 0 <= q < 2048 and 1 <= d <= 400 as (q * m) >> 20, m = ceil(2^20 / d)
+// (the same exact range as the NCHW kernel's division).
+__device__ __forceinline__ int ng4_div(int q, uint32_t m) { return (int)(((uint32_t)q * m) >> 20); }
+
+__device__ __forceinline__ uint2 ng4_next_lane(uint2 v)
+{
+    return make_uint2((uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0x130, 0xf, 0xf, false),
+                      (uint32_t)__builtin_amdgcn_update_dpp((int)v.y, (int)v.y, 0x130, 0xf, 0xf, false));
+}
+
+typedef _Float16 ng4_f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 ng4_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float ng4_f32x4 __attribute__((ext_vector_type(4)));
+template <typename T> struct NMfma4;
+template <> struct NMfma4<_Float16> {
+    static __device__ __forceinline__ ng4_f32x4 run(uint2 a, uint2 b, ng4_f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(ng4_f16x4, a), __builtin_bit_cast(ng4_f16x4, b),
+                                                 c, 0, 0, 0);
+    }
+};
+template <> struct NMfma4<__bf16> {
+    static __device__ __forceinline__ ng4_f32x4 run(uint2 a, uint2 b, ng4_f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(ng4_bf16x4, a),
+                                                     __builtin_bit_cast(ng4_bf16x4, b), c, 0, 0, 0);
+    }
+};
+template <typename T> __device__ __forceinline__ uint32_t ng4_bits(T v) { return __builtin_bit_cast(uint16_t, v); }
+
+constexpr int kNG4MaxLoads = 8;   // 16-byte input loads per thread (H*W*GPB/2 <= 2048)
+
+template <typename T, int GPB>
+__global__ void __launch_bounds__(kThreads)
+conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+                    T *__restrict__ y, int C, int H, int W, int OH, int OW, int ph, int pw, int cblocks, int img,
+                    uint32_t mw, uint32_t mwp, int wgs, int wgs_per_xcd)
+{
+    constexpr int PP = GPB / 2;       // 16-byte pieces of a position's block
+    constexpr int GPW = GPB / 4;      // groups per wave
+    constexpr int YS = GPB + 1;       // entries per position of the output image
+    extern __shared__ __attribute__((aligned(16))) uint2 ng4s[];
+    uint2 *xs = ng4s;                 // [GPB][img] padded planes
+    uint2 *ys = ng4s + GPB * img;     // [OH*OW][YS] outputs
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Workgroup b runs on XCD b % 8; the XCDs take contiguous runs of (image, channel
+    // block) pairs, so the neighbouring blocks of a position, which share its cache
+    // lines, are read and written through one L2.
+    const int wg = (blockIdx.x & 7) * wgs_per_xcd + (blockIdx.x >> 3);
+    if (wg >= wgs) return;   // uniform over the workgroup
+    const int cb = wg % cblocks, n = wg / cblocks;
+    const int HP = H + 2 * ph, WP = W + 2 * pw, HW = H * W, OHW = OH * OW;
+    const int c0 = cb * 4 * GPB;      // first channel of the block
+    const int npiece = HW * PP;
+
+    // Every global load is issued before the first is used: the image pieces, then
+    // this wave's filters (lane i % 4: output i's 4 inputs at each tap) and biases.
+    const T *xn = x + (int64_t)n * HW * C + c0;
+    uint4 xv[kNG4MaxLoads];
+#pragma unroll
+    for (int j = 0; j < kNG4MaxLoads; ++j) {
+        if (kThreads * j < npiece) {   // uniform; the piece index is clamped, not branched on
+            const int i = min(tid + kThreads * j, npiece - 1);
+            const int pos = i / PP, part = i - pos * PP;
+            xv[j] = *reinterpret_cast<const uint4 *>(xn + (int64_t)pos * C + 8 * part);
+        }
+    }
+    uint2 fa[GPW][9], bz[GPW];
+#pragma unroll
+    for (int s = 0; s < GPW; ++s) {
+        const int o = c0 + 4 * (wave + 4 * s);   // first output channel of the group
+        const T *wg = w + (int64_t)(o + (lane & 3)) * 36;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) fa[s][t] = *reinterpret_cast<const uint2 *>(wg + 4 * t);
+        bz[s] = bias ? *reinterpret_cast<const uint2 *>(bias + o) : make_uint2(0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
+
+    // Planes: border entries zero (the ph top and bottom rows, then the pw left and
+    // right columns of every image row), image entries from the pieces.
+    const int nborder = HP * WP - HW;
+    for (int i = tid; i < nborder * GPB; i += kThreads) {
+        const int gl = i / nborder, b = i - gl * nborder;
+        int hp, wp;
+        if (b < 2 * ph * WP) {
+            const int r = b / WP;
+            hp = r < ph ? r : H + r;
+            wp = b - r * WP;
+        } else {
+            const int j = b - 2 * ph * WP, r = j / (2 * pw), sd = j - r * (2 * pw);
+            hp = ph + r;
+            wp = sd < pw ? sd : W + sd;
+        }
+        xs[gl * img + hp * WP + wp] = make_uint2(0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kNG4MaxLoads; ++j) {
+        const int i = tid + kThreads * j;
+        if (kThreads * j < npiece && i < npiece) {
+            const int pos = i / PP, part = i - pos * PP;
+            const int h = ng4_div(pos, mw), ww = pos - h * W;
+            const int e = (h + ph) * WP + ww + pw;
+            xs[(2 * part) * img + e] = make_uint2(xv[j].x, xv[j].y);
+            xs[(2 * part + 1) * img + e] = make_uint2(xv[j].z, xv[j].w);
+        }
+    }
+    __syncthreads();
+
+    const int na = (OH - 1) * WP + OW;
+#pragma unroll
+    for (int s = 0; s < GPW; ++s) {
+        const int gl = wave + 4 * s;
+        const uint2 *pl = xs + gl * img;
+        ng4_f32x4 b0;
+        b0[0] = to_f32(__builtin_bit_cast(T, (uint16_t)(bz[s].x & 0xffffu)));
+        b0[1] = to_f32(__builtin_bit_cast(T, (uint16_t)(bz[s].x >> 16)));
+        b0[2] = to_f32(__builtin_bit_cast(T, (uint16_t)(bz[s].y & 0xffffu)));
+        b0[3] = to_f32(__builtin_bit_cast(T, (uint16_t)(bz[s].y >> 16)));
+        for (int a0 = 0; a0 < na; a0 += kNG4Step) {
+            const int a = a0 + lane;
+            ng4_f32x4 acc = b0;
+#pragma unroll
+            for (int kh = 0; kh < 3; ++kh) {
+                const uint2 v0 = pl[a + kh * WP];
+                const uint2 v1 = ng4_next_lane(v0);
+                const uint2 v2 = ng4_next_lane(v1);
+                acc = NMfma4<T>::run(fa[s][kh * 3 + 0], v0, acc);
+                acc = NMfma4<T>::run(fa[s][kh * 3 + 1], v1, acc);
+                acc = NMfma4<T>::run(fa[s][kh * 3 + 2], v2, acc);
+            }
+            const int oh = ng4_div(a, mwp), ow = a - oh * WP;
+            if (lane < kNG4Step && a < na && ow < OW)
+                ys[(oh * OW + ow) * YS + gl] =
+                    make_uint2(ng4_bits(from_f32<T>(acc[0])) | (ng4_bits(from_f32<T>(acc[1])) << 16),
+                               ng4_bits(from_f32<T>(acc[2])) | (ng4_bits(from_f32<T>(acc[3])) << 16));
+        }
+    }
+    __syncthreads();
+
+    // The block's outputs along C: piece (position, part) is channels c0 + 8*part ..
+    // of one position, 16 bytes.
+    T *yn = y + (int64_t)n * OHW * C + c0;
+    for (int i = tid; i < OHW * PP; i += kThreads) {
+        const int pos = i / PP, part = i - pos * PP;
+        const uint2 lo = ys[pos * YS + 2 * part], hi = ys[pos * YS + 2 * part + 1];
+        store_nt(reinterpret_cast<uint4 *>(yn + (int64_t)pos * C + 8 * part), make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+}
+
+// Groups per workgroup of conv2d_nhwc_g4_mfma, or 0 when it does not apply: 4*GPB
+// channels dividing C, the image within the load registers (H*W*GPB/2 pieces of
+// 16 bytes over 256 threads, 8 each at most) and the planes and outputs within
+// 40 KB of LDS (4 workgroups per CU).
+template <typename T>
+int nhwc_g4_mfma_gpb(const Conv2dArgs &a, size_t *lds, int *img)
+{
+    if constexpr (sizeof(T) != 2) {
+        return 0;
+    } else {
+        if (!(a.C == 4 * a.groups && a.Cout == a.C && !a.interleaved && a.KH == 3 && a.KW == 3 && a.sh == 1 &&
+              a.sw == 1 && a.dh == 1 && a.dw == 1 && a.ph <= 1 && a.pw <= 1 && a.W + 2 * a.pw <= 400 &&
+              (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= 1024 && a.H * a.W * a.C < (int64_t(1) << 31) &&
+              a.OH * a.OW * a.C < (int64_t(1) << 31) &&
+              ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.y)) & 15) == 0 &&
+              ((reinterpret_cast<uintptr_t>(a.w) | reinterpret_cast<uintptr_t>(a.bias)) & 7) == 0))
+            return 0;
+        const int HP = (int)(a.H + 2 * a.ph), WP = (int)(a.W + 2 * a.pw), OH = (int)a.OH, OW = (int)a.OW;
+        for (int gpb : {8, 4}) {
+            if (a.C % (4 * gpb) != 0 || a.H * a.W * (gpb / 2) > kThreads * kNG4MaxLoads) continue;
+            const int im = nhwc_g4_img(HP, WP, OH, OW);
+            const size_t bytes = ((size_t)gpb * im + (size_t)OH * OW * (gpb + 1)) * sizeof(uint2);
+            if (bytes > 40 * 1024) continue;
+            if (a.N * (a.C / (4 * gpb)) >= (int64_t(1) << 30)) continue;
+            *lds = bytes;
+            *img = im;
+            return gpb;
+        }
+        return 0;
+    }
+}
+
 template <typename T, int K, int S, int VE>
 hipError_t run_tile(const Conv2dArgs &a)
 {
@@ -487,6 +696,26 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
           reinterpret_cast<uintptr_t>(a.y)) & kVecAlign) == 0) {
         const int64_t npix = a.N * a.OH * a.OW;
         if constexpr (sizeof(T) == 2) {
+            size_t lds = 0;
+            int img = 0;
+            const int gpb = nhwc_g4_mfma_gpb<T>(a, &lds, &img);
+            if (gpb) {
+                *kname = "conv2d_nhwc_g4_mfma";
+                const int cblocks = (int)(a.C / (4 * gpb));
+                const int WP = (int)(a.W + 2 * a.pw);
+                const uint32_t mw = (uint32_t)(((1u << 20) + a.W - 1) / a.W), mwp = (uint32_t)(((1u << 20) + WP - 1) / WP);
+                const int wgs = (int)(a.N * cblocks), per_xcd = (int)ceil_div(wgs, 8);
+                auto launch = [&](auto kern) {
+                    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), lds, a.stream,
+                                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)a.C,
+                                       (int)a.H, (int)a.W, (int)a.OH, (int)a.OW, a.ph, a.pw, cblocks, img, mw, mwp,
+                                       wgs, per_xcd);
+                };
+                if (gpb == 16) launch(conv2d_nhwc_g4_mfma<T, 16>);
+                else if (gpb == 8) launch(conv2d_nhwc_g4_mfma<T, 8>);
+                else launch(conv2d_nhwc_g4_mfma<T, 4>);
+                return hipGetLastError();
+            }
             const int64_t nowb = ceil_div(a.OW, kRowOut);
             const int64_t nrb = a.N * a.OH * nowb, nkb = ceil_div(a.groups, 16);
             const int64_t total = nkb * ceil_div(nrb, 4) * 64;   // threads, whole waves

@@ -33,6 +33,7 @@ def test_flops_of_the_conformer_conv1d():
     ("direct2d_g4", "bf16", "mfma4x4x4"),
     ("direct2d_g4", "f32", "valu"),
     ("conv2d_nhwc_g4k3_row", "bf16", "dot2"),
+    ("conv2d_nhwc_g4_mfma", "bf16", "mfma4x4x4"),
     ("dw1d_btc_tile", "f32", "valu"),
     ("dw2d_rows", "bf16", "valu"),
 ])

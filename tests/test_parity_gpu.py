@@ -258,7 +258,37 @@ NHWC_SWEEP = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (3, 32, 32, 6, 13, 3, 3, 8, 1, 1, 1, True),        # 4 in / 4 out, rows of 13: a ragged 8-output block
     (1, 64, 64, 10, 17, 3, 3, 16, (2, 1), (1, 0), (2, 1), False),   # 4 in / 4 out, row stride and dilation 2
     (2, 16, 16, 5, 8, 3, 3, 4, 1, 0, 1, True),         # 4 in / 4 out, no padding
+    # 4 in / 4 out, 16-bit, 3 x 3, unit stride: the whole-image matrix-core kernel
+    (4, 128, 128, 14, 14, 3, 3, 32, 1, 1, 1, True),    # the fully grouped layer's image, 4 channel blocks
+    (2, 32, 32, 7, 23, 3, 3, 8, 1, 1, 1, True),        # ragged rows, 3 anchor passes per group
+    (2, 64, 64, 8, 12, 3, 3, 16, 1, (1, 0), 1, True),  # padding on the rows only
+    (1, 48, 48, 10, 10, 3, 3, 12, 1, 1, 1, False),     # 48 channels: blocks of 4 groups
+    (1, 32, 32, 40, 40, 3, 3, 8, 1, 1, 1, True),       # an image too large for it: the row kernel
 ]
+
+
+def nhwc_g4_mfma_applies(C, H, W, s, p, d, dt):
+    """Whether conv2d_nhwc_g4_mfma takes a 4-in/4-out 3x3 NHWC layer (its host
+    conditions: 16-bit, unit stride and dilation, padding at most 1, 4*GPB channels
+    per block with GPB = 8 or 4, the image within 8 loads of 16 bytes per thread and
+    the planes and outputs within 40 KB of LDS)."""
+    two = lambda v: v if isinstance(v, tuple) else (v, v)
+    (sh, sw), (ph, pw), (dh, dw) = two(s), two(p), two(d)
+    if dt == "f32" or (sh, sw, dh, dw) != (1, 1, 1, 1) or ph > 1 or pw > 1:
+        return False
+    HP, WP = H + 2 * ph, W + 2 * pw
+    if WP > 400 or HP * WP > 1024:
+        return False
+    OH, OW = HP - 2, WP - 2
+    na = (OH - 1) * WP + OW
+    npass = -(-na // 62)
+    img = max(HP * WP, 62 * (npass - 1) + 64 + 2 * WP + 2) | 1
+    for gpb in (8, 4):
+        if C % (4 * gpb) or H * W * gpb // 2 > 256 * 8:
+            continue
+        if (gpb * img + OH * OW * (gpb + 1)) * 8 <= 40 * 1024:
+            return True
+    return False
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
@@ -278,6 +308,8 @@ def test_nhwc_sweep_vs_oracle(ci, dt):
     dw_ = d[1] if isinstance(d, tuple) else d
     row = dt != "f32" and sw == 1 and dw_ == 1
     g4k = ("conv2d_nhwc_g4k3_row" if row else "conv2d_nhwc_g4k3") if (KH, KW) == (3, 3) else "conv2d_nhwc_g4"
+    if (KH, KW) == (3, 3) and nhwc_g4_mfma_applies(C, H, W, s, p, d, dt):
+        g4k = "conv2d_nhwc_g4_mfma"
     assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else g4k if g4 else "conv2d_nhwc_generic")
     assert check(as_f64(y.cpu()), r, dt)
 
@@ -611,8 +643,8 @@ def test_next_workload_full_size(name):
         assert gc.gconv_last_kernel() == "dw1d_btc_tile"
     elif wl.layout == "nhwc":
         r = oracle.conv2d_nhwc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
-        # the 4-in/4-out layers here are 16-bit, 3 x 3, unit column stride and dilation
-        expect = {1: "dw2d_nhwc_tile", 4: "conv2d_nhwc_g4k3_row"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
+        # the 4-in/4-out layers here are 16-bit, 3 x 3, unit stride and dilation, 14 x 14
+        expect = {1: "dw2d_nhwc_tile", 4: "conv2d_nhwc_g4_mfma"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
         assert gc.gconv_last_kernel() == expect
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
