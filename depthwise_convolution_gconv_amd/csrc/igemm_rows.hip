@@ -126,12 +126,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Halo map: 16-byte half `hf` (channels 0-7 or 8-15) of the 32-byte slot s, with one
-// spare unit after every 8 slots.  Slots 8 apart are 17 units apart, so the 16 lanes
-// of a half-wave reading the same window position of 16 runs hit 16 different
-// units modulo 16: no bank conflicts when the runs lie on one row.
-__device__ __forceinline__ int halo_unit(int s, int hf) { return 2 * s + hf + (s >> 3); }
-__host__ __device__ inline int halo_units(int slots) { return 2 * slots + slots / 8; }
+// Halo map: 16-byte half `hf` (channels 0-7 or 8-15) of the 32-byte slot of column
+// col in halo row `row`, with one spare unit after every 8 columns and a row stride
+// of rsu units.  Columns 8 apart are 17 units apart, so the 16 lanes of a half-wave
+// reading the same window position of 16 consecutive runs of one row hit 16
+// different units modulo 16; rsu is chosen congruent to the runs per row modulo 16
+// when a row has fewer than 16 runs, so that runs spanning several rows do too.
+__device__ __forceinline__ int halo_unit(int row, int col, int hf, int rsu)
+{
+    return row * rsu + 2 * col + (col >> 3) + hf;
+}
 
 // Filter image: per 16-filter half-block, per tap, 32 units; filter f (< 16) and
 // channel half hh at unit 2f + (hh ^ bit 3 of f).  The A-operand read (16 lanes on
@@ -166,16 +170,6 @@ __device__ __forceinline__ uint32_t col_pair(const uint32_t *ra, const uint32_t 
     return __builtin_amdgcn_perm(rb[v >> 1], ra[v >> 1], sel);
 }
 
-// Column v of 8 channel rows d[0..7] as one 16-byte unit of 8 channels, written to
-// halo slot slot0 + v, half oct.
-template <int VW, int DW, int v>
-__device__ __forceinline__ void write_octets(uint4 *hs, int slot0, int oct, const uint32_t (*d)[DW])
-{
-    hs[halo_unit(slot0 + v, oct)] = make_uint4(col_pair<v>(d[0], d[1]), col_pair<v>(d[2], d[3]),
-                                               col_pair<v>(d[4], d[5]), col_pair<v>(d[6], d[7]));
-    if constexpr (v + 1 < VW) write_octets<VW, DW, v + 1>(hs, slot0, oct, d);
-}
-
 struct RowsGeom {
     int N, C, H, W, Cout, Cg, Ng, OH, OW;
     int sh, ph, pw, dh;
@@ -183,7 +177,8 @@ struct RowsGeom {
     int RPR, NRUN;           // runs per output row; N*OH*RPR runs in all (< 2^31)
     int RTU;                 // runs a tile covers (at most its 32*PW lanes): whole rows or images
     int NR, SROW;            // halo rows; slots per halo row (a multiple of 8)
-    int kh_units;            // unit step of one filter row in the halo: 17 * dh * SROW / 8
+    int RSU;                 // units per halo row: 17 * SROW / 8 plus a padding below 16
+    int kh_units;            // unit step of one filter row in the halo: dh * RSU
     int nseg, xtasks;        // VW-wide segments per input row; staging tasks = 2*NR*nseg
     int npad;                // halo columns of a row outside the image: [0, pw) and [pw + W, SROW)
     int m_tiles, n_tiles, groups, nchunks, tiles, tiles_per_xcd;
@@ -244,20 +239,19 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
 
     // Input staging tasks (channel octet, halo row, VW-wide segment); task i of this
     // thread is tid + i*256.
-    int xrr[XR], xoct[XR], xslot0[XR], xcol[XR];
+    int xrr[XR], xoct[XR], xcol[XR];
     bool xtask[XR];
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
         const int tk = tid + i * kThreads;
         xtask[i] = tk < g.xtasks;
-        xrr[i] = xoct[i] = xslot0[i] = xcol[i] = 0;
+        xrr[i] = xoct[i] = xcol[i] = 0;
         if (xtask[i]) {
             const int rest = fdiv(tk, g.fd_nseg);
             const int sgm = fmod_q(tk, rest, g.fd_nseg);
             xoct[i] = fdiv(rest, g.fd_nr);
             xrr[i] = fmod_q(rest, xoct[i], g.fd_nr);
             xcol[i] = sgm * VW;
-            xslot0[i] = xrr[i] * g.SROW + g.pw + xcol[i];
         }
     }
     // Transpose: lane = (filter tf, channel half th) of the wave's block.
@@ -366,7 +360,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         const int w2 = v >> 1;
         const uint4 val = make_uint4(__builtin_amdgcn_perm(rb[w2], ra[w2], sel), __builtin_amdgcn_perm(rd[w2], rc[w2], sel),
                                      __builtin_amdgcn_perm(rf[w2], re[w2], sel), __builtin_amdgcn_perm(rh[w2], rg[w2], sel));
-        const int unit = xtask[r] ? halo_unit(xslot0[r] + v, xoct[r]) : HU - 1;
+        const int unit = xtask[r] ? halo_unit(xrr[r], g.pw + xcol[r] + v, xoct[r], g.RSU) : HU - 1;
         hal(stg)[unit] = val;
     };
 
@@ -375,11 +369,11 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
     for (int j = tid; j < g.NR * g.npad; j += kThreads) {
         const int row = j / g.npad, pc = j - row * g.npad;
         const int col = pc < g.pw ? pc : pc - g.pw + g.pw + g.W;
-        const int s = row * g.SROW + col;
-        hal0[halo_unit(s, 0)] = make_uint4(0, 0, 0, 0);
-        hal0[halo_unit(s, 1)] = make_uint4(0, 0, 0, 0);
-        hal1[halo_unit(s, 0)] = make_uint4(0, 0, 0, 0);
-        hal1[halo_unit(s, 1)] = make_uint4(0, 0, 0, 0);
+        const int u = halo_unit(row, col, 0, g.RSU);
+        hal0[u] = make_uint4(0, 0, 0, 0);
+        hal0[u + 1] = make_uint4(0, 0, 0, 0);
+        hal1[u] = make_uint4(0, 0, 0, 0);
+        hal1[u + 1] = make_uint4(0, 0, 0, 0);
     }
 
     TileState ts = tile_state(tile);
@@ -424,7 +418,7 @@ igemm_rows_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__rest
         const int n = fdiv(R, g.fd_oh);
         const int oh = fmod_q(R, n, g.fd_oh);
         const int ow0 = kRun * jr;
-        const int ub = 17 * (((n * g.Hp + oh * g.sh - ts.R_lo) * g.SROW + ow0) >> 3) + hf;
+        const int ub = halo_unit(n * g.Hp + oh * g.sh - ts.R_lo, ow0, hf, g.RSU);
 
         f32x16 acc[2][8];
 #pragma unroll
@@ -671,11 +665,15 @@ RowsPlan make_rows_plan(const Conv2dArgs &a)
     const int64_t WL = 8 * (int64_t)g.RPR + 2;   // padded columns the runs' windows read
     const int64_t SROW = (WL + 7) / 8 * 8;
     if (NR * SROW >= (int64_t(1) << 24)) return pl;
+    // Row stride in units: 17 per 8 columns, plus (RPR - SROW/8) mod 16 when a row
+    // has fewer than 16 runs (then the 16 runs a half-wave reads span several rows)
+    // and the padded rows fit.
     const int HU = pl.FW == 2 ? kHU<2> : kHU<1>;
-    if (halo_units((int)(NR * SROW)) > HU - 1) return pl;   // the last unit is the spare one
-    g.NR = (int)NR; g.SROW = (int)SROW;
-    g.kh_units = 17 * g.dh * g.SROW / 8;
-    if ((int64_t)17 * g.dh * (SROW / 8) * 2 + halo_units((int)(NR * SROW)) >= (int64_t(1) << 30)) return pl;
+    int64_t RSU = 17 * (SROW / 8) + (g.RPR < 16 ? ((g.RPR - SROW / 8) % 16 + 16) % 16 : 0);
+    if (NR * RSU > HU - 1) RSU = 17 * (SROW / 8);
+    if (NR * RSU > HU - 1) return pl;   // the last unit is the spare one
+    g.NR = (int)NR; g.SROW = (int)SROW; g.RSU = (int)RSU;
+    g.kh_units = g.dh * g.RSU;
     g.npad = g.pw + (int)(SROW - g.pw - g.W);
     // Input rows in VW-wide segments (whole rows: W a multiple of VW).
     const uintptr_t xa = reinterpret_cast<uintptr_t>(a.x);
