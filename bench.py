@@ -135,6 +135,7 @@ def source_digest(kernel_file):
 
 # Source file of each kernel (as gconv_last_kernel names it).
 KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_rows_mfma32x32x16": "igemm_rows.hip",
+                "igemm_defer_mfma32x32x16": "igemm_defer.hip",
                 "igemm_fwd_f32_mfma32x32x2": "igemm_f32.hip",
                 "direct2d_g4": "direct2d.hip", "direct2d_tiled": "direct2d.hip",
                 "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip",

@@ -24,8 +24,8 @@ LIB = os.path.join(PKG, "libgconv.so")
 PEAKS_SRC = "peaks.hip"
 PEAKS_LIB = os.path.join(PKG, "libgconv_peaks.so")
 
-SOURCES = ["api.cpp", "direct2d.hip", "dw2d.hip", "dw1d_ntc.hip", "dw1d_wgrad.hip", "nhwc.hip", "igemm_nhwc.hip", "igemm.hip", "igemm_rows.hip", "igemm_f32.hip"]
-HEADERS = ["common.hpp", "fastdiv.hpp"]
+SOURCES = ["api.cpp", "direct2d.hip", "dw2d.hip", "dw1d_ntc.hip", "dw1d_wgrad.hip", "nhwc.hip", "igemm_nhwc.hip", "igemm.hip", "igemm_rows.hip", "igemm_defer.hip", "igemm_f32.hip"]
+HEADERS = ["common.hpp", "fastdiv.hpp", "rows_common.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

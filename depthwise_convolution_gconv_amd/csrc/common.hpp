@@ -83,6 +83,8 @@ bool igemm_supported(const Conv2dArgs &a);            // fp16 / bf16
 hipError_t launch_igemm(const Conv2dArgs &a, const char **kname);
 bool igemm_rows_supported(const Conv2dArgs &a);       // fp16 / bf16, 3x3, unit column stride and dilation
 hipError_t launch_igemm_rows(const Conv2dArgs &a, const char **kname);
+bool igemm_defer_supported(const Conv2dArgs &a);      // fp16 / bf16, 3x3, 33-64 filters per group
+hipError_t launch_igemm_defer(const Conv2dArgs &a, const char **kname);
 bool igemm_f32_supported(const Conv2dArgs &a);        // fp32
 hipError_t launch_igemm_f32(const Conv2dArgs &a, const char **kname);
 hipError_t launch_dw1d(const Dw1dArgs &a, const char **kname);

@@ -51,15 +51,9 @@
 namespace gconv {
 namespace {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-#define GCONV_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+#include "rows_common.hpp"
 
 constexpr int kThreads = 256;
-constexpr int kLdsUnits = 160 * 1024 / 16;   // 16-byte units of LDS per workgroup (one per CU)
 constexpr int kBlockUnits = 576;             // one 32-filter block's chunk: 32 x 16 ch x 9 taps x 2 B
 constexpr int kSubUnits = 288;               // one 16-filter half of it
 // LDS stride of a 16-filter half-block in the filter image: 288 units with 128
@@ -70,61 +64,9 @@ template <int FW> constexpr int kSub = FW == 1 ? 320 : kSubUnits;
 template <int FW> constexpr int kBlk = 2 * kSub<FW>;                    // a 32-filter block
 constexpr int kRun = 8;                      // output columns per run
 constexpr int kWin = kRun + 2;               // window positions of one filter row (3 taps)
-constexpr uint32_t kOOB = 0x80000000u;       // byte offset past num_records: loads return 0, stores drop
-constexpr int kNT = 2;                       // cache policy of the output stores: non-temporal
 
 template <int FW> constexpr int kFU = 2 * FW * kBlk<FW>;                 // filter units per stage
 template <int FW> constexpr int kHU = (kLdsUnits - 2 * kFU<FW>) / 2;     // halo units per stage
-
-template <typename T> struct Mfma;
-template <> struct Mfma<_Float16> {
-    static __device__ __forceinline__ f32x16 run(uint4 a, uint4 b, f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-};
-template <> struct Mfma<__bf16> {
-    static __device__ __forceinline__ f32x16 run(uint4 a, uint4 b, f32x16 c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-};
-
-template <typename T> __device__ __forceinline__ float half_to_f32(uint32_t hbits);
-template <> __device__ __forceinline__ float half_to_f32<_Float16>(uint32_t hbits)
-{
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)hbits);
-}
-template <> __device__ __forceinline__ float half_to_f32<__bf16>(uint32_t hbits)
-{
-    return __builtin_bit_cast(float, hbits << 16);
-}
-// Two fp32 values rounded to nearest even into one dword of T (a in the low half).
-template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b);
-template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float a, float b)
-{
-    return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
-}
-template <> __device__ __forceinline__ uint32_t pack2<__bf16>(float a, float b)
-{
-    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
-}
-
-// One accumulator copied out of its accumulation register at this point of the
-// program (otherwise the allocator moves all of them into VGPRs at once).
-__device__ __forceinline__ float acc_read(float v)
-{
-    float r;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
-    return r;
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Halo map: 16-byte half `hf` (channels 0-7 or 8-15) of the 32-byte slot of column
 // col in halo row `row`, with one spare unit after every 8 columns and a row stride
@@ -137,38 +79,8 @@ __device__ __forceinline__ int halo_unit(int row, int col, int hf, int rsu)
     return row * rsu + 2 * col + (col >> 3) + hf;
 }
 
-// Filter image: per 16-filter half-block, per tap, 32 units; filter f (< 16) and
-// channel half hh at unit 2f + (hh ^ bit 3 of f).  The A-operand read (16 lanes on
-// 16 consecutive filters, one channel half) and the transposing write (16 lanes on
-// 8 filters x 2 halves) both hit 16 different units modulo 16.
-__device__ __forceinline__ int fimg_unit(int f, int hh) { return 2 * f + (hh ^ ((f >> 3) & 1)); }
 
-// VW consecutive 16-bit elements of one input row, as VW/2 dwords.
-template <int VW> struct VecLoad;
-template <> struct VecLoad<8> {
-    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, uint32_t *d)
-    {
-        const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, vo, so, 0));
-        d[0] = u.x; d[1] = u.y; d[2] = u.z; d[3] = u.w;
-    }
-};
-template <> struct VecLoad<4> {
-    static __device__ __forceinline__ void run(__amdgpu_buffer_rsrc_t r, uint32_t vo, uint32_t so, uint32_t *d)
-    {
-        const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, vo, so, 0));
-        d[0] = u.x; d[1] = u.y;
-    }
-};
 
-// Dword of element v of row ra (low half) and element v of row rb (high half); each
-// row holds VW 16-bit elements in VW/2 dwords.
-template <int v>
-__device__ __forceinline__ uint32_t col_pair(const uint32_t *ra, const uint32_t *rb)
-{
-    constexpr uint32_t b = 2 * (v & 1);
-    constexpr uint32_t sel = ((b + 5) << 24) | ((b + 4) << 16) | ((b + 1) << 8) | b;
-    return __builtin_amdgcn_perm(rb[v >> 1], ra[v >> 1], sel);
-}
 
 struct RowsGeom {
     int N, C, H, W, Cout, Cg, Ng, OH, OW;
@@ -744,10 +656,13 @@ hipError_t run_typed(const Conv2dArgs &a, const RowsPlan &pl)
 
 }  // namespace
 
-bool igemm_rows_supported(const Conv2dArgs &a) { return make_rows_plan(a).ok; }
+bool igemm_rows_supported(const Conv2dArgs &a) { return make_rows_plan(a).ok || igemm_defer_supported(a); }
 
 hipError_t launch_igemm_rows(const Conv2dArgs &a, const char **kname)
 {
+    // 33 to 64 filters per group: the kernel with runs of 4 columns and deferred
+    // output stores (igemm_defer.hip) where it applies.
+    if (igemm_defer_supported(a)) return launch_igemm_defer(a, kname);
     const RowsPlan pl = make_rows_plan(a);
     if (!pl.ok) return hipErrorInvalidValue;
     *kname = "igemm_rows_mfma32x32x16";

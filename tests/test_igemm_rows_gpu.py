@@ -25,6 +25,11 @@ pytestmark = pytest.mark.gpu
 TOL = {"f16": 1e-2, "bf16": 1e-2}       # the 16-bit accuracy bar
 REG = {"f16": 1e-3, "bf16": 4e-3}       # regression bound of the 16-bit MFMA kernels
 KERNEL = "igemm_rows_mfma32x32x16"
+DEFER = "igemm_defer_mfma32x32x16"   # 32 channels, 33 to 64 filters per group: deferred stores
+
+
+def kernel_for(Cg, Ng):
+    return DEFER if Cg == 32 and 32 < Ng <= 64 else KERNEL
 
 
 def errors(y, r):
@@ -55,14 +60,18 @@ ROWS = [  # N, C, Cout, H, W, groups, stride_h, pad, dilation_h, bias
     (1, 64, 160, 8, 8, 2, 1, 0, 1, False),        # no padding: 6 x 6 outputs, 80 filters per group
     (5, 32, 96, 5, 8, 1, 1, 1, 1, True),          # tiles spanning several images
     (2, 64, 256, 3, 48, 2, 1, 1, 1, True),        # the whole batch in one tile, 6 runs per row
-    # 33 to 64 filters per group: one wave across the filters, each wave staging a
-    # 16-filter half-block
+    # 33 to 64 filters per group, each wave staging a 16-filter half-block; with 32
+    # channels per group igemm_defer.hip (runs of 4 columns, each tile's stores
+    # issued during the next tile), otherwise igemm_rows.hip with one filter wave
     (2, 64, 128, 16, 16, 2, 1, 1, 1, True),       # 64 filters per group
     (3, 96, 144, 14, 28, 3, 1, 1, 1, True),       # 48: the last half-block empty; 28-wide rows in 4-wide segments
     (2, 64, 80, 10, 16, 2, 1, 1, 1, True),        # 40: a half-block partly empty
     (1, 32, 33, 6, 8, 1, 1, 1, 1, False),         # 33, the fewest on this kernel
     (3, 64, 128, 12, 12, 2, 2, 1, 1, True),       # 64 per group, row stride 2
     (4, 64, 128, 28, 28, 2, 1, 1, 1, False),      # the ensemble layer's 28 x 28 rows, tiles across images
+    (2, 128, 128, 12, 20, 2, 1, 1, 1, True),      # 64 channels per group: 4 chunks (igemm_rows)
+    (1, 96, 48, 9, 16, 1, 1, 1, 1, True),         # 96 channels, 48 filters: 6 chunks (igemm_rows)
+    (2, 64, 128, 10, 12, 2, 1, 0, 1, True),       # no padding: 10-wide rows, a partial last run, 2-byte stores
 ]
 
 
@@ -80,7 +89,7 @@ def test_rows_kernel_vs_oracle(ci, dt):
     assert gc.gconv_select_route(x.shape, w.shape, stride, p, dil, g, "nchw", dt) == "igemm"
     y = gc.gconv_fwd(x.cuda(), w.cuda(), None if b is None else b.cuda(), stride, p, dil, g, "nchw")
     torch.cuda.synchronize()
-    assert gc.gconv_last_kernel() == KERNEL
+    assert gc.gconv_last_kernel() == kernel_for(C // g, Co // g)
     check(f"rows{ci}", as_f64(y.cpu()), r, dt)
 
 
@@ -89,7 +98,8 @@ def test_rows_kernel_vs_oracle(ci, dt):
 MANY = [  # N, C, Cout, H, W, groups, bias
     (40, 128, 512, 32, 32, 4, True),      # 128 filters per group, 320 tiles
     (24, 128, 640, 24, 40, 2, False),     # 320 filters per group: 3 filter tiles, the last one partly empty
-    (48, 256, 512, 28, 28, 8, True),      # 64 filters per group, 336 tiles
+    (48, 256, 512, 28, 28, 8, True),      # 64 filters per group: 384 tiles, 1 or 2 per workgroup
+    (40, 256, 384, 14, 28, 8, False),     # 48 filters per group: 400 tiles
 ]
 
 
@@ -104,7 +114,7 @@ def test_rows_kernel_many_tiles_vs_oracle(ci):
     r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=1, padding=1, dilation=1, groups=g)
     y = gc.gconv_fwd(x.cuda(), w.cuda(), None if b is None else b.cuda(), 1, 1, 1, g, "nchw")
     torch.cuda.synchronize()
-    assert gc.gconv_last_kernel() == KERNEL
+    assert gc.gconv_last_kernel() == kernel_for(C // g, Co // g)
     check(f"many{ci}", as_f64(y.cpu()), r, dt)
 
 
@@ -128,6 +138,29 @@ def test_rows_kernel_interleaved_order_and_unaligned_output():
     torch.cuda.synchronize()
     assert gc.gconv_last_kernel() == KERNEL
     check("unaligned y", as_f64(y.cpu()), r, "f16")
+    assert torch.isnan(buf[0]) and bool(torch.isnan(buf[1 + n:]).all())
+
+
+def test_defer_kernel_interleaved_order_and_unaligned_output():
+    N, C, Co, H, W, g = 2, 64, 128, 12, 16, 2
+    x = draw((N, C, H, W), 1.0, 7850, "bf16")
+    w = draw((Co, C // g, 3, 3), 1.0 / (C // g * 9), 8850, "bf16")
+    b = draw((Co,), 0.01, 9850, "bf16")
+    xd, wd, bd = x.cuda(), w.cuda(), b.cuda()
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), 1, 1, 1, g, out_order="interleaved")
+    y = gc.gconv_fwd_ex(xd, wd, bd, 1, 1, 1, g, "nchw", route="igemm", out_order="interleaved")
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == DEFER
+    check("defer interleaved", as_f64(y.cpu()), r, "bf16")
+    # y two bytes past an 8-byte boundary: the 2-byte store path
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), 1, 1, 1, g)
+    n = N * Co * H * W
+    buf = torch.full((n + 8,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = buf[1:1 + n].view(N, Co, H, W)
+    gc.gconv_fwd(xd, wd, bd, 1, 1, 1, g, "nchw", y=y)
+    torch.cuda.synchronize()
+    assert gc.gconv_last_kernel() == DEFER
+    check("defer unaligned y", as_f64(y.float().cpu()), r, "bf16")
     assert torch.isnan(buf[0]) and bool(torch.isnan(buf[1 + n:]).all())
 
 
