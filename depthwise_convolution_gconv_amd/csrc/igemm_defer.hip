@@ -26,8 +26,10 @@
 // a load also waits for the stores issued before it.  All the global loads of the
 // first chunk (the next tile's filters, both chunks, and input rows) are issued
 // before its stores, and what later waits for them does not wait for the stores:
-// the filters are copied raw into two LDS buffers of their own and transposed into
-// the filter images between the tiles.
+// the filters are copied raw into LDS buffers of their own (chunk 0's, and chunk
+// 1's in one of two by tile parity) and transposed into the filter images during
+// the chunks: the next tile's chunk 0 during this tile's chunk 1, a tile's chunk 1
+// during its chunk 0.
 //
 // Input staging as in igemm_rows.hip (two halo stages, the rows of step c+2 loaded
 // into registers during chunk c and written during chunk c+1).  The halo keeps 9
@@ -50,7 +52,7 @@ constexpr int kWin = kRun + 2;                   // window positions of one filt
 constexpr int kSub = 320;                        // units of a 16-filter half-block (288 + padding)
 constexpr int kBlk = 2 * kSub;                   // a 32-filter block
 constexpr int kFU = 2 * kBlk;                    // filter units per image: 64 filters
-constexpr int kHU = (kLdsUnits - 4 * kFU) / 2;   // halo units per stage (2 images, 2 raw buffers)
+constexpr int kHU = (kLdsUnits - 5 * kFU) / 2;   // halo units per stage (2 images, 3 raw buffers)
 constexpr int kRT = 128;                         // runs per tile: 4 waves x 32
 constexpr int kNFC = 5;                          // filter copy instructions per wave and chunk
 constexpr int kStores = 32;                      // output stores per lane and tile
@@ -88,16 +90,21 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
     constexpr int DW = VW / 2;
     __shared__ uint4 hal0[kHU], hal1[kHU];
     __shared__ uint4 fim0[kFU], fim1[kFU];   // filter images of chunks 0 and 1
-    __shared__ uint4 raw0[kFU], raw1[kFU];   // the next tile's filter runs, as copied
+    // The filter runs as copied: chunk 0's (raw0), and chunk 1's in one of two
+    // buffers by tile parity (raw1a for even tiles of the walk, raw1b for odd ones).
+    __shared__ uint4 raw0[kFU], raw1a[kFU], raw1b[kFU];
     auto hal = [&](auto st) -> uint4 * {
         if constexpr (decltype(st)::value == 0) return hal0; else return hal1;
     };
     auto fim = [&](auto st) -> uint4 * {
         if constexpr (decltype(st)::value == 0) return fim0; else return fim1;
     };
-    auto raw = [&](auto st) -> uint4 * {
-        if constexpr (decltype(st)::value == 0) return raw0; else return raw1;
+    auto raw = [&](auto b) -> uint4 * {   // 0: raw0, 1: raw1a, 2: raw1b
+        if constexpr (decltype(b)::value == 0) return raw0;
+        else if constexpr (decltype(b)::value == 1) return raw1a;
+        else return raw1b;
     };
+    using B0 = std::integral_constant<int, 0>;
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     using P0 = std::integral_constant<int, 0>;
@@ -180,15 +187,15 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
 
     uint32_t d[2][XR][8][DW];   // staged input rows, two sets
     uint32_t E[36];             // a filter run being transposed: 8 channels x 9 taps
-    // Filter copy instruction i (< 5), into raw buffer stg (the chunk's): pieces
+    // Filter copy instruction i (< 5) of chunk ch of tile s into raw buffer rb: pieces
     // 64i + lane of the wave's half-block,
     // piece q being bytes 16*(q % 18) of filter q / 18's 288-byte run; pieces past the
     // 16 filters (and filters past Ng) read zeros into the padding.
-    auto filter_copy = [&](const TileState &s, int ch, auto stg, int i) {
+    auto filter_copy = [&](const TileState &s, int ch, auto rb, int i) {
         const int q = 64 * i + lane;
         const int pf = (q * 3641) >> 16;    // q / 18 for q < 576
         const uint32_t off = pf < s.nfw ? (uint32_t)(pf * g.Cg * 18 + 16 * (q - 18 * pf)) : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, GCONV_LDS(raw(stg) + kSub * wave + 64 * i), 16, off,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, GCONV_LDS(raw(rb) + kSub * wave + 64 * i), 16, off,
                                                  (uint32_t)(s.fbase * g.Cg + ch * 16) * 18, 0, 0);
     };
     auto input_load = [&](auto set, const TileState &s, int ch, int j) {
@@ -196,8 +203,8 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         VecLoad<VW>::run(s.xr, xtask[r] ? s.xvo[r] : kOOB, (uint32_t)(ch * 16 + e) * HW * 2,
                          d[decltype(set)::value][r][e]);
     };
-    auto transpose_read = [&](auto stg, int u) {
-        const uint4 v = raw(stg)[kSub * wave + traw + u];
+    auto transpose_read = [&](auto rb, int u) {
+        const uint4 v = raw(rb)[kSub * wave + traw + u];
         E[4 * u] = v.x; E[4 * u + 1] = v.y; E[4 * u + 2] = v.z; E[4 * u + 3] = v.w;
     };
     auto transpose_write = [&](auto stg, int t) {
@@ -211,10 +218,10 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         }
         fim(stg)[kSub * wave + tdst + 32 * t] = make_uint4(o[0], o[1], o[2], o[3]);
     };
-    // Transpose of the wave's half-block of chunk stg: raw buffer -> filter image.
-    auto transpose_all = [&](auto stg) {
+    // Transpose of the wave's half-block: raw buffer rb -> filter image stg.
+    auto transpose_all = [&](auto rb, auto stg) {
 #pragma unroll
-        for (int u = 0; u < 9; ++u) transpose_read(stg, u);
+        for (int u = 0; u < 9; ++u) transpose_read(rb, u);
 #pragma unroll
         for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
 #pragma unroll
@@ -245,7 +252,7 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         hal1[u + 1] = make_uint4(0, 0, 0, 0);
     }
 
-    // Bias of a tile's filters, seeding its accumulators: lane's filter rows
+    // Bias of a tile's filters (seeding its accumulators): lane's filter rows
     // nb*32 + 8q + 4hf .. +3 as 4 packed 16-bit values (zeros without bias).
     uint2 bz[2][4];
     auto bias_load = [&](const TileState &s) {
@@ -259,25 +266,35 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
             }
     };
 
-    // Prologue: the first tile's filters (both chunks, raw, then transposed), bias
-    // and input rows of both chunks.
+    f32x16 acc[2][2][kRun];   // [set][filter block][column]
+    // The bias seeds a tile's accumulators: row (r/4)*8 + hf*4 + r%4 of block nb is
+    // element r%4 of bz[nb][r/4].  Item q (< 32) seeds the 4 columns of (nb, r) =
+    // (q / 16, q % 16).
+    auto seed = [&](auto set, int q) {
+        constexpr int PS = decltype(set)::value;
+        const int nb = q >> 4, r = q & 15;
+        const uint32_t dwd = (r & 2) ? bz[nb][r >> 2].y : bz[nb][r >> 2].x;
+        const float b0 = half_to_f32<T>((r & 1) ? (dwd >> 16) : (dwd & 0xffffu));
+#pragma unroll
+        for (int mb = 0; mb < kRun; ++mb) acc[PS][nb][mb][r] = b0;
+    };
+
+    // Prologue: the first tile's filters (chunk 0 raw then transposed; chunk 1 raw,
+    // transposed during chunk 0), bias, and input rows of both chunks.
     TileState ts = tile_state(tile);
 #pragma unroll
-    for (int i = 0; i < kNFC; ++i) filter_copy(ts, 0, S0{}, i);
+    for (int i = 0; i < kNFC; ++i) filter_copy(ts, 0, B0{}, i);
 #pragma unroll
-    for (int i = 0; i < kNFC; ++i) filter_copy(ts, 1, S1{}, i);
+    for (int i = 0; i < kNFC; ++i) filter_copy(ts, 1, std::integral_constant<int, 1>{}, i);
     bias_load(ts);
 #pragma unroll
     for (int j = 0; j < 8 * XR; ++j) input_load(S0{}, ts, 0, j);
 #pragma unroll
     for (int j = 0; j < 8 * XR; ++j) input_load(S1{}, ts, 1, j);
-    transpose_all(S0{});
-    transpose_all(S1{});
+    transpose_all(B0{}, S0{});
 #pragma unroll
     for (int o = 0; o < XR * VW; ++o) input_write(S0{}, S0{}, o);
     __syncthreads();
-
-    f32x16 acc[2][2][kRun];   // [set][filter block][column]
 
     // The stores of the previous tile: its output base (a buffer resource at its
     // first image), the lane's byte offset from there for its first filter row
@@ -331,18 +348,11 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         const int oh = fmod_q(R, n, g.fd_oh);
         const int ow0 = kRun * jr;
         const int ub = dhalo_unit(n * g.Hp + oh * g.sh - ts.R_lo, ow0, hf, g.RSU);
+        // Seed this tile's accumulators with its bias (loaded during the previous
+        // tile's first chunk, or the prologue).
+#pragma unroll
+        for (int q = 0; q < 32; ++q) seed(par, q);
 
-        // The bias seeds the accumulators: row (r/4)*8 + hf*4 + r%4 of block nb is
-        // element r%4 of bz[nb][r/4].
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const uint32_t dwd = (r & 2) ? bz[nb][r >> 2].y : bz[nb][r >> 2].x;
-                const float b0 = half_to_f32<T>((r & 1) ? (dwd >> 16) : (dwd & 0xffffu));
-#pragma unroll
-                for (int mb = 0; mb < kRun; ++mb) acc[P][nb][mb][r] = b0;
-            }
 
         const int next_tile = tile + nbx;
         const bool has_next = next_tile < t_hi;
@@ -355,12 +365,17 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         //  * window positions of the next filter row, each read right after the MFMA
         //    that last uses it in this row;
         //  * chunk 0, slots 1-26, one per slot: the next tile's filter copies (both
-        //    chunks, into the raw buffers) and its chunk-0 bias, then the input rows
-        //    two steps ahead (the next tile's chunk 0); slots 27-58, one per slot: the
-        //    previous tile's 32 stores;
+        //    chunks, into raw0 and the raw buffer of its parity) and its bias, then the
+        //    input rows two steps ahead (the next tile's chunk 0); slots 27-58, one per
+        //    slot: the previous tile's 32 stores;
         //  * chunk 1, slots 1-16: the input rows two steps ahead (the next tile's
         //    chunk 1);
+        //  * slots 46-54 and 56-64: the transpose into the other filter image (chunk
+        //    0: this tile's chunk 1, from the raw buffer of this tile's parity; chunk 1:
+        //    the next tile's chunk 0, from raw0);
         //  * odd slots 57-71: the input staging writes into the other stage.
+        using RT = std::integral_constant<int, 1 + P>;   // this tile's chunk-1 raw buffer
+        using RN = std::integral_constant<int, 2 - P>;   // the next tile's
         auto chunk = [&](auto cur) {
             using CUR = decltype(cur);
             constexpr int C0 = CUR::value == 0;
@@ -392,14 +407,23 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
                     }
                     if (s >= 1 && s - 1 < NVM) {
                         const int o = s - 1;
-                        if (C0 && o < kNFC) filter_copy(nts, 0, S0{}, o);
-                        else if (C0 && o < 2 * kNFC) filter_copy(nts, 1, S1{}, o - kNFC);
+                        if (C0 && o < kNFC) filter_copy(nts, 0, B0{}, o);
+                        else if (C0 && o < 2 * kNFC) filter_copy(nts, 1, RN{}, o - kNFC);
                         else if (C0 && o == 2 * kNFC) bias_load(nts);
                         else input_load(cur, nts, CUR::value, o - NFIL);
                     }
                     if constexpr (C0) {
                         if (s >= 27 && s - 27 < kStores) store_item(PP{}, s - 27);
                     }
+                    if (s >= 46 && s <= 54) {
+                        if constexpr (C0) transpose_read(RT{}, s - 46);
+                        else transpose_read(B0{}, s - 46);
+                    }
+                    if (s == 55) {
+#pragma unroll
+                        for (int q = 0; q < 36; ++q) asm volatile("" : "+v"(E[q]));
+                    }
+                    if (s >= 56 && s <= 64) transpose_write(nst, s - 56);
                     if (s >= 57 && (s & 1) == 1 && (s - 57) / 2 < XR * VW) input_write(nst, nst, (s - 57) / 2);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -409,14 +433,7 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         chunk(S0{});
         chunk(S1{});
 
-        // Between the tiles: the next tile's filter images from the raw copies (made
-        // during chunk 0, before its stores), and this tile's outputs become the
-        // previous tile's.
-        if (has_next) {
-            transpose_all(S0{});
-            transpose_all(S1{});
-        }
-        __syncthreads();
+        // This tile's outputs become the previous tile's.
         pyr = make_rsrc(y + (int64_t)ts.n_first * g.Cout * OHW, 0x7fffffffu);
         pyh = run_ok ? (uint32_t)(((n - ts.n_first) * g.Cout + ts.k * g.okg) * OHW + oh * g.OW + ow0) * 2u +
                            (uint32_t)(4 * hf * fs2)
