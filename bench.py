@@ -144,7 +144,7 @@ KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_rows_mfma32x32x16"
                 "dw1d_btc_generic": "dw1d_ntc.hip", "dw2d_nhwc_tile": "nhwc.hip",
                 "igemm_nhwc_mfma32x32x16": "igemm_nhwc.hip", "conv2d_nhwc_g4": "nhwc.hip",
                 "conv2d_nhwc_g4k3": "nhwc.hip", "conv2d_nhwc_g4k3_row": "nhwc.hip",
-                "conv2d_nhwc_g4_mfma": "nhwc.hip",
+                "conv2d_nhwc_g4_mfma": "nhwc.hip", "dw2d_nhwc_pair": "nhwc.hip",
                 "conv2d_nhwc_generic": "nhwc.hip"}
 
 

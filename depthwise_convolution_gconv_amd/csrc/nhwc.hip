@@ -645,6 +645,128 @@ int nhwc_g4_mfma_gpb(const Conv2dArgs &a, size_t *lds, int *img)
     }
 }
 
+// dw2d_nhwc_pair<T, K, S>: the depthwise tile kernel for 16-bit tensors with C a
+// multiple of 8, each lane taking a pair of adjacent channels.  The patch stays in
+// the tensor's 16-bit format in LDS, one dword per (position, channel pair), so a
+// 16-byte load along C (8 channels) is one 16-byte LDS write and one window read
+// serves two channels: a tile is 128 channels x ROWS output rows x TW columns, with
+// the LDS footprint of the fp32 tile of 64 channels.
+constexpr int kCP = 2 * kCT;   // channels per tile of the pair kernel
+
+template <typename T> __device__ __forceinline__ float lo16(uint32_t v);
+template <typename T> __device__ __forceinline__ float hi16(uint32_t v);
+template <> __device__ __forceinline__ float lo16<_Float16>(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); }
+template <> __device__ __forceinline__ float hi16<_Float16>(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+template <> __device__ __forceinline__ float lo16<__bf16>(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+template <> __device__ __forceinline__ float hi16<__bf16>(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
+
+template <typename T, int K, int S>
+__global__ void __launch_bounds__(kThreads)
+dw2d_nhwc_pair(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+               T *__restrict__ y, int H, int W, int C, int OH, int OW, int ph, int pw,
+               int tiles_w, int tiles_h, int cblocks)
+{
+    constexpr int TW = Tile<K, S>::TW;
+    constexpr int RPW = Tile<K, S>::RPW;
+    constexpr int IRH = Tile<K, S>::IRH;
+    constexpr int IRW = Tile<K, S>::IRW;
+    constexpr int KK = K * K;
+    constexpr int PPP = kCP / 8;                      // 16-byte pieces per position
+    constexpr int NCH = IRH * IRW * PPP;              // staging loads per tile
+    constexpr int NB = 8;
+    __shared__ uint4 xs[IRH][IRW][kCT / 4];           // [row][column][channel pair], 4 pairs a unit
+    __shared__ float2 ws[KK][kCT];                    // [tap][channel pair]
+
+    int rest = blockIdx.x;
+    const int cb = rest % cblocks; rest /= cblocks;
+    const int tw = rest % tiles_w; rest /= tiles_w;
+    const int th = rest % tiles_h;
+    const int n = rest / tiles_h;
+    const int tid = threadIdx.x, lane = tid % kCT, rg = tid / kCT;
+    const int c0 = cb * kCP, c = c0 + 2 * lane;       // the lane's channels c, c + 1
+    const int oh0 = th * Tile<K, S>::ROWS, ow0 = tw * TW;
+    const int ih0 = oh0 * S - ph, iw0 = ow0 * S - pw;
+    // The pair's bias, loaded ahead of the staging from a valid address either way.
+    const uint32_t braw = *reinterpret_cast<const uint32_t *>((bias ? bias : w) + (c < C ? c : 0));
+
+    // Filters [tap][pair] (zero past C).
+    for (int i = tid; i < KK * kCT; i += kThreads) {
+        const int t = i / kCT, p = i % kCT, cc = c0 + 2 * p;
+        ws[t][p] = cc < C ? make_float2(to_f32(w[(int64_t)cc * KK + t]), to_f32(w[(int64_t)(cc + 1) * KK + t]))
+                          : make_float2(0.0f, 0.0f);
+    }
+    // Input patch, NB 16-byte loads in flight per thread, zero outside the image and
+    // past C (C is a multiple of 8: a piece is all in or all out).
+    const T *xn = x + (int64_t)n * H * W * C;
+    uint4 *xsu = &xs[0][0][0];
+    for (int base = 0; base < NCH; base += NB * kThreads) {
+        uint4 v[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            const int pix = i / PPP, part = i - pix * PPP;
+            const int r = pix / IRW, q = pix - r * IRW;
+            const int ih = ih0 + r, iw = iw0 + q, cc = c0 + 8 * part;
+            v[j] = make_uint4(0, 0, 0, 0);
+            if (i < NCH && ih >= 0 && ih < H && iw >= 0 && iw < W && cc < C)
+                v[j] = *reinterpret_cast<const uint4 *>(xn + ((int64_t)ih * W + iw) * C + cc);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            if (i < NCH) xsu[i] = v[j];   // unit i = (row, column, part) in row-major order
+        }
+    }
+    __syncthreads();
+
+    if (c >= C) return;
+    const uint32_t *xsp = reinterpret_cast<const uint32_t *>(&xs[0][0][0]);
+    const float b0 = bias ? lo16<T>(braw) : 0.0f, b1 = bias ? hi16<T>(braw) : 0.0f;
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+        const int lr = rg * RPW + rr, oh = oh0 + lr;
+        if (oh >= OH) break;
+        float a0[TW], a1[TW];
+#pragma unroll
+        for (int r = 0; r < TW; ++r) { a0[r] = b0; a1[r] = b1; }
+#pragma unroll
+        for (int kh = 0; kh < K; ++kh) {
+            uint32_t win[IRW];
+#pragma unroll
+            for (int q = 0; q < IRW; ++q) win[q] = xsp[((lr * S + kh) * IRW + q) * kCT + lane];
+#pragma unroll
+            for (int kw = 0; kw < K; ++kw) {
+                const float2 wv = ws[kh * K + kw][lane];
+#pragma unroll
+                for (int r = 0; r < TW; ++r) {
+                    a0[r] = fmaf(lo16<T>(win[r * S + kw]), wv.x, a0[r]);
+                    a1[r] = fmaf(hi16<T>(win[r * S + kw]), wv.y, a1[r]);
+                }
+            }
+        }
+        T *yp = y + (((int64_t)n * OH + oh) * OW + ow0) * C + c;
+#pragma unroll
+        for (int r = 0; r < TW; ++r)
+            if (ow0 + r < OW)
+                store_nt(reinterpret_cast<uint32_t *>(yp + (int64_t)r * C),
+                         (uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(a0[r])) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<T>(a1[r])) << 16));
+    }
+}
+
+template <typename T, int K, int S>
+hipError_t run_pair(const Conv2dArgs &a)
+{
+    constexpr int TW = Tile<K, S>::TW;
+    const int tiles_w = (int)ceil_div(a.OW, TW), tiles_h = (int)ceil_div(a.OH, Tile<K, S>::ROWS);
+    const int cblocks = (int)ceil_div(a.C, kCP);
+    const int64_t blocks = a.N * tiles_h * tiles_w * cblocks;
+    hipLaunchKernelGGL((dw2d_nhwc_pair<T, K, S>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, (int)a.H, (int)a.W,
+                       (int)a.C, (int)a.OH, (int)a.OW, a.ph, a.pw, tiles_w, tiles_h, cblocks);
+    return hipGetLastError();
+}
+
 template <typename T, int K, int S, int VE>
 hipError_t run_tile(const Conv2dArgs &a)
 {
@@ -682,6 +804,20 @@ hipError_t run_typed(const Conv2dArgs &a, const char **kname)
                     a.dh == 1 && a.dw == 1 && a.H * a.W * a.C < (int64_t(1) << 31) &&
                     a.N * a.OH * ceil_div(a.OW, 8 / a.sh) * ceil_div(a.C, kCT) < (int64_t(1) << 31);
     if (dw) {
+        if constexpr (sizeof(T) == 2) {
+            // 16-bit, C a multiple of 8, x 16-byte and y, w, bias 4-byte aligned: the
+            // channel-pair kernel.
+            if (a.C % 8 == 0 && (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 &&
+                ((reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.w) |
+                  reinterpret_cast<uintptr_t>(a.bias)) & 3) == 0) {
+                *kname = "dw2d_nhwc_pair";
+                switch (a.KH) {
+                case 3: return a.sh == 2 ? run_pair<T, 3, 2>(a) : run_pair<T, 3, 1>(a);
+                case 5: return a.sh == 2 ? run_pair<T, 5, 2>(a) : run_pair<T, 5, 1>(a);
+                default: return a.sh == 2 ? run_pair<T, 7, 2>(a) : run_pair<T, 7, 1>(a);
+                }
+            }
+        }
         *kname = "dw2d_nhwc_tile";
         switch (a.KH) {
         case 3: return run_tile_s<T, 3>(a);

@@ -264,6 +264,9 @@ NHWC_SWEEP = [  # N, C, Cout, H, W, KH, KW, groups, stride, pad, dil, bias
     (2, 64, 64, 8, 12, 3, 3, 16, 1, (1, 0), 1, True),  # padding on the rows only
     (1, 48, 48, 10, 10, 3, 3, 12, 1, 1, 1, False),     # 48 channels: blocks of 4 groups
     (1, 32, 32, 40, 40, 3, 3, 8, 1, 1, 1, True),       # an image too large for it: the row kernel
+    # depthwise, 16-bit channel pairs (C a multiple of 8)
+    (2, 200, 200, 11, 13, 3, 3, 200, 1, 1, 1, True),   # 2 channel blocks, the second partly empty
+    (1, 136, 136, 9, 10, 5, 5, 136, 2, 2, 1, False),   # 5x5, stride 2
 ]
 
 
@@ -310,7 +313,8 @@ def test_nhwc_sweep_vs_oracle(ci, dt):
     g4k = ("conv2d_nhwc_g4k3_row" if row else "conv2d_nhwc_g4k3") if (KH, KW) == (3, 3) else "conv2d_nhwc_g4"
     if (KH, KW) == (3, 3) and nhwc_g4_mfma_applies(C, H, W, s, p, d, dt):
         g4k = "conv2d_nhwc_g4_mfma"
-    assert gc.gconv_last_kernel() == ("dw2d_nhwc_tile" if dw else g4k if g4 else "conv2d_nhwc_generic")
+    dwk = "dw2d_nhwc_pair" if dt != "f32" and C % 8 == 0 else "dw2d_nhwc_tile"   # 16-bit channel pairs
+    assert gc.gconv_last_kernel() == (dwk if dw else g4k if g4 else "conv2d_nhwc_generic")
     assert check(as_f64(y.cpu()), r, dt)
 
 
@@ -644,7 +648,8 @@ def test_next_workload_full_size(name):
     elif wl.layout == "nhwc":
         r = oracle.conv2d_nhwc_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
         # the 4-in/4-out layers here are 16-bit, 3 x 3, unit stride and dilation, 14 x 14
-        expect = {1: "dw2d_nhwc_tile", 4: "conv2d_nhwc_g4_mfma"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
+        dwk = "dw2d_nhwc_pair" if wl.dtype != "f32" else "dw2d_nhwc_tile"
+        expect = {1: dwk, 4: "conv2d_nhwc_g4_mfma"}.get(wl.w_shape[3], "igemm_nhwc_mfma32x32x16")
         assert gc.gconv_last_kernel() == expect
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
