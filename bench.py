@@ -138,7 +138,7 @@ KERNEL_FILES = {"igemm_fwd_mfma32x32x16": "igemm.hip", "igemm_rows_mfma32x32x16"
                 "igemm_defer_mfma32x32x16": "igemm_defer.hip",
                 "igemm_fwd_f32_mfma32x32x2": "igemm_f32.hip",
                 "direct2d_g4": "direct2d.hip", "direct2d_tiled": "direct2d.hip",
-                "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip",
+                "direct2d_naive": "direct2d.hip", "dw2d_rows": "dw2d.hip", "dw2d_band": "dw2d.hip",
                 "dw1d_btc_tile": "dw1d_ntc.hip", "dw1d_btc_window": "dw1d_ntc.hip",
                 "dw1d_btc_tile_flip": "dw1d_ntc.hip",
                 "dw1d_btc_generic": "dw1d_ntc.hip", "dw2d_nhwc_tile": "nhwc.hip",

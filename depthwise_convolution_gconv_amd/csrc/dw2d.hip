@@ -38,6 +38,7 @@ constexpr int kThreads = 256;
 constexpr int kLdsTarget = 20 * 1024;     // LDS per workgroup that keeps 8 resident per CU
 constexpr int kLdsBudget = 40 * 1024;     // most LDS per workgroup (>= 4 resident per CU)
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past num_records: the load returns 0
+constexpr int kStoreNT = 2;               // buffer-store cache policy: non-temporal (outputs are not read again)
 
 struct Dw2dGeom {
     int C, H, W, Cout, OH, OW;
@@ -233,6 +234,209 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// dw2d_band<T, K, S, KR>: 16-bit layers at full width, OW * S == W (for odd K
+// that is pw = (K - 1) / 2), with W a multiple of 8 and at most 512 columns.
+//  * Chunk: 8 input columns, 16 bytes.  Run: the R = 8 / S outputs of one output
+//    row whose windows start in one chunk; the window is PW columns before the
+//    chunk, the chunk, and NWIN - 8 - PW columns after it.
+//  * Strip: KR runs stacked in one chunk column, output rows oh0 .. oh0+KR-1 of
+//    one plane (rows past OH are computed and not stored).  A wave takes G =
+//    64 / CPR strips side by side (CPR = W / 8 chunks per row), lane = slot * CPR
+//    + chunk column, so a row's chunks sit in adjacent lanes of one wave; a
+//    workgroup takes 4 G consecutive strips.
+//  * Staging: the padded input rows of the workgroup's strips (virtual rows of
+//    the padded planes, as in dw2d_rows) go to LDS chunk by chunk, coalesced
+//    16-byte buffer loads (zero outside the image), each written as one aligned
+//    16-byte LDS store.  Chunk c of staged row r sits at 16-byte unit
+//    r * CPR + c + (r / (KR * S)) * GAP with GAP = CPR * (1 - KR * S) mod 8: the
+//    strips of a wave then start CPR units apart modulo 8 units, so the chunks
+//    its lanes read together fall on distinct bank groups in every 8 lanes.
+//  * Compute: per input row of its strip a lane reads its own chunk (one 16-byte
+//    LDS read) and takes the window columns outside it from the lanes beside it
+//    by DPP wave shifts (zero at the row ends).  dw2d_rows reads the whole
+//    window per row (two 16-byte reads at 3 x 3, stride 2) and stages each row
+//    at the padding offset, 2 bytes past 16-byte alignment.  Products and sums
+//    are fp32 in the order of dw2d_rows (kh, then kw): both give the same bits.
+
+// Lane i gets lane i - 1's value (DPP wave_shr:1); lane 0 gets 0.
+__device__ __forceinline__ uint32_t from_lane_before(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xf, 0xf, false);
+}
+// Lane i gets lane i + 1's value (DPP wave_shl:1); lane 63 gets 0.
+__device__ __forceinline__ uint32_t from_lane_after(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, false);
+}
+
+// Element e of a chunk of 16-bit values held as dwords, widened to fp32.
+template <typename T> __device__ __forceinline__ float chunk_elem(const uint32_t *d, int e)
+{
+    const uint32_t v = d[e >> 1];
+    if constexpr (std::is_same_v<T, _Float16>)
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> (16 * (e & 1))));
+    else
+        return __builtin_bit_cast(float, (e & 1) ? (v & 0xffff0000u) : (v << 16));
+}
+
+struct BandGeom {
+    int C, H, W, Cout, OH, OW, ph;
+    int Hp;            // H + 2*ph: rows of one padded plane in the virtual row space
+    int planes;        // N * Cout output planes
+    int CPR;           // chunks per row (W / 8), at most 64
+    int G;             // strips side by side in one wave (64 / CPR)
+    int SPP;           // strips per output plane (ceil(OH / KR))
+    int strips;        // planes * SPP
+    int spw;           // strips per workgroup (4 G)
+    int GAP;           // 16-byte units left free after every KR * S staged rows
+    int units;         // 16-byte LDS units reserved for the staged rows (the filters follow)
+    int wgs, wgs_per_xcd;
+    FastDiv fd_cpr, fd_spp, fd_hp, fd_cout, fd_m;
+};
+
+template <typename T, int K, int S, int KR>
+__global__ void __launch_bounds__(kThreads)
+dw2d_band(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
+          T *__restrict__ y, BandGeom g)
+{
+    static_assert(sizeof(T) == 2, "16-bit tensors");
+    constexpr int R = 8 / S;                    // outputs per run
+    constexpr int PW = (K - 1) / 2;             // window columns before the chunk
+    constexpr int NWIN = (R - 1) * S + K;       // window columns of a run
+    constexpr int NAFT = NWIN - 8 - PW;         // window columns after the chunk (<= 0: none)
+    constexpr int NRW = (KR - 1) * S + K;       // input rows of a strip
+    constexpr int BAND = KR * S;                // staged rows per gap
+    constexpr int KK = K * K;
+    constexpr int DB = (8 - PW) / 2;            // first dword of the lane before that the window uses
+    constexpr int DA = NAFT > 0 ? (NAFT + 1) / 2 : 0;   // dwords of the lane after that it uses
+    constexpr int NB = 8;                       // staging loads in flight per thread
+    constexpr int RB = R * 2;                   // bytes of one run of outputs
+    extern __shared__ uint4 lds[];              // [units] staged rows, then [planes][K*K + 1] fp32
+    float *ws = reinterpret_cast<float *>(lds + g.units);
+
+    const int xcd = blockIdx.x & 7, rank = blockIdx.x >> 3;
+    const int wg = xcd * g.wgs_per_xcd + rank;
+    if (wg >= min((xcd + 1) * g.wgs_per_xcd, g.wgs)) return;   // uniform over the workgroup
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slot = fdiv(lane, g.fd_cpr), rc = lane - slot * g.CPR;
+    const int s_first = wg * g.spw, s_last = min(s_first + g.spw, g.strips) - 1;
+    const int pa = fdiv(s_first, g.fd_spp), pb = fdiv(s_last, g.fd_spp);
+    // Staged rows: from the first strip's first padded row to the last strip's last.
+    const int R_lo = pa * g.Hp + (s_first - pa * g.SPP) * BAND;
+    const int NR = pb * g.Hp + (s_last - pb * g.SPP) * BAND + NRW - R_lo;
+
+    // Input plane read by output plane q: image n = q / Cout, channel (q % Cout) / M.
+    auto in_plane = [&](int q) {
+        const int n = fdiv(q, g.fd_cout);
+        return n * g.C + fdiv(q - n * g.Cout, g.fd_m);
+    };
+    // Offsets relative to the workgroup's first input and output planes (the host
+    // bounds both spans to 31 bits); kOOB reads 0 and drops stores.
+    const int pia = in_plane(pa);
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(x + (int64_t)pia * g.H * g.W), (short)0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+        y + (int64_t)pa * g.OH * g.OW, (short)0, 0x7fffffff, 0x00020000);
+
+    // Stage the rows, NB loads per thread in flight at a time.
+    const int nchunks = NR * g.CPR;
+    for (int base = 0; base < nchunks; base += NB * kThreads) {
+        uint32_t d[NB][4];
+        int dst[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const int i = base + j * kThreads + tid;
+            uint32_t off = kOOB;
+            dst[j] = -1;
+            if (i < nchunks) {
+                const int r = fdiv(i, g.fd_cpr), c = i - r * g.CPR;
+                const int vrow = R_lo + r;
+                const int p = fdiv(vrow, g.fd_hp), ih = vrow - p * g.Hp - g.ph;
+                if (p < g.planes && ih >= 0 && ih < g.H)
+                    off = (uint32_t)((((in_plane(p) - pia) * g.H + ih) * g.W + 8 * c) * 2);
+                dst[j] = r * g.CPR + c + (r / BAND) * g.GAP;
+            }
+            Load<16>::run(xr, off, d[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+            if (dst[j] >= 0) lds[dst[j]] = make_uint4(d[j][0], d[j][1], d[j][2], d[j][3]);
+    }
+    // Filters of output planes pa .. pb, each followed by the plane's bias (zero
+    // without one), from addresses that are always valid.
+    for (int i = tid; i < (pb - pa + 1) * (KK + 1); i += kThreads) {
+        const int q = pa + i / (KK + 1), t = i - (i / (KK + 1)) * (KK + 1);
+        const int o = q - fdiv(q, g.fd_cout) * g.Cout;
+        const bool has = t < KK || bias != nullptr;
+        const T *src = t < KK ? w + (int64_t)o * KK + t : (has ? bias + o : w);
+        const float v = to_f32(*src);
+        ws[i] = has ? v : 0.0f;
+    }
+    __syncthreads();
+
+    // This lane's strip (lanes past the wave's strips, and strips past the
+    // workgroup's, are idle: they take the first strip and store nothing).
+    const int s = s_first + wave * g.G + slot;
+    const bool act = slot < g.G && s <= s_last;
+    const int sc = act ? s : s_first;
+    const int p = fdiv(sc, g.fd_spp), oh0 = (sc - p * g.SPP) * KR;
+    const int lr0 = p * g.Hp + oh0 * S - R_lo;   // staged row of the strip's first input row
+    const float *wt = ws + (p - pa) * (KK + 1);
+    float wk[KK + 1];
+#pragma unroll
+    for (int t = 0; t <= KK; ++t) wk[t] = wt[t];
+    // The DPP moves run on the whole wave (a lane reads its neighbour's register, so
+    // no lane may be masked off); the row ends are cleared afterwards with masks.
+    const uint32_t keep_before = rc == 0 ? 0u : ~0u, keep_after = rc == g.CPR - 1 ? 0u : ~0u;
+    float acc[KR][R];
+#pragma unroll
+    for (int i = 0; i < KR; ++i)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[i][j] = wk[KK];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+        const int lr = lr0 + r;
+        const uint4 q = lds[lr * g.CPR + rc + (lr / BAND) * g.GAP];
+        const uint32_t own[4] = {q.x, q.y, q.z, q.w};
+        uint32_t bef[4], aft[4];
+#pragma unroll
+        for (int e = DB; e < 4; ++e) bef[e] = from_lane_before(own[e]) & keep_before;
+#pragma unroll
+        for (int e = 0; e < DA; ++e) aft[e] = from_lane_after(own[e]) & keep_after;
+        float win[NWIN];
+#pragma unroll
+        for (int t = 0; t < NWIN; ++t) {
+            const int c = t - PW;
+            win[t] = c < 0 ? chunk_elem<T>(bef, 8 + c) : c < 8 ? chunk_elem<T>(own, c) : chunk_elem<T>(aft, c - 8);
+        }
+#pragma unroll
+        for (int i = 0; i < KR; ++i) {
+            const int kh = r - i * S;
+            if (kh >= 0 && kh < K) {
+#pragma unroll
+                for (int kw = 0; kw < K; ++kw)
+#pragma unroll
+                    for (int j = 0; j < R; ++j) acc[i][j] = fmaf(win[j * S + kw], wk[kh * K + kw], acc[i][j]);
+            }
+        }
+    }
+    // Branch-free stores: rows past OH and idle lanes get the dropped offset.
+    const int row0 = (p - pa) * g.OH + oh0;
+#pragma unroll
+    for (int i = 0; i < KR; ++i) {
+        const uint32_t off = act && oh0 + i < g.OH ? (uint32_t)((row0 + i) * g.OW * 2 + rc * RB) : kOOB;
+        uint32_t d[RB / 4];
+#pragma unroll
+        for (int e = 0; e < RB / 4; ++e) d[e] = bits_of<T>(acc[i][2 * e]) | (bits_of<T>(acc[i][2 * e + 1]) << 16);
+        if constexpr (RB == 8)
+            __builtin_amdgcn_raw_buffer_store_b64(gconv_u32x2{d[0], d[1]}, yr, off, 0, kStoreNT);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(gconv_u32x4{d[0], d[1], d[2], d[3]}, yr, off, 0, kStoreNT);
+    }
+}
+
 struct Plan {
     Dw2dGeom g;
     int K, S, R, VI;
@@ -368,12 +572,131 @@ hipError_t run_typed(const Conv2dArgs &a, const Plan &pl)
     }
 }
 
+struct BandPlan {
+    BandGeom g;
+    int K, S, KR;
+    size_t lds;
+    bool ok;
+};
+
+// Staged rows of a workgroup of spw strips at most (bound over all workgroups), and
+// the LDS they and the filter table take.
+int64_t band_rows(int64_t spw, int64_t SPP, int64_t Hp, int64_t planes, int KR, int S, int K)
+{
+    const int64_t NRW = (int64_t)(KR - 1) * S + K;
+    const int64_t band = (int64_t)KR * S;
+    // c plane boundaries crossed add c * (Hp - SPP * band) rows to (spw - 1) * band + NRW.
+    const int64_t cmax = std::min<int64_t>(spw <= 1 ? 0 : (spw - 2) / SPP + 1, planes - 1);
+    return (spw - 1) * band + NRW + std::max<int64_t>(0, cmax * (Hp - SPP * band));
+}
+
+BandPlan make_band_plan(const Conv2dArgs &a)
+{
+    BandPlan pl{};
+    pl.ok = false;
+    if (a.dtype == DT_F32) return pl;
+    if (a.groups != a.C || a.KH != a.KW || (a.KH != 3 && a.KH != 5 && a.KH != 7)) return pl;
+    if (a.sh != a.sw || (a.sh != 1 && a.sh != 2) || a.dh != 1 || a.dw != 1) return pl;
+    if (a.ph > a.KH) return pl;
+    if (a.interleaved && a.Cout != a.C) return pl;
+    const int K = (int)a.KH, S = a.sh, R = 8 / S;
+    // Full width: every chunk of a row starts one run (OW * S == W), and a row's
+    // chunks fit in one wave.
+    if (a.pw != (K - 1) / 2 || a.OW * S != a.W || a.W % 8 != 0 || a.W / 8 > 64) return pl;
+    if (reinterpret_cast<uintptr_t>(a.x) % 16 != 0) return pl;
+    if (reinterpret_cast<uintptr_t>(a.y) % (uintptr_t)(R * 2) != 0) return pl;
+    const int64_t planes = a.N * a.Cout;
+    const int64_t Hp = a.H + 2 * (int64_t)a.ph;
+    const int CPR = (int)(a.W / 8), G = 64 / CPR, spw = 4 * G;
+    const int KK1 = K * K + 1;
+    // Two output rows per strip where the staged rows fit kLdsTarget (8 workgroups
+    // per CU), else one; planes shorter than a strip would leave most of it empty.
+    auto lds_for = [&](int KR, int64_t *units) {
+        const int64_t SPP = ceil_div(a.OH, (int64_t)KR);
+        const int64_t NR = std::min<int64_t>(band_rows(spw, SPP, Hp, planes, KR, S, K),
+                                             planes * Hp + (int64_t)(KR - 1) * S + K);
+        const int GAP = (int)(((int64_t)CPR * (1 - KR * S) % 8 + 8) % 8);
+        *units = NR * CPR + (NR / (KR * S) + 1) * GAP;
+        const int64_t NP = std::min<int64_t>(planes, (spw - 1) / SPP + 2);
+        return *units * 16 + NP * KK1 * (int64_t)sizeof(float);
+    };
+    int64_t units = 0;
+    int KR = 2;
+    if (a.OH < 2 || lds_for(2, &units) > kLdsTarget) KR = 1;
+    const int64_t bytes = lds_for(KR, &units);
+    if (bytes > kLdsBudget) return pl;
+    const int64_t SPP = ceil_div(a.OH, (int64_t)KR);
+    const int64_t strips = planes * SPP;
+    if (strips + spw >= (int64_t(1) << 31) || planes * Hp + 2 * K >= (int64_t(1) << 31)) return pl;
+    // Offsets relative to a workgroup's first input / output plane fit 31 bits.
+    const int64_t NP = std::min<int64_t>(planes, (spw - 1) / SPP + 2);
+    if ((NP + 1) * a.H * a.W * 2 >= (int64_t(1) << 31) || (NP + 1) * a.OH * a.OW * 2 >= (int64_t(1) << 31)) return pl;
+    BandGeom &g = pl.g;
+    g.C = (int)a.C; g.H = (int)a.H; g.W = (int)a.W; g.Cout = (int)a.Cout;
+    g.OH = (int)a.OH; g.OW = (int)a.OW; g.ph = a.ph;
+    g.Hp = (int)Hp;
+    g.planes = (int)planes;
+    g.CPR = CPR;
+    g.G = G;
+    g.SPP = (int)SPP;
+    g.strips = (int)strips;
+    g.spw = spw;
+    g.GAP = (int)(((int64_t)CPR * (1 - KR * S) % 8 + 8) % 8);
+    g.units = (int)units;
+    g.wgs = (int)ceil_div(strips, (int64_t)spw);
+    g.wgs_per_xcd = (int)ceil_div(g.wgs, 8);
+    g.fd_cpr = make_fastdiv((uint32_t)CPR);
+    g.fd_spp = make_fastdiv((uint32_t)SPP);
+    g.fd_hp = make_fastdiv((uint32_t)Hp);
+    g.fd_cout = make_fastdiv((uint32_t)a.Cout);
+    g.fd_m = make_fastdiv((uint32_t)(a.Cout / a.C));
+    pl.K = K;
+    pl.S = S;
+    pl.KR = KR;
+    pl.lds = (size_t)bytes;
+    pl.ok = true;
+    return pl;
+}
+
+template <typename T, int K, int S, int KR>
+hipError_t run_band(const Conv2dArgs &a, const BandPlan &pl)
+{
+    const unsigned blocks = (unsigned)(8 * (int64_t)pl.g.wgs_per_xcd);
+    hipLaunchKernelGGL((dw2d_band<T, K, S, KR>), dim3(blocks), dim3(kThreads), pl.lds, a.stream,
+                       (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, pl.g);
+    return hipGetLastError();
+}
+
+template <typename T, int K, int S>
+hipError_t run_band_kr(const Conv2dArgs &a, const BandPlan &pl)
+{
+    return pl.KR == 2 ? run_band<T, K, S, 2>(a, pl) : run_band<T, K, S, 1>(a, pl);
+}
+
+template <typename T>
+hipError_t run_band_typed(const Conv2dArgs &a, const BandPlan &pl)
+{
+    switch (pl.K * 4 + pl.S) {
+    case 13: return run_band_kr<T, 3, 1>(a, pl);
+    case 14: return run_band_kr<T, 3, 2>(a, pl);
+    case 21: return run_band_kr<T, 5, 1>(a, pl);
+    case 22: return run_band_kr<T, 5, 2>(a, pl);
+    case 29: return run_band_kr<T, 7, 1>(a, pl);
+    default: return run_band_kr<T, 7, 2>(a, pl);
+    }
+}
+
 }  // namespace
 
-bool dw2d_supported(const Conv2dArgs &a) { return make_plan(a).ok; }
+bool dw2d_supported(const Conv2dArgs &a) { return make_band_plan(a).ok || make_plan(a).ok; }
 
 hipError_t launch_dw2d(const Conv2dArgs &a, const char **kname)
 {
+    const BandPlan bp = make_band_plan(a);
+    if (bp.ok) {
+        *kname = "dw2d_band";
+        return a.dtype == DT_F16 ? run_band_typed<_Float16>(a, bp) : run_band_typed<__bf16>(a, bp);
+    }
     const Plan pl = make_plan(a);
     if (!pl.ok) return hipErrorInvalidValue;
     *kname = "dw2d_rows";

@@ -221,7 +221,29 @@ DW2D_SWEEP = [  # N, C, M (filters per channel), H, W, K, stride, pad, bias
     (2, 4, 2, 12, 16, 3, 2, 1, False),    # two filters per channel, stride 2, 16-byte runs in 16-bit
     (1, 4, 1, 9, 9, 3, 3, 1, True),       # stride 3: not this kernel (tiled)
     (1, 4, 1, 9, 9, 4, 1, 1, True),       # even filter: not this kernel (tiled)
+    # full-width layers (OW * stride == W, W a multiple of 8): dw2d_band in 16-bit
+    (2, 3, 1, 70, 8, 3, 1, 1, True),      # one chunk per row: 64 strips side by side in a wave
+    (1, 4, 2, 80, 16, 5, 2, 2, True),     # two filters per channel, 5x5 stride 2
+    (1, 2, 1, 68, 56, 7, 2, 3, True),     # 7x7 stride 2
+    (2, 5, 1, 66, 40, 3, 2, 1, False),    # 33 output rows: a half-empty last strip; 5 chunks per row (4 idle lanes)
+    (1, 2, 1, 64, 512, 3, 1, 1, True),    # 64 chunks per row: one strip per wave
+    (1, 2, 3, 16, 40, 5, 1, 2, True),     # three filters per channel, stride 1
+    (4, 33, 1, 37, 24, 3, 2, 1, True),    # one output row per strip (LDS), many planes per workgroup
+    (1, 3, 1, 21, 24, 7, 1, 3, True),     # 7x7 stride 1, odd output rows
+    (3, 2, 1, 50, 8, 3, 2, 0, True),      # no vertical padding
+    (1, 1, 1, 1, 8, 3, 2, 1, True),       # a single output row
 ]
+
+
+def dw2d_kernel(N, C, M, H, W, K, s, p, dt):
+    """The depthwise conv2d kernel the dispatcher picks for an aligned NCHW layer
+    (every full-width layer here fits the band kernel's LDS)."""
+    if K not in (3, 5, 7) or s not in (1, 2):
+        return "direct2d_tiled"
+    OW = (W + 2 * p - K) // s + 1
+    if dt != "f32" and p == (K - 1) // 2 and OW * s == W and W % 8 == 0 and W // 8 <= 64:
+        return "dw2d_band"
+    return "dw2d_rows"
 
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
@@ -234,8 +256,7 @@ def test_dw2d_sweep_vs_oracle(ci, dt):
     b = draw((C * M,), 0.01, 9700 + seed, dt) if has_b else None
     r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=p, dilation=1, groups=C)
     y = run_conv2d(x, w, b, s, p, 1, C, "auto")
-    expect = "dw2d_rows" if K in (3, 5, 7) and s in (1, 2) else "direct2d_tiled"
-    assert gc.gconv_last_kernel() == expect
+    assert gc.gconv_last_kernel() == dw2d_kernel(N, C, M, H, W, K, s, p, dt)
     assert check(as_f64(y.cpu()), r, dt)
 
 
@@ -653,7 +674,9 @@ def test_next_workload_full_size(name):
         assert gc.gconv_last_kernel() == expect
     else:
         r = oracle.conv2d_at(xd, wd, idx, bd, wl.stride, wl.pad, wl.dilation, wl.groups)
-        assert gc.gconv_last_kernel() == "dw2d_rows"
+        N, C, H, W = wl.x_shape
+        assert gc.gconv_last_kernel() == dw2d_kernel(N, C, wl.w_shape[0] // C, H, W, wl.w_shape[2],
+                                                     wl.stride, wl.pad, wl.dtype)
     err = normwise(yc.ravel()[idx], r)
     print(f"{name}: kernel={gc.gconv_last_kernel()} normwise err={err:.3e} "
           f"elementwise over |r| > 1e-3 max|r| {elementwise(yc.ravel()[idx], r):.3e}")
