@@ -38,7 +38,6 @@ constexpr int kThreads = 256;
 constexpr int kLdsTarget = 20 * 1024;     // LDS per workgroup that keeps 8 resident per CU
 constexpr int kLdsBudget = 40 * 1024;     // most LDS per workgroup (>= 4 resident per CU)
 constexpr uint32_t kOOB = 0x80000000u;    // buffer offset past num_records: the load returns 0
-constexpr int kStoreNT = 2;               // buffer-store cache policy: non-temporal (outputs are not read again)
 
 struct Dw2dGeom {
     int C, H, W, Cout, OH, OW;
@@ -422,7 +421,11 @@ dw2d_band(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
             }
         }
     }
-    // Branch-free stores: rows past OH and idle lanes get the dropped offset.
+    // Branch-free stores: rows past OH and idle lanes get the dropped offset.  Store
+    // i writes row i of every strip, so it covers every other output row of the
+    // wave and a line is completed by the next store.  Write-back stores let L2
+    // join the two halves; non-temporal ones reached HBM as partial lines (1.5x
+    // the output bytes on the 8 x 256 x 512 x 40 layer).
     const int row0 = (p - pa) * g.OH + oh0;
 #pragma unroll
     for (int i = 0; i < KR; ++i) {
@@ -431,9 +434,9 @@ dw2d_band(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
 #pragma unroll
         for (int e = 0; e < RB / 4; ++e) d[e] = bits_of<T>(acc[i][2 * e]) | (bits_of<T>(acc[i][2 * e + 1]) << 16);
         if constexpr (RB == 8)
-            __builtin_amdgcn_raw_buffer_store_b64(gconv_u32x2{d[0], d[1]}, yr, off, 0, kStoreNT);
+            __builtin_amdgcn_raw_buffer_store_b64(gconv_u32x2{d[0], d[1]}, yr, off, 0, 0);
         else
-            __builtin_amdgcn_raw_buffer_store_b128(gconv_u32x4{d[0], d[1], d[2], d[3]}, yr, off, 0, kStoreNT);
+            __builtin_amdgcn_raw_buffer_store_b128(gconv_u32x4{d[0], d[1], d[2], d[3]}, yr, off, 0, 0);
     }
 }
 
