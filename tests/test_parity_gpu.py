@@ -230,7 +230,7 @@ DW2D_SWEEP = [  # N, C, M (filters per channel), H, W, K, stride, pad, bias
     (1, 2, 3, 16, 40, 5, 1, 2, True),     # three filters per channel, stride 1
     (4, 33, 1, 37, 24, 3, 2, 1, True),    # one output row per strip (LDS), many planes per workgroup
     (1, 3, 1, 21, 24, 7, 1, 3, True),     # 7x7 stride 1, odd output rows
-    (3, 2, 1, 50, 8, 3, 2, 0, True),      # no vertical padding
+    (3, 2, 1, 50, 8, 3, 2, 0, True),      # no padding: output narrower than W/2, dw2d_rows
     (1, 1, 1, 1, 8, 3, 2, 1, True),       # a single output row
 ]
 
@@ -461,6 +461,30 @@ def test_autotune_skips_routes_that_cannot_run_the_call():
     x, w, b = (gpu(t) for t in make_inputs(wl))
     assert gc.gconv_autotune(x, w, b, wl.stride, wl.pad, wl.dilation, wl.groups, "ntc", reps=2) == "direct"
     gc.gconv_autotune_clear()
+
+
+# dw2d_band with vertical padding other than the filter's half (the horizontal one
+# is fixed by the full-width condition).
+BAND_PAD = [  # N, C, M, H, W, K, stride, (ph, pw), bias
+    (2, 3, 1, 20, 16, 3, 2, (0, 1), True),     # no vertical padding
+    (1, 4, 2, 17, 24, 3, 2, (2, 1), False),    # two padding rows: zero rows inside a strip
+    (2, 2, 1, 19, 40, 5, 1, (0, 2), True),
+    (1, 3, 1, 23, 8, 7, 2, (1, 3), True),
+]
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(BAND_PAD)))
+def test_dw2d_band_vertical_padding(ci, dt):
+    N, C, M, H, W, K, s, pad, has_b = BAND_PAD[ci]
+    seed = 40 * ci + {"f16": 1, "bf16": 2}[dt]
+    x = draw((N, C, H, W), 1.0, 7300 + seed, dt)
+    w = draw((C * M, 1, K, K), 1.0 / (K * K), 8300 + seed, dt)
+    b = draw((C * M,), 0.01, 9300 + seed, dt) if has_b else None
+    r = oracle.conv2d(as_f64(x), as_f64(w), as_f64(b), stride=s, padding=pad, dilation=1, groups=C)
+    y = run_conv2d(x, w, b, s, pad, 1, C, "auto")
+    assert gc.gconv_last_kernel() == "dw2d_band"
+    assert check(as_f64(y.cpu()), r, dt)
 
 
 def test_dw2d_unaligned_output_and_input():
