@@ -9,6 +9,9 @@
 // Conformer's 1-D depthwise conv (Fast Conformer's subsampling CNN, which needs
 // stride).
 //
+// Two kernels: dw2d_band (below dw2d_rows) for 16-bit layers whose output rows
+// cover the input rows exactly (OW * S == W), dw2d_rows for the rest.
+//
 // dw2d_rows<T, K, S, R, VI>: K x K filters, stride S, dilation 1.
 //  * Work unit: a run of R consecutive outputs of one output row (R*sizeof(T) =
 //    16 or 8 bytes, or R = 1).  Runs are numbered over (output plane, row, run),
