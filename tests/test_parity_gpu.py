@@ -232,6 +232,7 @@ DW2D_SWEEP = [  # N, C, M (filters per channel), H, W, K, stride, pad, bias
     (1, 3, 1, 21, 24, 7, 1, 3, True),     # 7x7 stride 1, odd output rows
     (3, 2, 1, 50, 8, 3, 2, 0, True),      # no padding: output narrower than W/2, dw2d_rows
     (1, 1, 1, 1, 8, 3, 2, 1, True),       # a single output row
+    (3, 4, 1, 65, 40, 3, 2, 1, True),     # a plane's last strip reads into the next plane's padded rows
 ]
 
 
