@@ -293,6 +293,7 @@ struct BandGeom {
     int spw;           // strips per workgroup (4 G)
     int GAP;           // 16-byte units left free after every KR * S staged rows
     int units;         // 16-byte LDS units reserved for the staged rows (the filters follow)
+    int sp_p, sp_hp;   // 4G staged rows as (planes, rows) of the padded row space
     int wgs, wgs_per_xcd;
     FastDiv fd_cpr, fd_spp, fd_hp, fd_cout, fd_m;
 };
@@ -342,29 +343,41 @@ dw2d_band(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
         y + (int64_t)pa * g.OH * g.OW, (short)0, 0x7fffffff, 0x00020000);
 
-    // Stage the rows, NB loads per thread in flight at a time.
-    const int nchunks = NR * g.CPR;
-    for (int base = 0; base < nchunks; base += NB * kThreads) {
-        uint32_t d[NB][4];
-        int dst[NB];
+    // Stage the rows, NB loads per thread in flight at a time.  A thread takes chunk
+    // rc of staged rows r = wave * G + slot + k * 4G (the compute lanes' mapping: a
+    // load instruction covers G consecutive rows, contiguous in x within a plane).
+    // The row advances by 4G, a multiple of BAND, so the plane and row within it
+    // advance by a fixed step and the LDS unit by a fixed stride: no division per row.
+    {
+        const int rstep = 4 * g.G;
+        const int r0 = wave * g.G + slot;
+        int vr = R_lo + r0;
+        int sp = fdiv(vr, g.fd_hp);
+        int shp = vr - sp * g.Hp;                     // row within the padded plane
+        int su = r0 * g.CPR + rc + (r0 / BAND) * g.GAP;
+        const int ustep = rstep * g.CPR + (rstep / BAND) * g.GAP;
+        const bool lane_ok = slot < g.G;
+        for (int kb = r0; kb < NR; kb += NB * rstep) {
+            uint32_t d[NB][4];
+            int dst[NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int i = base + j * kThreads + tid;
-            uint32_t off = kOOB;
-            dst[j] = -1;
-            if (i < nchunks) {
-                const int r = fdiv(i, g.fd_cpr), c = i - r * g.CPR;
-                const int vrow = R_lo + r;
-                const int p = fdiv(vrow, g.fd_hp), ih = vrow - p * g.Hp - g.ph;
-                if (p < g.planes && ih >= 0 && ih < g.H)
-                    off = (uint32_t)((((in_plane(p) - pia) * g.H + ih) * g.W + 8 * c) * 2);
-                dst[j] = r * g.CPR + c + (r / BAND) * g.GAP;
+            for (int j = 0; j < NB; ++j) {
+                const int r = kb + j * rstep;
+                const int ih = shp - g.ph;
+                const bool ok = lane_ok && r < NR && sp < g.planes && ih >= 0 && ih < g.H;
+                const uint32_t off =
+                    ok ? (uint32_t)((((in_plane(sp) - pia) * g.H + ih) * g.W + 8 * rc) * 2) : kOOB;
+                dst[j] = lane_ok && r < NR ? su : -1;
+                Load<16>::run(xr, off, d[j]);
+                su += ustep;
+                shp += g.sp_hp;
+                sp += g.sp_p;
+                if (shp >= g.Hp) { shp -= g.Hp; ++sp; }
             }
-            Load<16>::run(xr, off, d[j]);
-        }
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-            if (dst[j] >= 0) lds[dst[j]] = make_uint4(d[j][0], d[j][1], d[j][2], d[j][3]);
+            for (int j = 0; j < NB; ++j)
+                if (dst[j] >= 0) lds[dst[j]] = make_uint4(d[j][0], d[j][1], d[j][2], d[j][3]);
+        }
     }
     // Filters of output planes pa .. pb, each followed by the plane's bias (zero
     // without one), from addresses that are always valid.
@@ -649,6 +662,8 @@ BandPlan make_band_plan(const Conv2dArgs &a)
     g.spw = spw;
     g.GAP = (int)(((int64_t)CPR * (1 - KR * S) % 8 + 8) % 8);
     g.units = (int)units;
+    g.sp_p = (int)(4 * G / Hp);
+    g.sp_hp = (int)(4 * G % Hp);
     g.wgs = (int)ceil_div(strips, (int64_t)spw);
     g.wgs_per_xcd = (int)ceil_div(g.wgs, 8);
     g.fd_cpr = make_fastdiv((uint32_t)CPR);
