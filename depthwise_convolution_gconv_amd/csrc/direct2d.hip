@@ -193,15 +193,21 @@ constexpr int kG4Filters = 36;    // LDS entries of a group's filters: [tap][out
 constexpr int kG4Step = 62;       // output anchors per pass: lanes 62 and 63 only supply shifted operands
 
 // q / d for 0 <= q < 2048 and 1 <= d <= 400 as (q * m) >> 20 with m = ceil(2^20 / d):
-// exact on that range (checked exhaustively on the host side of the tests).
-__device__ __forceinline__ int g4_div(int q, uint32_t m) { return (int)(((uint32_t)q * m) >> 20); }
+// exact on that range (checked exhaustively on the host side of the tests).  Both
+// factors are below 2^24 and the product below 2^31, so the full-rate 24-bit
+// multiply gives it exactly.
+__device__ __forceinline__ int g4_div(int q, uint32_t m) { return (int)(__umul24((uint32_t)q, m) >> 20); }
+// a * b for 0 <= a, b < 2^24 with a product below 2^31 (image positions and sizes).
+__device__ __forceinline__ int g4_mul(int a, int b) { return (int)__umul24((uint32_t)a, (uint32_t)b); }
 
-// The value lane + 1 holds (lane 63 keeps its own; its result is not used).
+// The value lane + 1 holds (lane 63 receives zero; its result is not used).  A DPP
+// move with no old value, so the compiler need not copy the source first.
 __device__ __forceinline__ uint2 g4_next_lane(uint2 v)
 {
-    return make_uint2((uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0x130, 0xf, 0xf, false),
-                      (uint32_t)__builtin_amdgcn_update_dpp((int)v.y, (int)v.y, 0x130, 0xf, 0xf, false));
+    return make_uint2((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x130, 0xf, 0xf, true),
+                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x130, 0xf, 0xf, true));
 }
+constexpr int kG4NT = 2;   // buffer-store cache policy: non-temporal
 
 // LDS entries (8 bytes each) of one wave's slab: the padded image and the entries
 // past it that the last pass's lanes may read, the filters, and the staged outputs.
@@ -260,39 +266,43 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
     const T *xg = x + ((int64_t)n * C + 4 * k) * HW;
     const T *wg = w + (int64_t)(4 * k) * 36;   // [output o][input c][tap t]
     const int npair = HW / 2;
+    // The slab's 4 channels as one buffer: a lane's pair offset is shared by the 4
+    // loads, the channel offset is a scalar.
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(xg), (short)0, 8 * HW, 0x00020000);
     uint32_t xv[kMaxL][4], wv[3];
 #pragma unroll
     for (int j = 0; j < kMaxL; ++j) {
         if (64 * j < npair) {   // uniform; the pair index is clamped, not branched on
             const int q = min(lane + 64 * j, npair - 1);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) xv[j][c] = *reinterpret_cast<const uint32_t *>(xg + c * HW + 2 * q);
+            for (int c = 0; c < 4; ++c) xv[j][c] = __builtin_amdgcn_raw_buffer_load_b32(xr, 4 * q, 2 * c * HW, 0);
         }
     }
 #pragma unroll
     for (int j = 0; j < 3; ++j) wv[j] = bits16(wg[min(lane + 64 * j, 143)]);
     const T *bp = bias ? bias + 4 * k : wg;   // loaded either way; zero when there is no bias
-    g4_f32x4 b0;
+    T braw[4];
 #pragma unroll
-    for (int o = 0; o < 4; ++o) b0[o] = to_f32(bp[o]);
-    if (!bias) b0 = g4_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int o = 0; o < 4; ++o) braw[o] = bp[o];
     __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
 
-    // The padded image: border positions zero (the ph top and bottom rows, then the
-    // pw left and right columns of every image row), image positions from the pairs.
+    // The padded image: border positions zero (with padding 0 or 1: the top and
+    // bottom rows, 2*ph*WP entries, then the left and right columns of the H image
+    // rows, 2*pw*H entries), image positions from the pairs.
     const int nborder = HP * WP - HW;
     for (int i = lane; i < nborder; i += 64) {
         int hp, wp;
         if (i < 2 * ph * WP) {
-            const int r = i / WP;
-            hp = r < ph ? r : H + r;
-            wp = i - r * WP;
+            const bool bottom = i >= WP;
+            hp = bottom ? HP - 1 : 0;
+            wp = bottom ? i - WP : i;
         } else {
-            const int j = i - 2 * ph * WP, r = j / (2 * pw), sd = j - r * (2 * pw);
-            hp = ph + r;
-            wp = sd < pw ? sd : W + sd;
+            const int j = i - 2 * ph * WP;
+            hp = ph + (j >> 1);
+            wp = (j & 1) ? WP - 1 : 0;
         }
-        xs[hp * WP + wp] = make_uint2(0, 0);
+        xs[g4_mul(hp, WP) + wp] = make_uint2(0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kMaxL; ++j) {
@@ -301,10 +311,10 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int p = 2 * q + e;
-                const int h = g4_div(p, mw), ww = p - h * W;
+                const int h = g4_div(p, mw), ww = p - g4_mul(h, W);
                 // half e of each channel's pair: channels (0,1) and (2,3) side by side
                 const uint32_t sel = e ? 0x07060302u : 0x05040100u;
-                xs[(h + ph) * WP + ww + pw] = make_uint2(__builtin_amdgcn_perm(xv[j][1], xv[j][0], sel),
+                xs[g4_mul(h + ph, WP) + ww + pw] = make_uint2(__builtin_amdgcn_perm(xv[j][1], xv[j][0], sel),
                                                          __builtin_amdgcn_perm(xv[j][3], xv[j][2], sel));
             }
         }
@@ -324,6 +334,9 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
     for (int t = 0; t < 9; ++t) fa[t] = fs[t * 4 + (lane & 3)];
 
+    g4_f32x4 b0;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) b0[o] = bias ? to_f32(braw[o]) : 0.0f;
     const int na = (OH - 1) * WP + OW;
     T *yg = y + ((int64_t)n * C + k * okg) * OHW;   // filter o of the group: channel o*ocs + k*okg
     for (int a0 = 0; a0 < na; a0 += kG4Step) {
@@ -338,9 +351,9 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
             acc = Mfma4<T>::run(fa[kh * 3 + 1], v1, acc);
             acc = Mfma4<T>::run(fa[kh * 3 + 2], v2, acc);
         }
-        const int oh = g4_div(a, mwp), ow = a - oh * WP;
+        const int oh = g4_div(a, mwp), ow = a - g4_mul(oh, WP);
         if (lane < kG4Step && a < na && ow < OW) {
-            const int p = oh * OW + ow;
+            const int p = g4_mul(oh, OW) + ow;
             if (ystage) {
                 ys[p] = make_uint2(bits16(from_f32<T>(acc[0])) | (bits16(from_f32<T>(acc[1])) << 16),
                                    bits16(from_f32<T>(acc[2])) | (bits16(from_f32<T>(acc[3])) << 16));
@@ -356,16 +369,21 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
         // entries of 4 outputs) and writes one 8-byte piece per output plane (2-byte
         // stores would reach HBM as partial lines, the stores being non-temporal).
         wave_sync();
+        // The group's 4 output planes as one buffer: the lane's piece offset is shared
+        // by the 4 stores, the plane offset is a scalar.
+        const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(yg, (short)0, 8 * OHW, 0x00020000);
         for (int i = lane; 4 * i < OHW; i += 64) {
             const uint4 pa = *reinterpret_cast<const uint4 *>(ys + 4 * i);       // positions 4i, 4i+1
             const uint4 pb = *reinterpret_cast<const uint4 *>(ys + 4 * i + 2);   // positions 4i+2, 4i+3
             // output o of a position: the low (o even) or high half of dword o / 2 of its entry
             const uint32_t lo = 0x05040100u, hi = 0x07060302u;
-            uint2 *yo = reinterpret_cast<uint2 *>(yg) + i;
-            store_nt(yo, make_uint2(__builtin_amdgcn_perm(pa.z, pa.x, lo), __builtin_amdgcn_perm(pb.z, pb.x, lo)));
-            store_nt(yo + OHW / 4, make_uint2(__builtin_amdgcn_perm(pa.z, pa.x, hi), __builtin_amdgcn_perm(pb.z, pb.x, hi)));
-            store_nt(yo + OHW / 2, make_uint2(__builtin_amdgcn_perm(pa.w, pa.y, lo), __builtin_amdgcn_perm(pb.w, pb.y, lo)));
-            store_nt(yo + 3 * (OHW / 4), make_uint2(__builtin_amdgcn_perm(pa.w, pa.y, hi), __builtin_amdgcn_perm(pb.w, pb.y, hi)));
+            auto put = [&](int o, uint32_t a, uint32_t b) {
+                __builtin_amdgcn_raw_buffer_store_b64(gconv_u32x2{a, b}, yr, 8 * i, 2 * o * OHW, kG4NT);
+            };
+            put(0, __builtin_amdgcn_perm(pa.z, pa.x, lo), __builtin_amdgcn_perm(pb.z, pb.x, lo));
+            put(1, __builtin_amdgcn_perm(pa.z, pa.x, hi), __builtin_amdgcn_perm(pb.z, pb.x, hi));
+            put(2, __builtin_amdgcn_perm(pa.w, pa.y, lo), __builtin_amdgcn_perm(pb.w, pb.y, lo));
+            put(3, __builtin_amdgcn_perm(pa.w, pa.y, hi), __builtin_amdgcn_perm(pb.w, pb.y, hi));
         }
     }
 }
