@@ -464,14 +464,20 @@ __host__ __device__ inline int nhwc_g4_img(int HP, int WP, int OH, int OW)
 }
 
 // q / d for 0 <= q < 2048 and 1 <= d <= 400 as (q * m) >> 20, m = ceil(2^20 / d)
-// (the same exact range as the NCHW kernel's division).
-__device__ __forceinline__ int ng4_div(int q, uint32_t m) { return (int)(((uint32_t)q * m) >> 20); }
+// (the same exact range as the NCHW kernel's division), on the full-rate 24-bit
+// multiply: both factors are below 2^24 and the product below 2^31.
+__device__ __forceinline__ int ng4_div(int q, uint32_t m) { return (int)(__umul24((uint32_t)q, m) >> 20); }
+// a * b for 0 <= a, b < 2^24 with a product below 2^31 (plane positions and sizes).
+__device__ __forceinline__ int ng4_mul(int a, int b) { return (int)__umul24((uint32_t)a, (uint32_t)b); }
 
+// The value lane + 1 holds (lane 63 receives zero; its result is not used): a DPP
+// move with no old value, so the compiler need not copy the source first.
 __device__ __forceinline__ uint2 ng4_next_lane(uint2 v)
 {
-    return make_uint2((uint32_t)__builtin_amdgcn_update_dpp((int)v.x, (int)v.x, 0x130, 0xf, 0xf, false),
-                      (uint32_t)__builtin_amdgcn_update_dpp((int)v.y, (int)v.y, 0x130, 0xf, 0xf, false));
+    return make_uint2((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x130, 0xf, 0xf, true),
+                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x130, 0xf, 0xf, true));
 }
+constexpr int kNG4NT = 2;   // buffer-store cache policy: non-temporal
 
 typedef _Float16 ng4_f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 ng4_bf16x4 __attribute__((ext_vector_type(4)));
@@ -521,14 +527,18 @@ conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *_
 
     // Every global load is issued before the first is used: the image pieces, then
     // this wave's filters (lane i % 4: output i's 4 inputs at each tap) and biases.
+    // The image's block through one buffer: byte offsets (pos * C + 8 * part) * 2,
+    // below 2^31, with pos * C on the 24-bit multiply (C < 2^24; both planned).
     const T *xn = x + (int64_t)n * HW * C + c0;
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(xn), (short)0, 0x7fffffff, 0x00020000);
     uint4 xv[kNG4MaxLoads];
 #pragma unroll
     for (int j = 0; j < kNG4MaxLoads; ++j) {
         if (kThreads * j < npiece) {   // uniform; the piece index is clamped, not branched on
             const int i = min(tid + kThreads * j, npiece - 1);
             const int pos = i / PP, part = i - pos * PP;
-            xv[j] = *reinterpret_cast<const uint4 *>(xn + (int64_t)pos * C + 8 * part);
+            xv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xr, 2 * (ng4_mul(pos, C) + 8 * part), 0, 0));
         }
     }
     uint2 fa[GPW][9], bz[GPW];
@@ -542,32 +552,35 @@ conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *_
     }
     __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first use
 
-    // Planes: border entries zero (the ph top and bottom rows, then the pw left and
-    // right columns of every image row), image entries from the pieces.
+    // Planes: border entries zero (with padding 0 or 1: the top and bottom rows,
+    // 2*ph*WP entries, then the left and right columns of the H image rows, 2*pw*H
+    // entries; a lane decodes one and zeroes it in the wave's planes), image entries
+    // from the pieces.
     const int nborder = HP * WP - HW;
-    for (int i = tid; i < nborder * GPB; i += kThreads) {
-        const int gl = i / nborder, b = i - gl * nborder;
+    for (int b = lane; b < nborder; b += 64) {
         int hp, wp;
         if (b < 2 * ph * WP) {
-            const int r = b / WP;
-            hp = r < ph ? r : H + r;
-            wp = b - r * WP;
+            const bool bottom = b >= WP;
+            hp = bottom ? HP - 1 : 0;
+            wp = bottom ? b - WP : b;
         } else {
-            const int j = b - 2 * ph * WP, r = j / (2 * pw), sd = j - r * (2 * pw);
-            hp = ph + r;
-            wp = sd < pw ? sd : W + sd;
+            const int j = b - 2 * ph * WP;
+            hp = ph + (j >> 1);
+            wp = (j & 1) ? WP - 1 : 0;
         }
-        xs[gl * img + hp * WP + wp] = make_uint2(0, 0);
+        const int e = ng4_mul(hp, WP) + wp;
+#pragma unroll
+        for (int sg = 0; sg < GPW; ++sg) xs[ng4_mul(wave + 4 * sg, img) + e] = make_uint2(0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kNG4MaxLoads; ++j) {
         const int i = tid + kThreads * j;
         if (kThreads * j < npiece && i < npiece) {
             const int pos = i / PP, part = i - pos * PP;
-            const int h = ng4_div(pos, mw), ww = pos - h * W;
-            const int e = (h + ph) * WP + ww + pw;
-            xs[(2 * part) * img + e] = make_uint2(xv[j].x, xv[j].y);
-            xs[(2 * part + 1) * img + e] = make_uint2(xv[j].z, xv[j].w);
+            const int h = ng4_div(pos, mw), ww = pos - ng4_mul(h, W);
+            const int e = ng4_mul(h + ph, WP) + ww + pw;
+            xs[ng4_mul(2 * part, img) + e] = make_uint2(xv[j].x, xv[j].y);
+            xs[ng4_mul(2 * part + 1, img) + e] = make_uint2(xv[j].z, xv[j].w);
         }
     }
     __syncthreads();
@@ -594,9 +607,9 @@ conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *_
                 acc = NMfma4<T>::run(fa[s][kh * 3 + 1], v1, acc);
                 acc = NMfma4<T>::run(fa[s][kh * 3 + 2], v2, acc);
             }
-            const int oh = ng4_div(a, mwp), ow = a - oh * WP;
+            const int oh = ng4_div(a, mwp), ow = a - ng4_mul(oh, WP);
             if (lane < kNG4Step && a < na && ow < OW)
-                ys[(oh * OW + ow) * YS + gl] =
+                ys[ng4_mul(ng4_mul(oh, OW) + ow, YS) + gl] =
                     make_uint2(ng4_bits(from_f32<T>(acc[0])) | (ng4_bits(from_f32<T>(acc[1])) << 16),
                                ng4_bits(from_f32<T>(acc[2])) | (ng4_bits(from_f32<T>(acc[3])) << 16));
         }
@@ -605,11 +618,15 @@ conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *_
 
     // The block's outputs along C: piece (position, part) is channels c0 + 8*part ..
     // of one position, 16 bytes.
+    // Byte offsets (pos * C + 8 * part) * 2 from the block's first output, below 2^31
+    // (planned).
     T *yn = y + (int64_t)n * OHW * C + c0;
+    const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(yn, (short)0, 0x7fffffff, 0x00020000);
     for (int i = tid; i < OHW * PP; i += kThreads) {
         const int pos = i / PP, part = i - pos * PP;
-        const uint2 lo = ys[pos * YS + 2 * part], hi = ys[pos * YS + 2 * part + 1];
-        store_nt(reinterpret_cast<uint4 *>(yn + (int64_t)pos * C + 8 * part), make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const uint2 lo = ys[ng4_mul(pos, YS) + 2 * part], hi = ys[ng4_mul(pos, YS) + 2 * part + 1];
+        __builtin_amdgcn_raw_buffer_store_b128(gconv_u32x4{lo.x, lo.y, hi.x, hi.y}, yr, 2 * (ng4_mul(pos, C) + 8 * part), 0,
+                                               kNG4NT);
     }
 }
 
@@ -625,8 +642,8 @@ int nhwc_g4_mfma_gpb(const Conv2dArgs &a, size_t *lds, int *img)
     } else {
         if (!(a.C == 4 * a.groups && a.Cout == a.C && !a.interleaved && a.KH == 3 && a.KW == 3 && a.sh == 1 &&
               a.sw == 1 && a.dh == 1 && a.dw == 1 && a.ph <= 1 && a.pw <= 1 && a.W + 2 * a.pw <= 400 &&
-              (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= 1024 && a.H * a.W * a.C < (int64_t(1) << 31) &&
-              a.OH * a.OW * a.C < (int64_t(1) << 31) &&
+              (a.H + 2 * a.ph) * (a.W + 2 * a.pw) <= 1024 && a.H * a.W * a.C < (int64_t(1) << 30) &&
+              a.OH * a.OW * a.C < (int64_t(1) << 30) && a.C < (int64_t(1) << 24) &&
               ((reinterpret_cast<uintptr_t>(a.x) | reinterpret_cast<uintptr_t>(a.y)) & 15) == 0 &&
               ((reinterpret_cast<uintptr_t>(a.w) | reinterpret_cast<uintptr_t>(a.bias)) & 7) == 0))
             return 0;
