@@ -294,6 +294,8 @@ struct BandGeom {
     int GAP;           // 16-byte units left free after every KR * S staged rows
     int units;         // 16-byte LDS units reserved for the staged rows (the filters follow)
     int sp_p, sp_hp;   // 4G staged rows as (planes, rows) of the padded row space
+    int step_off;      // with one filter per channel: input elements between rows 4G apart
+    int wrap_off;      // and the correction when the padded row wraps into the next plane
     int wgs, wgs_per_xcd;
     FastDiv fd_cpr, fd_spp, fd_hp, fd_cout, fd_m;
 };
@@ -348,12 +350,17 @@ dw2d_band(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     // load instruction covers G consecutive rows, contiguous in x within a plane).
     // The row advances by 4G, a multiple of BAND, so the plane and row within it
     // advance by a fixed step and the LDS unit by a fixed stride: no division per row.
-    {
+    // With one filter per channel the input plane is the output plane, and the row's
+    // input offset advances by a fixed step too (ONE); otherwise each row maps its
+    // plane to the input plane it reads.
+    auto stage = [&](auto one) {
+        constexpr bool ONE = decltype(one)::value;
         const int rstep = 4 * g.G;
         const int r0 = wave * g.G + slot;
         int vr = R_lo + r0;
         int sp = fdiv(vr, g.fd_hp);
         int shp = vr - sp * g.Hp;                     // row within the padded plane
+        int rowoff = (sp - pa) * g.H * g.W + (shp - g.ph) * g.W;   // ONE: the row's first input element
         int su = r0 * g.CPR + rc + (r0 / BAND) * g.GAP;
         const int ustep = rstep * g.CPR + (rstep / BAND) * g.GAP;
         const bool lane_ok = slot < g.G;
@@ -365,20 +372,28 @@ dw2d_band(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
                 const int r = kb + j * rstep;
                 const int ih = shp - g.ph;
                 const bool ok = lane_ok && r < NR && sp < g.planes && ih >= 0 && ih < g.H;
-                const uint32_t off =
-                    ok ? (uint32_t)((((in_plane(sp) - pia) * g.H + ih) * g.W + 8 * rc) * 2) : kOOB;
+                uint32_t off;
+                if constexpr (ONE)
+                    off = ok ? (uint32_t)((rowoff + 8 * rc) * 2) : kOOB;
+                else
+                    off = ok ? (uint32_t)((((in_plane(sp) - pia) * g.H + ih) * g.W + 8 * rc) * 2) : kOOB;
                 dst[j] = lane_ok && r < NR ? su : -1;
                 Load<16>::run(xr, off, d[j]);
                 su += ustep;
                 shp += g.sp_hp;
                 sp += g.sp_p;
-                if (shp >= g.Hp) { shp -= g.Hp; ++sp; }
+                rowoff += g.step_off;
+                if (shp >= g.Hp) { shp -= g.Hp; ++sp; rowoff += g.wrap_off; }
             }
 #pragma unroll
             for (int j = 0; j < NB; ++j)
                 if (dst[j] >= 0) lds[dst[j]] = make_uint4(d[j][0], d[j][1], d[j][2], d[j][3]);
         }
-    }
+    };
+    if (g.Cout == g.C)
+        stage(std::true_type{});
+    else
+        stage(std::false_type{});
     // Filters of output planes pa .. pb, each followed by the plane's bias (zero
     // without one), from addresses that are always valid.
     for (int i = tid; i < (pb - pa + 1) * (KK + 1); i += kThreads) {
@@ -664,6 +679,8 @@ BandPlan make_band_plan(const Conv2dArgs &a)
     g.units = (int)units;
     g.sp_p = (int)(4 * G / Hp);
     g.sp_hp = (int)(4 * G % Hp);
+    g.step_off = (int)(g.sp_hp * a.W + (int64_t)g.sp_p * a.H * a.W);
+    g.wrap_off = (int)(a.H * a.W - Hp * a.W);
     g.wgs = (int)ceil_div(strips, (int64_t)spw);
     g.wgs_per_xcd = (int)ceil_div(g.wgs, 8);
     g.fd_cpr = make_fastdiv((uint32_t)CPR);
