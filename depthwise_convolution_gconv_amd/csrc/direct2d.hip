@@ -186,6 +186,18 @@ template <> struct Mfma4<__bf16> {
     }
 };
 template <typename T> __device__ __forceinline__ uint32_t bits16(T v) { return __builtin_bit_cast(uint16_t, v); }
+// Two fp32 values rounded to T and packed (a low), one paired conversion.
+typedef _Float16 g4_f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 g4_bf16x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t g4_pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t g4_pack2<_Float16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, g4_f16x2{(_Float16)a, (_Float16)b});
+}
+template <> __device__ __forceinline__ uint32_t g4_pack2<__bf16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, g4_bf16x2{(__bf16)a, (__bf16)b});
+}
 
 constexpr int kG4Waves = kThreads / 64;
 constexpr int kG4MaxPos = 1024;   // positions of one padded slab image
@@ -228,9 +240,9 @@ __host__ __device__ inline G4Lds g4_lds(int HP, int WP, int OH, int OW)
 // pass: the image positions from the loaded pairs, the border positions as zeros.
 // Output positions are anchors a = oh * WP + ow of the padded image (the window's
 // top-left entry); tap (kh, kw) of anchor a reads entry a + kh*WP + kw.  Per pass
-// and filter row, one 8-byte LDS read gives each lane its kw = 0 operand and the
-// kw = 1, 2 operands are the next lanes' values (a whole-wave DPP shift by one
-// lane, twice), so a pass of 62 anchors takes 3 reads instead of 9.  Each tap is
+// and filter row, two 8-byte LDS reads give each lane its kw = 0 and kw = 2
+// operands and the kw = 1 operand is the next lane's kw = 0 value (a whole-wave DPP
+// shift by one lane), so a pass of 62 anchors takes 6 reads instead of 9.  Each tap is
 // one 4x4x4 MFMA for the 16 blocks of 4 anchors: A = the group's 4 x 4 filter
 // matrix at that tap, B = the 4 input channels of each anchor, D = the 4 outputs
 // of the lane's anchor, fp32 accumulation.
@@ -304,18 +316,28 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
         }
         xs[g4_mul(hp, WP) + wp] = make_uint2(0, 0);
     }
+    // Half e of each channel's pair: channels (0,1) and (2,3) side by side.
+    auto entry = [&](int j, int e) {
+        const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+        return make_uint2(__builtin_amdgcn_perm(xv[j][1], xv[j][0], sel), __builtin_amdgcn_perm(xv[j][3], xv[j][2], sel));
+    };
+    const bool w_even = (W & 1) == 0;   // a pair's two positions then share a row
 #pragma unroll
     for (int j = 0; j < kMaxL; ++j) {
         const int q = lane + 64 * j;
         if (64 * j < npair && q < npair) {
+            if (w_even) {
+                const int h = g4_div(2 * q, mw), ww = 2 * q - g4_mul(h, W);
+                uint2 *d = xs + g4_mul(h + ph, WP) + ww + pw;
+                d[0] = entry(j, 0);
+                d[1] = entry(j, 1);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int p = 2 * q + e;
-                const int h = g4_div(p, mw), ww = p - g4_mul(h, W);
-                // half e of each channel's pair: channels (0,1) and (2,3) side by side
-                const uint32_t sel = e ? 0x07060302u : 0x05040100u;
-                xs[g4_mul(h + ph, WP) + ww + pw] = make_uint2(__builtin_amdgcn_perm(xv[j][1], xv[j][0], sel),
-                                                         __builtin_amdgcn_perm(xv[j][3], xv[j][2], sel));
+                for (int e = 0; e < 2; ++e) {
+                    const int p = 2 * q + e;
+                    const int h = g4_div(p, mw), ww = p - g4_mul(h, W);
+                    xs[g4_mul(h + ph, WP) + ww + pw] = entry(j, e);
+                }
             }
         }
     }
@@ -345,8 +367,8 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh) {
             const uint2 v0 = xs[a + kh * WP];
+            const uint2 v2 = xs[a + kh * WP + 2];   // inside the image area for every lane (g4_lds)
             const uint2 v1 = g4_next_lane(v0);
-            const uint2 v2 = g4_next_lane(v1);
             acc = Mfma4<T>::run(fa[kh * 3 + 0], v0, acc);
             acc = Mfma4<T>::run(fa[kh * 3 + 1], v1, acc);
             acc = Mfma4<T>::run(fa[kh * 3 + 2], v2, acc);
@@ -355,8 +377,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
         if (lane < kG4Step && a < na && ow < OW) {
             const int p = g4_mul(oh, OW) + ow;
             if (ystage) {
-                ys[p] = make_uint2(bits16(from_f32<T>(acc[0])) | (bits16(from_f32<T>(acc[1])) << 16),
-                                   bits16(from_f32<T>(acc[2])) | (bits16(from_f32<T>(acc[3])) << 16));
+                ys[p] = make_uint2(g4_pack2<T>(acc[0], acc[1]), g4_pack2<T>(acc[2], acc[3]));
             } else {
 #pragma unroll
                 for (int o = 0; o < 4; ++o) store_nt(yg + (int64_t)o * ocs * OHW + p, from_f32<T>(acc[o]));
