@@ -447,8 +447,9 @@ conv2d_nhwc_g4k3_row(const T *__restrict__ x, const T *__restrict__ w, const T *
 //    lanes take 64 consecutive anchors of its padded plane (anchor = the window's
 //    top-left entry), each tap is one MFMA with A = the group's 4 x 4 filter matrix
 //    at that tap (lane i%4 holds output i's 4 inputs, read straight from w) and
-//    B = the anchor's 4 channels; per filter row one LDS read gives the kw = 0
-//    operand and the kw = 1, 2 operands are the next lanes' values (DPP shifts).
+//    B = the anchor's 4 channels; per filter row two LDS reads give the kw = 0 and
+//    kw = 2 operands and the kw = 1 operand is the next lane's kw = 0 value (a DPP
+//    shift).
 //  * Outputs: each anchor's 4 outputs (8 bytes) go to an LDS image of the block's
 //    outputs, [position][GPB + 1 entries] (an odd row stride: the 8-byte writes of
 //    64 consecutive positions fall on distinct banks), and the workgroup then
@@ -497,7 +498,18 @@ template <> struct NMfma4<__bf16> {
                                                      __builtin_bit_cast(ng4_bf16x4, b), c, 0, 0, 0);
     }
 };
-template <typename T> __device__ __forceinline__ uint32_t ng4_bits(T v) { return __builtin_bit_cast(uint16_t, v); }
+// Two fp32 values rounded to T and packed (a low), one paired conversion.
+typedef _Float16 ng4_f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 ng4_bf16x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t ng4_pack2(float a, float b);
+template <> __device__ __forceinline__ uint32_t ng4_pack2<_Float16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, ng4_f16x2{(_Float16)a, (_Float16)b});
+}
+template <> __device__ __forceinline__ uint32_t ng4_pack2<__bf16>(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, ng4_bf16x2{(__bf16)a, (__bf16)b});
+}
 
 constexpr int kNG4MaxLoads = 8;   // 16-byte input loads per thread (H*W*GPB/2 <= 2048)
 
@@ -601,8 +613,8 @@ conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *_
 #pragma unroll
             for (int kh = 0; kh < 3; ++kh) {
                 const uint2 v0 = pl[a + kh * WP];
+                const uint2 v2 = pl[a + kh * WP + 2];   // inside the plane's entries for every lane
                 const uint2 v1 = ng4_next_lane(v0);
-                const uint2 v2 = ng4_next_lane(v1);
                 acc = NMfma4<T>::run(fa[s][kh * 3 + 0], v0, acc);
                 acc = NMfma4<T>::run(fa[s][kh * 3 + 1], v1, acc);
                 acc = NMfma4<T>::run(fa[s][kh * 3 + 2], v2, acc);
@@ -610,8 +622,7 @@ conv2d_nhwc_g4_mfma(const T *__restrict__ x, const T *__restrict__ w, const T *_
             const int oh = ng4_div(a, mwp), ow = a - ng4_mul(oh, WP);
             if (lane < kNG4Step && a < na && ow < OW)
                 ys[ng4_mul(ng4_mul(oh, OW) + ow, YS) + gl] =
-                    make_uint2(ng4_bits(from_f32<T>(acc[0])) | (ng4_bits(from_f32<T>(acc[1])) << 16),
-                               ng4_bits(from_f32<T>(acc[2])) | (ng4_bits(from_f32<T>(acc[3])) << 16));
+                    make_uint2(ng4_pack2<T>(acc[0], acc[1]), ng4_pack2<T>(acc[2], acc[3]));
         }
     }
     __syncthreads();
