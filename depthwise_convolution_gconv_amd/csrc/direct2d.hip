@@ -282,7 +282,7 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
     // loads, the channel offset is a scalar.
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(xg), (short)0, 8 * HW, 0x00020000);
-    uint32_t xv[kMaxL][4], wv[3];
+    uint32_t xv[kMaxL][4];
 #pragma unroll
     for (int j = 0; j < kMaxL; ++j) {
         if (64 * j < npair) {   // uniform; the pair index is clamped, not branched on
@@ -291,8 +291,13 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
             for (int c = 0; c < 4; ++c) xv[j][c] = __builtin_amdgcn_raw_buffer_load_b32(xr, 4 * q, 2 * c * HW, 0);
         }
     }
+    // The group's 144 filter values: lane L < 16 takes output L / 4 and input L % 4,
+    // whose 9 taps are the 9 consecutive values at 9 L (the other lanes load lane
+    // 15's and write nothing).
+    uint16_t wv[9];
+    const T *wl = wg + 9 * min(lane, 15);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) wv[j] = bits16(wg[min(lane + 64 * j, 143)]);
+    for (int t = 0; t < 9; ++t) wv[t] = (uint16_t)bits16(wl[t]);
     const T *bp = bias ? bias + 4 * k : wg;   // loaded either way; zero when there is no bias
     T braw[4];
 #pragma unroll
@@ -341,14 +346,12 @@ direct2d_g4(const T *__restrict__ x, const T *__restrict__ w, const T *__restric
             }
         }
     }
+    // Filter entry (t, o) holds output o's 4 inputs at tap t: value (o, c, t) at
+    // halfword 16 t + 4 o + c, i.e. 16 t + L for lane L.
     uint16_t *fs16 = reinterpret_cast<uint16_t *>(fs);
+    if (lane < 16) {
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int i = lane + 64 * j;
-        if (i < 144) {
-            const int o = i / 36, c = (i / 9) % 4, t = i % 9;
-            fs16[(t * 4 + o) * 4 + c] = (uint16_t)wv[j];
-        }
+        for (int t = 0; t < 9; ++t) fs16[16 * t + lane] = wv[t];
     }
     wave_sync();
 
