@@ -82,7 +82,10 @@ struct DeferGeom {
 // W4: every run lies inside its output row (OW a multiple of 4) and y is 8-byte
 // aligned, so a run's 4 outputs of a filter are one 8-byte store; otherwise 2-byte
 // stores.
-template <typename T, int XR, int VW, bool W4>
+// FN: the group has 64 filters, so every filter row a lane stores exists and no store
+// tests its row (a lane without a run still stores past the end: its base is past
+// the end and 59 filter steps from there stay below 2^32, planned).
+template <typename T, int XR, int VW, bool W4, bool FN>
 __global__ void __launch_bounds__(kThreads, 1)
 igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict__ bias,
                 T *__restrict__ y, DeferGeom g)
@@ -317,7 +320,7 @@ igemm_defer_fwd(const T *__restrict__ x, const T *__restrict__ w, const T *__res
         uint32_t pb = pyh;
         int lim = plim;
         asm volatile("" : "+v"(pb), "+v"(lim));
-        const uint32_t yo = rowc < lim ? pb + (uint32_t)(rowc * fs2) : kOOB;
+        const uint32_t yo = (FN || rowc < lim) ? pb + (uint32_t)(rowc * fs2) : kOOB;
         float v[kRun];
 #pragma unroll
         for (int mb = 0; mb < kRun; ++mb) v[mb] = acc_read(acc[PS][nb][mb][r]);
@@ -571,7 +574,7 @@ DeferPlan make_defer_plan(const Conv2dArgs &a)
     return pl;
 }
 
-template <typename T, int XR, int VW, bool W4>
+template <typename T, int XR, int VW, bool W4, bool FN>
 hipError_t run(const Conv2dArgs &a, const DeferPlan &pl)
 {
     int dev = 0, cus = 0;
@@ -579,7 +582,7 @@ hipError_t run(const Conv2dArgs &a, const DeferPlan &pl)
     if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (err != hipSuccess) return err;
     const int64_t blocks = std::min<int64_t>(pl.g.tiles, std::max(cus, 8));
-    hipLaunchKernelGGL((igemm_defer_fwd<T, XR, VW, W4>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((igemm_defer_fwd<T, XR, VW, W4, FN>), dim3((unsigned)blocks), dim3(kThreads), 0, a.stream,
                        (const T *)a.x, (const T *)a.w, (const T *)a.bias, (T *)a.y, pl.g);
     return hipGetLastError();
 }
@@ -587,9 +590,15 @@ hipError_t run(const Conv2dArgs &a, const DeferPlan &pl)
 template <typename T>
 hipError_t run_typed(const Conv2dArgs &a, const DeferPlan &pl)
 {
-    // (XR, VW) = (1, 8) or (at most 2, 4).
-    if (pl.W4) return pl.VW == 8 ? run<T, 1, 8, true>(a, pl) : run<T, 2, 4, true>(a, pl);
-    return pl.VW == 8 ? run<T, 1, 8, false>(a, pl) : run<T, 2, 4, false>(a, pl);
+    // (XR, VW) = (1, 8) or (at most 2, 4).  FN: 64 filters per group, and a base
+    // past the end plus 59 filter steps (2 * ocs * OH * OW bytes each) below 2^32.
+    const bool fn = pl.g.Ng == 64 && 59 * 2 * (int64_t)pl.g.ocs * pl.g.OH * pl.g.OW < (int64_t(1) << 31);
+    if (fn) {
+        if (pl.W4) return pl.VW == 8 ? run<T, 1, 8, true, true>(a, pl) : run<T, 2, 4, true, true>(a, pl);
+        return pl.VW == 8 ? run<T, 1, 8, false, true>(a, pl) : run<T, 2, 4, false, true>(a, pl);
+    }
+    if (pl.W4) return pl.VW == 8 ? run<T, 1, 8, true, false>(a, pl) : run<T, 2, 4, true, false>(a, pl);
+    return pl.VW == 8 ? run<T, 1, 8, false, false>(a, pl) : run<T, 2, 4, false, false>(a, pl);
 }
 
 }  // namespace
