@@ -53,6 +53,11 @@ struct Dw2dGeom {
     int npad;          // LDS columns of a row outside the image (WP - W)
     int runs_per_wg, total_runs, wgs, wgs_per_xcd;
     int NRmax;         // LDS rows reserved for the input (bound on any workgroup's rows)
+    // A thread's staging chunks are 256 apart: (st_r rows, st_c chunks) of the staged
+    // rows, st_r = st_rq padded planes + st_rm rows; with one filter per channel the
+    // input offset advances by st_off elements (plus W for a carried row, plus
+    // st_wrap when the padded row wraps into the next plane).
+    int st_c, st_r, st_rq, st_rm, st_off, st_wrap;
     FastDiv fd_rpr, fd_oh, fd_hp, fd_cpr, fd_cout, fd_m, fd_npad;
 };
 
@@ -159,33 +164,54 @@ dw2d_rows(const T *__restrict__ x, const T *__restrict__ w, const T *__restrict_
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<T *>(x + (int64_t)pia * g.H * g.W), (short)0, 0x7fffffff, 0x00020000);
 
-    // Stage the rows, NB loads per thread in flight at a time.
+    // Stage the rows, NB loads per thread in flight at a time.  A thread's chunks are
+    // i = tid + 256 k: row r = i / CPR and column chunk ch advance by fixed steps, and
+    // so do the row's plane and row within it (and with one filter per channel, ONE,
+    // its input offset), with no division per chunk.
     const int nchunks = NR * g.CPR;
-    for (int base = 0; base < nchunks; base += NB * kThreads) {
-        uint32_t d[NB][DW];
-        int dst[NB];
+    auto stage = [&](auto one) {
+        constexpr bool ONE = decltype(one)::value;
+        int r = fdiv(tid, g.fd_cpr), ch = tid - r * g.CPR;
+        int sp = fdiv(R_lo + r, g.fd_hp), shp = R_lo + r - sp * g.Hp;
+        int rowoff = (sp - pa) * g.H * g.W + (shp - g.ph) * g.W;   // ONE: the row's first input element
+        for (int base = 0; base < nchunks; base += NB * kThreads) {
+            uint32_t d[NB][DW];
+            int dst[NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int i = base + j * kThreads + tid;
-            uint32_t off = kOOB;
-            dst[j] = -1;
-            if (i < nchunks) {
-                const int r = fdiv(i, g.fd_cpr), ch = i - r * g.CPR;
-                const int vrow = R_lo + r;
-                const int p = fdiv(vrow, g.fd_hp), ih = vrow - p * g.Hp - g.ph;
-                if (p < g.planes && ih >= 0 && ih < g.H)
-                    off = (uint32_t)((((int64_t)(in_plane(p) - pia) * g.H + ih) * g.W + ch * VI) * sizeof(T));
-                dst[j] = r * g.WP + g.pw + ch * VI;
+            for (int j = 0; j < NB; ++j) {
+                uint32_t off = kOOB;
+                dst[j] = -1;
+                if (r < NR) {
+                    const int ih = shp - g.ph;
+                    if (sp < g.planes && ih >= 0 && ih < g.H) {
+                        if constexpr (ONE)
+                            off = (uint32_t)((rowoff + ch * VI) * (int)sizeof(T));
+                        else
+                            off = (uint32_t)((((int64_t)(in_plane(sp) - pia) * g.H + ih) * g.W + ch * VI) * sizeof(T));
+                    }
+                    dst[j] = r * g.WP + g.pw + ch * VI;
+                }
+                Load<VI * sizeof(T) >= 4 ? 4 * DW : 2>::run(xr, off, d[j]);
+                ch += g.st_c;
+                r += g.st_r;
+                shp += g.st_rm;
+                sp += g.st_rq;
+                rowoff += g.st_off;
+                if (ch >= g.CPR) { ch -= g.CPR; ++r; ++shp; rowoff += g.W; }
+                if (shp >= g.Hp) { shp -= g.Hp; ++sp; rowoff += g.st_wrap; }
             }
-            Load<VI * sizeof(T) >= 4 ? 4 * DW : 2>::run(xr, off, d[j]);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                if (dst[j] >= 0) {
+#pragma unroll
+                    for (int q = 0; q < VI; ++q) xs[dst[j] + q] = lds_elem<T>(d[j], q);
+                }
         }
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-            if (dst[j] >= 0) {
-#pragma unroll
-                for (int q = 0; q < VI; ++q) xs[dst[j] + q] = lds_elem<T>(d[j], q);
-            }
-    }
+    };
+    if (g.Cout == g.C)
+        stage(std::true_type{});
+    else
+        stage(std::false_type{});
     // Columns outside the image: zero.
     for (int i = tid; i < NR * g.npad; i += kThreads) {
         const int r = fdiv(i, g.fd_npad), c = i - r * g.npad;
@@ -548,6 +574,12 @@ Plan make_plan(const Conv2dArgs &a)
     g.wgs = (int)ceil_div(total_runs, g.runs_per_wg);
     g.wgs_per_xcd = (int)ceil_div(g.wgs, 8);
     g.NRmax = (int)nr;
+    g.st_c = kThreads % g.CPR;
+    g.st_r = kThreads / g.CPR;
+    g.st_rq = (int)(g.st_r / Hp);
+    g.st_rm = (int)(g.st_r % Hp);
+    g.st_off = (int)(g.st_rq * a.H * a.W + g.st_rm * a.W);
+    g.st_wrap = (int)(a.H * a.W - Hp * a.W);
     g.fd_rpr = make_fastdiv((uint32_t)RPR);
     g.fd_oh = make_fastdiv((uint32_t)a.OH);
     g.fd_hp = make_fastdiv((uint32_t)Hp);
